@@ -1,0 +1,220 @@
+"""Benchmark of libsgemm on one MI355X.
+
+A step is one sgemm_f32 call on the headline workload: M = N = K = 5120,
+row-major fp32, A and B uniform on [-1, 1), C preloaded uniform, alpha = 1.5,
+beta = 0.5 (the largest point of the square sweep).  Inputs are resident in
+HBM before timing starts.  The line printed also carries:
+  * roofline: the MFMA tile kernel's achieved fp32 rate against the MI355X
+    dense fp32 matrix peak, from HIP events around the timed launches, and
+    the HBM traffic per launch measured with rocprofv3 counters when the
+    stored counter summary matches the current kernel sources;
+  * cpu_baseline: the CPU reference timed on the host cores on a bounded
+    sample of the same product (the first rows of C);
+  * im2col: the six convolution-as-GEMM shapes, each timed on its own with
+    the memory-side caches flushed between launches, with TFLOPS and the
+    HBM bandwidth the algorithmic bytes imply.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-im2col]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "SGEMM TFLOPS at 5120³ + im2col shapes; % of FP32 peak / HBM roofline"
+PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 matrix (and packed vector) peak
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_tile_5120.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources, to tell whether stored counters still apply."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp32_gemm_04_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """Bytes per launch from the committed counter summary, or None if stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_steps(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms
+
+
+def device_operands(case):
+    import torch
+    A, B, C = workloads.operands(case, integer=False)
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    if C is None:
+        dC = torch.zeros((case.M, case.N), dtype=torch.float32, device="cuda")
+    else:
+        dC = torch.from_numpy(C).cuda()
+    return A, B, C, dA, dB, dC
+
+
+def cpu_baseline(case, A, B, C, budget_s):
+    """Time the CPU reference on the first R rows of the product."""
+    import oracle
+    lib = oracle.load()
+    threads = oracle.num_threads(lib)
+    rows = max(1, min(case.M, threads))
+    while True:
+        t0 = time.perf_counter()
+        oracle.sgemm(A[:rows], B, None if C is None else C[:rows], case.alpha, case.beta,
+                     with_absdot=False, lib=lib)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 2 or rows >= case.M:
+            break
+        rows = min(case.M, max(rows * 2, int(rows * budget_s * 0.8 / max(dt, 1e-3))))
+    flops = 2.0 * rows * case.N * case.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": "first %d of %d rows of C for M=N=K=%d, alpha=%g, beta=%g (%.1f s)"
+                      % (rows, case.M, case.M, case.alpha, case.beta, dt)}
+
+
+def bench_im2col(sg, stream, reps):
+    """Each im2col shape: median time of `reps` launches, caches flushed between."""
+    import torch
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    out = []
+    for case in workloads.SKINNY + workloads.MID:
+        log("im2col", case.name)
+        _, _, _, dA, dB, dC = device_operands(case)
+        args = (case.M, case.N, case.K, case.alpha, dA.data_ptr(), case.K, dB.data_ptr(),
+                case.N, case.beta, dC.data_ptr(), case.N, stream.cuda_stream)
+        rc = sg.sgemm_f32(*args)
+        assert rc == 0, sg.sgemm_status_string(rc)
+        times = []
+        for _ in range(reps):
+            flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            sg.sgemm_f32(*args)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        tflops = case.flops / (ms * 1e-3) / 1e12
+        gbps = case.alg_bytes / (ms * 1e-3) / 1e9
+        roof_us = max(case.alg_bytes / (PEAK_HBM_GBPS * 1e9), case.flops / (PEAK_FP32_TFLOPS * 1e12)) * 1e6
+        _, plan = sg.sgemm_plan(0, case.M, case.N, case.K, case.K, case.N, case.N, case.alpha,
+                                torch.cuda.get_device_properties(0).multi_processor_count)
+        out.append({"shape": [case.M, case.N, case.K], "us": round(ms * 1e3, 2),
+                    "tflops": round(tflops, 2), "hbm_gbps": round(gbps, 1),
+                    "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                    "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4),
+                    "frac_roofline": round(roof_us / (ms * 1e3), 4), "kernel": plan})
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-reference baseline")
+    ap.add_argument("--no-im2col", action="store_true", help="skip the im2col shapes")
+    ap.add_argument("--im2col-reps", type=int, default=10)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU reference work")
+    ap.add_argument("--variant", type=int, default=0, help="force a kernel family (tuning)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(an N-split of B and C needs no collective; see the design notes).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import fp32_gemm_04_amd as sg
+
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    case = workloads.HEADLINE
+    log("device", props.name, "CUs", props.multi_processor_count)
+    A, B, C, dA, dB, dC = device_operands(case)
+    stream = torch.cuda.current_stream()
+    call_args = (case.M, case.N, case.K, case.alpha, dA.data_ptr(), case.K, dB.data_ptr(),
+                 case.N, case.beta, dC.data_ptr(), case.N, stream.cuda_stream)
+
+    def step():
+        rc = sg.sgemm_f32_variant(args.variant, *call_args)
+        if rc != 0:
+            raise RuntimeError(sg.sgemm_status_string(rc))
+
+    log("timing %d steps after %d warmup" % (args.steps, args.warmup))
+    ms = time_steps(step, args.steps, args.warmup, stream)
+    tflops = case.flops / (ms * 1e-3) / 1e12
+    _, plan = sg.sgemm_plan(args.variant, case.M, case.N, case.K, case.K, case.N, case.N,
+                            case.alpha, props.multi_processor_count)
+    traffic = stored_traffic()
+    roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP32_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_TFLOPS, 4),
+                "traffic": traffic, "kernel": plan,
+                "algorithmic_flops_per_launch": case.flops,
+                "avg_launch_ms": round(ms, 4)}
+
+    result = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "sgemm M=N=K=5120 row-major fp32, alpha=1.5, beta=0.5, "
+                               "C preloaded, uniform[-1,1) inputs",
+                   "M": case.M, "N": case.N, "K": case.K, "alpha": case.alpha,
+                   "beta": case.beta, "device": props.name},
+        "roofline": roofline,
+    }
+    if not args.no_im2col:
+        result["im2col"] = bench_im2col(sg, stream, args.im2col_reps)
+    if not args.no_cpu:
+        log("cpu baseline")
+        result["cpu_baseline"] = cpu_baseline(case, A, B, C, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,119 @@
+"""Python binding of libsgemm, the MI355X single-precision GEMM.
+
+Argument marshalling only: every step of the product runs in the HIP
+kernels of ``libsgemm.so`` (built from ``csrc/`` by ``_build.py``).  If the
+library is missing, importing this package raises; there is no fallback.
+
+The functions have the names and arguments of the C ABI in
+``include/sgemm.h``; ``gemm`` is a convenience that takes torch tensors and
+passes their data pointers, leading dimensions and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libsgemm.so")
+
+SGEMM_VARIANT_AUTO = 0
+SGEMM_VARIANT_MFMA = 1
+SGEMM_VARIANT_VALU = 2
+SGEMM_VARIANT_MFMA_TILE = 16
+SGEMM_ERR_BAD_VARIANT = -100
+
+EXPORTS = ("sgemm_f32", "sgemm_f32_variant", "sgemm_plan", "sgemm_num_mfma_tiles",
+           "sgemm_status_string")
+
+if not os.path.exists(LIBRARY):
+    raise ImportError("libsgemm.so is not built; run __graft_entry__.build() "
+                      "(or python fp32_gemm_04_amd/_build.py)")
+
+# torch must be loaded first.  Its wheel carries its own HIP runtime
+# (libamdhip64, soname libamdhip64.so.7, found through torch's RPATH as
+# "libamdhip64.so"); libsgemm asks for "libamdhip64.so.7", which then
+# resolves to that same already-loaded runtime.  Loaded the other way round,
+# the process would hold two HIP runtimes, and torch's streams and memory
+# would be foreign to the one libsgemm calls.
+import torch  # noqa: E402,F401
+
+_lib = ctypes.CDLL(LIBRARY)
+
+_gemm_args = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+              ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+              ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+_lib.sgemm_f32.restype = ctypes.c_int
+_lib.sgemm_f32.argtypes = _gemm_args
+_lib.sgemm_f32_variant.restype = ctypes.c_int
+_lib.sgemm_f32_variant.argtypes = [ctypes.c_int] + _gemm_args
+_lib.sgemm_plan.restype = ctypes.c_int
+_lib.sgemm_plan.argtypes = [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int,
+                                                 ctypes.c_char_p, ctypes.c_int]
+_lib.sgemm_num_mfma_tiles.restype = ctypes.c_int
+_lib.sgemm_num_mfma_tiles.argtypes = []
+_lib.sgemm_status_string.restype = ctypes.c_char_p
+_lib.sgemm_status_string.argtypes = [ctypes.c_int]
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__("sgemm failed with status %d: %s" % (status, sgemm_status_string(status)))
+        self.status = status
+
+
+def sgemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    """C ABI ``sgemm_f32``; pointers and stream are integers.  Returns the status."""
+    return _lib.sgemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_f32_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    """C ABI ``sgemm_f32_variant``.  Returns the status."""
+    return _lib.sgemm_f32_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_plan(variant, M, N, K, lda, ldb, ldc, alpha, num_cus):
+    """C ABI ``sgemm_plan``.  Returns (status, text)."""
+    buf = ctypes.create_string_buffer(256)
+    rc = _lib.sgemm_plan(variant, M, N, K, lda, ldb, ldc, alpha, num_cus, buf, len(buf))
+    return rc, buf.value.decode()
+
+
+def sgemm_num_mfma_tiles() -> int:
+    """C ABI ``sgemm_num_mfma_tiles``."""
+    return _lib.sgemm_num_mfma_tiles()
+
+
+def sgemm_status_string(status: int) -> str:
+    return _lib.sgemm_status_string(status).decode()
+
+
+def _ld(t, name):
+    if t.dim() != 2 or t.dtype.__repr__() != "torch.float32":
+        raise TypeError("%s must be a 2-D float32 tensor" % name)
+    if t.numel() and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have unit column stride" % name)
+    if t.shape[0] > 1 and t.numel():
+        return t.stride(0)
+    return max(1, t.shape[1])
+
+
+def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant: int = SGEMM_VARIANT_AUTO,
+         stream=None):
+    """C <- alpha*A@B + beta*C in place, for float32 CUDA/HIP tensors.
+
+    Rows may be padded (stride(0) >= columns).  Queues on ``stream`` (a
+    torch stream) or the current stream; raises SgemmError on a non-zero
+    status.
+    """
+    import torch
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape), tuple(C.shape)))
+    s = stream if stream is not None else torch.cuda.current_stream(C.device)
+    rc = _lib.sgemm_f32_variant(variant, M, N, K, alpha, A.data_ptr(), _ld(A, "A"),
+                                B.data_ptr(), _ld(B, "B"), beta, C.data_ptr(), _ld(C, "C"),
+                                s.cuda_stream)
+    if rc != 0:
+        raise SgemmError(rc)
+    return C

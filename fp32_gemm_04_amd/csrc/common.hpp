@@ -1,0 +1,57 @@
+// Shared device-side pieces of the SGEMM kernels: argument block, vector
+// type, and the workgroup -> output-tile mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgemm {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Everything a tile kernel needs.  Leading dimensions are 64-bit so that
+// row*ld never overflows, whatever the matrix size.
+struct GemmArgs {
+    const float *A;
+    const float *B;
+    float *C;
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+    float alpha, beta;
+    int tiles_m, tiles_n;  // output tiles along M and N
+    int group_m;           // tile rows per raster group (L2 reuse)
+};
+
+// Number of XCDs (accelerator complex dies) on MI355X.  The hardware hands
+// consecutive workgroup ids to the XCDs in turn, and each XCD has its own L2.
+constexpr int kNumXcd = 8;
+
+// Map a workgroup id to the output tile (tm, tn) it computes.
+//
+// Step 1 (XCD-aware): workgroups b, b+8, b+16, ... all run on one XCD, so
+// they are given one contiguous range of logical tile numbers; tiles that
+// share rows of A and columns of B then meet in the same L2.  The mapping
+// is a bijection on [0, nblocks) for any nblocks.
+// Step 2 (grouped raster): logical tiles walk down `group_m` tile rows before
+// moving one tile column right, so the tiles resident at one time form a
+// compact rectangle rather than a long strip.
+__device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
+                                              int group_m, int &tm, int &tn)
+{
+    const int nblocks = tiles_m * tiles_n;
+    const int q = nblocks / kNumXcd;
+    const int r = nblocks % kNumXcd;
+    const int x = bid % kNumXcd;
+    const int i = bid / kNumXcd;
+    const int logical = x * q + (x < r ? x : r) + i;
+
+    const int per_group = group_m * tiles_n;
+    const int group = logical / per_group;
+    const int first_m = group * group_m;
+    const int rows = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+    const int in_group = logical - group * per_group;
+    tm = first_m + in_group % rows;
+    tn = in_group / rows;
+}
+
+}  // namespace sgemm

@@ -1,0 +1,213 @@
+// fp32 matrix-core (MFMA) tile kernel for gfx950.
+//
+// Prior art: the block-tiled kernels of the NVIDIA_SGEMM_PRACTICE README
+// (kernels 2-7: shared-memory slabs, 2-D tiles per thread, 128-bit loads,
+// double-buffered prefetch) and the "Advanced" kernel of the cnblogs
+// matmul_opt.cu post (BM x BN x BK slabs, double buffer, one barrier per
+// slab, zero-filled masked edge loads).  Those were written for NVIDIA SIMT
+// cores; here the inner product runs on the CDNA matrix cores with
+// v_mfma_f32_16x16x4_f32 (fp32 in, fp32 accumulate, no down-conversion) and
+// each 64-lane wave owns a (BM/WM) x (BN/WN) sub-tile of the output.
+//
+// One workgroup computes one BM x BN tile of C:
+//   1. K is walked in slabs of BK.  The A slab (BM x BK) and B slab
+//      (BK x BN) are fetched from HBM with 128-bit loads when alignment
+//      allows (32-bit otherwise), zero-filled outside the matrix, and kept
+//      in registers until the current slab's math is done (prefetch).
+//   2. They are written to one of two LDS buffers (ping-pong), so one
+//      barrier per slab suffices: the buffer being written was last read
+//      before the previous barrier.
+//   3. Each wave reads its MFMA operands from LDS and issues FM x FN
+//      independent 16x16x4 MFMAs per k-step into FM x FN accumulators.
+//   4. Epilogue: C = alpha*acc + beta*C, with C not read when beta == 0,
+//      stores masked to the M x N window.
+//
+// MFMA operand layout (v_mfma_f32_16x16x4_f32, 64 lanes, lane l):
+//   A operand: one float, A[row = l%16][k = l/16]
+//   B operand: one float, B[k = l/16][col = l%16]
+//   D (4 floats): D[row = 4*(l/16) + i][col = l%16], i = 0..3
+// The contraction index may be permuted freely as long as A and B agree, so
+// within a 16-wide k chunk lane group g = l/16 takes k = 4g + s at step s.
+// That makes a lane's four A values for steps s = 0..3 contiguous in an
+// m-major LDS row: one 128-bit LDS read feeds four MFMAs.
+//
+// LDS layout (floats):
+//   A slab: m-major, row pitch SA = BK + 4.  A 128-bit read by 16 lanes of
+//           consecutive m starts at m*SA; SA = 4*odd spreads the 16 rows
+//           over all 64 banks, so the read is conflict-free.
+//   B slab: k-major, row pitch SB = BN + 4.  Lanes of group g read row
+//           4g + s; the +4 shifts each group to its own 16 banks.
+#pragma once
+
+#include "common.hpp"
+
+namespace sgemm {
+
+// Four consecutive floats p[0..3] of one matrix row, zero where the row is
+// out of range or a column is >= limit.  With VEC the caller guarantees that
+// p is 16-byte aligned whenever col is a multiple of 4.
+template <bool VEC>
+__device__ __forceinline__ f32x4 load4_masked(const float *__restrict__ p, bool row_ok,
+                                              int col, int limit)
+{
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (row_ok) {
+        if (VEC && col + 3 < limit) {
+            v = *reinterpret_cast<const f32x4 *>(p);
+        } else {
+            if (col < limit) v.x = p[0];
+            if (col + 1 < limit) v.y = p[1];
+            if (col + 2 < limit) v.z = p[2];
+            if (col + 3 < limit) v.w = p[3];
+        }
+    }
+    return v;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool AVEC, bool BVEC>
+__global__ void __launch_bounds__(WM *WN * 64)
+mfma_tile_kernel(GemmArgs g)
+{
+    constexpr int NT = WM * WN * 64;  // threads per workgroup
+    constexpr int TM = BM / WM;       // wave sub-tile rows
+    constexpr int TN = BN / WN;       // wave sub-tile columns
+    constexpr int FM = TM / 16;       // 16x16 MFMA blocks per wave, along M
+    constexpr int FN = TN / 16;       // ... along N
+    constexpr int SA = BK + 4;        // LDS pitch of an A slab row (m-major)
+    constexpr int SB = BN + 4;        // LDS pitch of a B slab row (k-major)
+    constexpr int AQ = BK / 4;        // float4 per A slab row
+    constexpr int BQ = BN / 4;        // float4 per B slab row
+    constexpr int NA = BM * AQ / NT;  // float4 global loads per thread, A
+    constexpr int NB = BK * BQ / NT;  // float4 global loads per thread, B
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert(BK % 16 == 0, "BK must be a multiple of 16");
+    static_assert((BM * AQ) % NT == 0 && (BK * BQ) % NT == 0, "slab must split evenly");
+    static_assert(BN % 16 == 0, "B pitch needs BN % 16 == 0 for conflict-free reads");
+
+    __shared__ __attribute__((aligned(16))) float As[2][BM * SA];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK * SB];
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int M = g.M, N = g.N, K = g.K;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wr = wave / WN;
+    const int wc = wave % WN;
+    const int lm = lane & 15;  // row (A) / column (B, D) inside a 16-block
+    const int lg = lane >> 4;  // k group (A, B) / row group (D)
+
+    // Where this thread's slab loads come from and go to.
+    int a_row[NA], a_col[NA];
+    bool a_ok[NA];
+    const float *a_src[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const int f = tid + i * NT;
+        a_row[i] = f / AQ;
+        a_col[i] = (f % AQ) * 4;
+        a_ok[i] = m0 + a_row[i] < M;
+        a_src[i] = g.A + (int64_t)(m0 + a_row[i]) * g.lda + a_col[i];
+    }
+    int b_row[NB], b_col[NB];
+    const float *b_src[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int f = tid + i * NT;
+        b_row[i] = f / BQ;
+        b_col[i] = (f % BQ) * 4;
+        b_src[i] = g.B + (int64_t)b_row[i] * g.ldb + n0 + b_col[i];
+    }
+
+    f32x4 ra[NA], rb[NB];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+            ra[i] = load4_masked<AVEC>(a_src[i] + k0, a_ok[i], k0 + a_col[i], K);
+        const int64_t boff = (int64_t)k0 * g.ldb;
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            rb[i] = load4_masked<BVEC>(b_src[i] + boff, k0 + b_row[i] < K, n0 + b_col[i], N);
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+            *reinterpret_cast<f32x4 *>(&As[buf][a_row[i] * SA + a_col[i]]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            *reinterpret_cast<f32x4 *>(&Bs[buf][b_row[i] * SB + b_col[i]]) = rb[i];
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int buf) {
+        const float *as = &As[buf][(wr * TM + lm) * SA + 4 * lg];
+        const float *bs = &Bs[buf][(4 * lg) * SB + wc * TN + lm];
+#pragma unroll
+        for (int q = 0; q < BK / 16; ++q) {
+            f32x4 af[FM];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                af[fm] = *reinterpret_cast<const f32x4 *>(as + fm * 16 * SA + 16 * q);
+            float bf[4][FN];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    bf[s][fn] = bs[(16 * q + s) * SB + fn * 16];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            af[fm][s], bf[s][fn], acc[fm][fn], 0, 0, 0);
+        }
+    };
+
+    const int nslab = (K + BK - 1) / BK;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int t = 0; t < nslab; ++t) {
+        const int cur = t & 1;
+        const bool more = t + 1 < nslab;
+        if (more) fetch((t + 1) * BK);
+        compute(cur);
+        if (more) stash(cur ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: C = alpha*acc + beta*C over the valid window.
+    const float alpha = g.alpha, beta = g.beta;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + wr * TM + fm * 16 + 4 * lg + i;
+            if (row >= M) continue;
+            float *crow = g.C + (int64_t)row * g.ldc;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int col = n0 + wc * TN + fn * 16 + lm;
+                if (col < N) {
+                    float v = alpha * acc[fm][fn][i];
+                    if (beta != 0.f) v = fmaf(beta, crow[col], v);
+                    crow[col] = v;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace sgemm

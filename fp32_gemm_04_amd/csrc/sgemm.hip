@@ -1,0 +1,276 @@
+// libsgemm host side: argument checks, the shape-driven tile selector and
+// kernel launches behind the C ABI declared in include/sgemm.h.
+//
+// Every kernel lives in the headers included below; this file only decides
+// which one runs and with what grid.  No call here allocates, frees, copies
+// or synchronises: work is queued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/sgemm.h"
+#include "common.hpp"
+#include "mfma_tile.hpp"
+#include "valu_tile.hpp"
+
+namespace sgemm {
+namespace {
+
+typedef void (*KernelFn)(GemmArgs);
+
+// One entry of the tile table.
+struct TileConfig {
+    const char *family;  // "mfma" or "valu"
+    int bm, bn, bk;      // workgroup tile and K slab
+    int wm, wn;          // wave grid inside the workgroup
+    int threads;         // workgroup size the kernel is compiled for
+    int occupancy;       // workgroups that fit on one CU (LDS/registers)
+    double efficiency;   // fraction of the CU's fp32 peak a full tile reaches
+    KernelFn fn[2][2];   // [A 128-bit loads][B 128-bit loads]
+};
+
+#define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, EFF)                                  \
+    {"mfma", BM, BN, BK, WM, WN, WM * WN * 64, OCC, EFF,                                 \
+     {{mfma_tile_kernel<BM, BN, BK, WM, WN, false, false>,                                \
+       mfma_tile_kernel<BM, BN, BK, WM, WN, false, true>},                                \
+      {mfma_tile_kernel<BM, BN, BK, WM, WN, true, false>,                                 \
+       mfma_tile_kernel<BM, BN, BK, WM, WN, true, true>}}}
+
+// The MFMA tile table.  Occupancy follows from LDS use (2 slabs of
+// BM*(BK+4) + BK*(BN+4) floats) and from the accumulator registers;
+// efficiency is the measured fraction of peak a CU reaches on a full tile.
+const TileConfig kMfmaTiles[] = {
+    SGEMM_MFMA_ENTRY(160, 160, 32, 2, 2, 1, 0.90),
+    SGEMM_MFMA_ENTRY(128, 128, 32, 2, 2, 2, 0.85),
+    SGEMM_MFMA_ENTRY(64, 64, 32, 2, 2, 4, 0.60),
+    SGEMM_MFMA_ENTRY(32, 256, 32, 1, 4, 2, 0.50),
+    SGEMM_MFMA_ENTRY(64, 256, 32, 1, 4, 2, 0.60),
+};
+
+// Four waves of 64 threads, as 16 x 16 threads with 8 x 8 outputs each.
+const TileConfig kValuTile = {"valu", 128, 128, 8, 2, 2, 256, 2, 0.45,
+                              {{valu_tile_kernel<false, false>, valu_tile_kernel<false, true>},
+                               {valu_tile_kernel<true, false>, valu_tile_kernel<true, true>}}};
+
+constexpr double kHbmBytesPerCuCycle = 8.0e12 / (256 * 2.4e9);  // MI355X HBM share
+constexpr double kFlopsPerCuCycle = 256.0;                      // fp32 MFMA per CU
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Rough time (in CU cycles) of running the problem with tile config c:
+// whole rounds of resident workgroups times the per-tile compute time, but
+// never less than the time to move the operands through HBM once.
+double estimate_cycles(const TileConfig &c, int M, int N, int K, int num_cus)
+{
+    const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
+    const int64_t slots = (int64_t)num_cus * c.occupancy;
+    const int64_t rounds = ceil_div(tiles, slots);
+    const double kpad = (double)ceil_div(K, c.bk) * c.bk;
+    const double tile_cycles = 2.0 * c.bm * c.bn * kpad / (kFlopsPerCuCycle * c.efficiency);
+    // A round runs `occupancy` tiles per CU side by side, sharing its MFMA pipes.
+    const double compute = (double)rounds * tile_cycles * c.occupancy;
+    const double bytes = 4.0 * ((double)M * K + (double)K * N + (double)M * N);
+    const double memory = bytes / (kHbmBytesPerCuCycle * num_cus);
+    return compute > memory ? compute : memory;
+}
+
+const TileConfig *select_tile(int variant, int M, int N, int K, int num_cus)
+{
+    if (variant == SGEMM_VARIANT_VALU) return &kValuTile;
+    if (variant >= SGEMM_VARIANT_MFMA_TILE) return &kMfmaTiles[variant - SGEMM_VARIANT_MFMA_TILE];
+    const TileConfig *best = nullptr;
+    double best_cycles = 0.0;
+    for (const TileConfig &c : kMfmaTiles) {
+        const double cyc = estimate_cycles(c, M, N, K, num_cus);
+        if (best == nullptr || cyc < best_cycles) {
+            best = &c;
+            best_cycles = cyc;
+        }
+    }
+    return best;
+}
+
+// Tile rows per raster group: enough rows that the tiles one XCD holds at
+// once (its 32 CUs times occupancy) form a roughly square patch.
+int group_rows(const TileConfig &c, int tiles_m, int tiles_n, int num_cus)
+{
+    const int resident = (num_cus / kNumXcd > 0 ? num_cus / kNumXcd : 1) * c.occupancy;
+    int gm = 1;
+    while (gm * gm < resident) ++gm;
+    if (gm > tiles_m) gm = tiles_m;
+    (void)tiles_n;
+    return gm > 0 ? gm : 1;
+}
+
+// Argument checks of the C ABI (no HIP call).  Returns 0 or -p.
+int check_args(int M, int N, int K, float alpha, const void *A, int lda, const void *B,
+               int ldb, const void *C, int ldc, bool check_pointers)
+{
+    if (M < 0) return -1;
+    if (N < 0) return -2;
+    if (K < 0) return -3;
+    const bool reads_ab = alpha != 0.0f && K > 0 && M > 0 && N > 0;
+    if (check_pointers && reads_ab && (A == nullptr || ((uintptr_t)A & 3u) != 0)) return -5;
+    if (lda < (K > 1 ? K : 1)) return -6;
+    if (check_pointers && reads_ab && (B == nullptr || ((uintptr_t)B & 3u) != 0)) return -7;
+    if (ldb < (N > 1 ? N : 1)) return -8;
+    if (check_pointers && M > 0 && N > 0 && (C == nullptr || ((uintptr_t)C & 3u) != 0))
+        return -10;
+    if (ldc < (N > 1 ? N : 1)) return -11;
+    return 0;
+}
+
+constexpr int kNumMfmaTiles = (int)(sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]));
+
+bool valid_variant(int v)
+{
+    return v == SGEMM_VARIANT_AUTO || v == SGEMM_VARIANT_MFMA || v == SGEMM_VARIANT_VALU ||
+           (v >= SGEMM_VARIANT_MFMA_TILE && v < SGEMM_VARIANT_MFMA_TILE + kNumMfmaTiles);
+}
+
+// Per-device compute-unit count, queried once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cus[kMaxDevices];
+
+hipError_t device_cus(int *cus)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int cached = g_num_cus[dev].load(std::memory_order_relaxed);
+        if (cached > 0) {
+            *cus = cached;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n < 1) n = 1;
+    if (dev >= 0 && dev < kMaxDevices) g_num_cus[dev].store(n, std::memory_order_relaxed);
+    *cus = n;
+    return hipSuccess;
+}
+
+bool is_vec_ok(const void *p, int ld) { return ((uintptr_t)p & 15u) == 0 && (ld & 3) == 0; }
+
+int launch(int variant, int M, int N, int K, float alpha, const float *A, int lda,
+           const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream)
+{
+    if (!valid_variant(variant)) return SGEMM_ERR_BAD_VARIANT;
+    const int bad = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
+    if (bad != 0) return bad;
+    if (M == 0 || N == 0) return 0;
+
+    if (K == 0 || alpha == 0.0f) {
+        const int64_t total = (int64_t)M * N;
+        int64_t blocks = ceil_div(total, 256);
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL(scale_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, C,
+                           (int64_t)ldc, M, N, beta);
+        return (int)hipGetLastError();
+    }
+
+    int cus = 0;
+    const hipError_t e = device_cus(&cus);
+    if (e != hipSuccess) return (int)e;
+
+    const TileConfig *c = select_tile(variant, M, N, K, cus);
+    GemmArgs g;
+    g.A = A;
+    g.B = B;
+    g.C = C;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.ldc = ldc;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.alpha = alpha;
+    g.beta = beta;
+    g.tiles_m = (int)ceil_div(M, c->bm);
+    g.tiles_n = (int)ceil_div(N, c->bn);
+    g.group_m = group_rows(*c, g.tiles_m, g.tiles_n, cus);
+    const int64_t blocks = (int64_t)g.tiles_m * g.tiles_n;
+    if (blocks > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
+    const int threads = c->threads;
+    const KernelFn fn = c->fn[is_vec_ok(A, lda)][is_vec_ok(B, ldb)];
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), 0, stream, g);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+}  // namespace sgemm
+
+extern "C" int sgemm_f32(int M, int N, int K, float alpha, const float *A, int lda,
+                         const float *B, int ldb, float beta, float *C, int ldc,
+                         hipStream_t stream)
+{
+    return sgemm::launch(SGEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         stream);
+}
+
+extern "C" int sgemm_f32_variant(int variant, int M, int N, int K, float alpha,
+                                 const float *A, int lda, const float *B, int ldb,
+                                 float beta, float *C, int ldc, hipStream_t stream)
+{
+    return sgemm::launch(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, int ldc,
+                          float alpha, int num_cus, char *buf, int buflen)
+{
+    using namespace sgemm;
+    if (!valid_variant(variant)) return SGEMM_ERR_BAD_VARIANT;
+    const int bad = check_args(M, N, K, alpha, nullptr, lda, nullptr, ldb, nullptr, ldc, false);
+    if (bad != 0) return bad;
+    if (num_cus < 1 || (buf == nullptr && buflen > 0) || buflen < 0) return -12;
+    char text[160];
+    if (M == 0 || N == 0) {
+        std::snprintf(text, sizeof text, "none");
+    } else if (K == 0 || alpha == 0.0f) {
+        std::snprintf(text, sizeof text, "scale m=%d n=%d", M, N);
+    } else {
+        const TileConfig *c = select_tile(variant, M, N, K, num_cus);
+        const int tiles_m = (int)ceil_div(M, c->bm);
+        const int tiles_n = (int)ceil_div(N, c->bn);
+        std::snprintf(text, sizeof text,
+                      "%s bm=%d bn=%d bk=%d waves=%dx%d vecA=%d vecB=%d grid=%lld group=%d",
+                      c->family, c->bm, c->bn, c->bk, c->wm, c->wn, (lda & 3) == 0,
+                      (ldb & 3) == 0, (long long)tiles_m * tiles_n,
+                      group_rows(*c, tiles_m, tiles_n, num_cus));
+    }
+    if (buflen > 0) {
+        std::strncpy(buf, text, (size_t)buflen - 1);
+        buf[buflen - 1] = '\0';
+    }
+    return 0;
+}
+
+extern "C" int sgemm_num_mfma_tiles(void) { return sgemm::kNumMfmaTiles; }
+
+extern "C" const char *sgemm_status_string(int status)
+{
+    switch (status) {
+    case 0: return "success";
+    case -1: return "invalid M (negative)";
+    case -2: return "invalid N (negative)";
+    case -3: return "invalid K (negative)";
+    case -5: return "invalid A (NULL or not 4-byte aligned)";
+    case -6: return "invalid lda (< max(1, K))";
+    case -7: return "invalid B (NULL or not 4-byte aligned)";
+    case -8: return "invalid ldb (< max(1, N))";
+    case -10: return "invalid C (NULL or not 4-byte aligned)";
+    case -11: return "invalid ldc (< max(1, N))";
+    case -12: return "invalid plan arguments (num_cus < 1 or no buffer)";
+    case SGEMM_ERR_BAD_VARIANT: return "unknown kernel variant";
+    default: break;
+    }
+    if (status > 0) return hipGetErrorString((hipError_t)status);
+    return "unknown status";
+}

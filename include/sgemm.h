@@ -1,0 +1,124 @@
+/*
+ * libsgemm -- single-precision GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every entry point takes plain sizes, scalars and device pointers;
+ * nothing here depends on PyTorch.
+ *
+ * The operation is the one every SGEMM kernel of the NVIDIA_SGEMM_PRACTICE
+ * README computes (kernel 1 section: C = alpha * A*B + beta * C), on
+ * row-major fp32 matrices addressed the way that README's OFFSET(row, col,
+ * ld) macro does (kernel 6 section): element (r, c) of a matrix with leading
+ * dimension ld lives at index r*ld + c.
+ */
+#ifndef LIBSGEMM_SGEMM_H
+#define LIBSGEMM_SGEMM_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Kernel families for sgemm_f32_variant(). */
+enum sgemm_variant {
+    SGEMM_VARIANT_AUTO = 0, /* shape-driven selection (what sgemm_f32 does) */
+    SGEMM_VARIANT_MFMA = 1, /* fp32 matrix-core tile kernel, tile chosen by shape */
+    SGEMM_VARIANT_VALU = 2, /* vector-FMA register-tile kernel (8x8 per thread) */
+    /* SGEMM_VARIANT_MFMA_TILE + i forces entry i of the MFMA tile table
+     * (0 <= i < sgemm_num_mfma_tiles()), bypassing the selector; sgemm_plan
+     * names the tile.  For tests and tuning. */
+    SGEMM_VARIANT_MFMA_TILE = 16
+};
+
+/* Status values other than 0 and the hipError_t codes. */
+#define SGEMM_ERR_BAD_VARIANT (-100)
+
+/*
+ * sgemm_f32 -- C <- alpha * A * B + beta * C, all row-major fp32.
+ *
+ *   M, N, K   sizes: A is M x K, B is K x N, C is M x N.  Each must be >= 0.
+ *   alpha     scale of the product.  alpha == 0: A and B are not read.
+ *   A, lda    device pointer to A(0,0); A(i,k) is A[i*lda + k]; lda >= max(1,K).
+ *   B, ldb    device pointer to B(0,0); B(k,j) is B[k*ldb + j]; ldb >= max(1,N).
+ *   beta      scale of the old C.  beta == 0: C is written but not read, so
+ *             NaN or Inf already in C does not reach the result.
+ *   C, ldc    device pointer to C(0,0); C(i,j) is C[i*ldc + j]; ldc >= max(1,N).
+ *             Only the M x N window is read or written; padding between
+ *             rows is never touched.  C must not overlap A or B.
+ *   stream    HIP stream the work is queued on (0 = the null stream).
+ *
+ * Ownership and synchronisation: all buffers belong to the caller and stay
+ * on the current HIP device.  The call allocates, frees, copies and
+ * synchronises nothing; it queues kernels on `stream` and returns.  Results
+ * are visible once the stream has been synchronised.
+ *
+ * Pointers need only float (4-byte) alignment; 16-byte aligned operands
+ * with leading dimensions divisible by 4 take 128-bit load paths.
+ *
+ * Quick returns: M == 0 or N == 0 does nothing and returns 0 without any
+ * HIP call.  K == 0 or alpha == 0 scales C by beta (beta == 0: C <- 0).
+ *
+ * Returns 0 on success; -p when parameter p (counting M as 1) is invalid:
+ *   -1 M < 0,  -2 N < 0,  -3 K < 0,
+ *   -5 A is NULL (while M*K > 0 and alpha != 0) or not 4-byte aligned,
+ *   -6 lda < max(1,K),
+ *   -7 B is NULL (while K*N > 0 and alpha != 0) or not 4-byte aligned,
+ *   -8 ldb < max(1,N),
+ *  -10 C is NULL (while M*N > 0) or not 4-byte aligned,
+ *  -11 ldc < max(1,N);
+ * all argument checks happen before any HIP call.  A positive value is the
+ * hipError_t of a failed HIP call (device query or kernel launch); in that
+ * case nothing was queued.
+ *
+ * Accuracy: each element is a fp32 sum of fp32 products (matrix-core
+ * accumulation) scaled by alpha plus beta times the old value.  It is
+ * within 1e-5 * (|alpha| * sum_k |A(i,k) B(k,j)| + |beta C(i,j)|) + 1e-6 of
+ * the exact result for data like the benchmark's, and exact for integer
+ * data whose partial sums stay below 2^24.
+ *
+ * Thread safety: re-entrant; the only shared state is a per-device cache of
+ * the compute-unit count, filled once.
+ */
+int sgemm_f32(int M, int N, int K, float alpha, const float *A, int lda,
+              const float *B, int ldb, float beta, float *C, int ldc,
+              hipStream_t stream);
+
+/*
+ * sgemm_f32_variant -- as sgemm_f32, but with the kernel family forced to
+ * `variant` (enum sgemm_variant).  This mirrors the page-2 driver's
+ * GEMM_MODE switch (UNIVERSAL_SGEMM_CUDA README, "Results" section), which
+ * picks one kernel of the optimisation ladder per run; it exists to
+ * benchmark and test each family on its own.  SGEMM_VARIANT_AUTO behaves
+ * exactly like sgemm_f32.  Returns SGEMM_ERR_BAD_VARIANT for an unknown
+ * variant (checked first), otherwise exactly what sgemm_f32 returns.
+ */
+int sgemm_f32_variant(int variant, int M, int N, int K, float alpha,
+                      const float *A, int lda, const float *B, int ldb,
+                      float beta, float *C, int ldc, hipStream_t stream);
+
+/*
+ * sgemm_plan -- describe, without touching any GPU, the kernel that
+ * sgemm_f32_variant would launch for this problem on a device with
+ * `num_cus` compute units, assuming 16-byte aligned base pointers.
+ * Writes a NUL-terminated text such as
+ *   "mfma bm=160 bn=160 bk=32 waves=2x2 vecA=1 vecB=1 grid=1024"
+ * into buf (at most buflen bytes, truncated if needed).  The leading word
+ * names the kernel: "none" (nothing to do), "scale" (K == 0 or alpha == 0),
+ * "mfma" or "valu".  Returns 0, or the same negative codes as sgemm_f32
+ * (pointer checks excepted), SGEMM_ERR_BAD_VARIANT, or -12 when num_cus < 1
+ * or buf is NULL with buflen > 0.
+ */
+int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, int ldc,
+               float alpha, int num_cus, char *buf, int buflen);
+
+/* Number of entries in the MFMA tile table (see SGEMM_VARIANT_MFMA_TILE). */
+int sgemm_num_mfma_tiles(void);
+
+/* Short English text for a status value returned above (never NULL). */
+const char *sgemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSGEMM_SGEMM_H */
