@@ -21,6 +21,9 @@
 //      independent 16x16x4 MFMAs per k-step into FM x FN accumulators.
 //   4. Epilogue: C = alpha*acc + beta*C, with C not read when beta == 0,
 //      stores masked to the M x N window.
+// Workgroups whose tile lies wholly inside C with 16-byte aligned operands
+// take an unmasked copy of the loop (only a ragged last K slab is masked);
+// edge tiles take the fully masked copy.
 //
 // MFMA operand layout (v_mfma_f32_16x16x4_f32, 64 lanes, lane l):
 //   A operand: one float, A[row = l%16][k = l/16]
@@ -64,33 +67,38 @@ __device__ __forceinline__ f32x4 load4_masked(const float *__restrict__ p, bool 
     return v;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool AVEC, bool BVEC>
-__global__ void __launch_bounds__(WM *WN * 64)
-mfma_tile_kernel(GemmArgs g)
-{
-    constexpr int NT = WM * WN * 64;  // threads per workgroup
-    constexpr int TM = BM / WM;       // wave sub-tile rows
-    constexpr int TN = BN / WN;       // wave sub-tile columns
-    constexpr int FM = TM / 16;       // 16x16 MFMA blocks per wave, along M
-    constexpr int FN = TN / 16;       // ... along N
-    constexpr int SA = BK + 4;        // LDS pitch of an A slab row (m-major)
-    constexpr int SB = BN + 4;        // LDS pitch of a B slab row (k-major)
-    constexpr int AQ = BK / 4;        // float4 per A slab row
-    constexpr int BQ = BN / 4;        // float4 per B slab row
-    constexpr int NA = BM * AQ / NT;  // float4 global loads per thread, A
-    constexpr int NB = BK * BQ / NT;  // float4 global loads per thread, B
+template <int BM, int BN, int BK, int WM, int WN>
+struct MfmaTile {
+    static constexpr int NT = WM * WN * 64;  // threads per workgroup
+    static constexpr int TM = BM / WM;       // wave sub-tile rows
+    static constexpr int TN = BN / WN;       // wave sub-tile columns
+    static constexpr int FM = TM / 16;       // 16x16 MFMA blocks per wave, along M
+    static constexpr int FN = TN / 16;       // ... along N
+    static constexpr int SA = BK + 4;        // LDS pitch of an A slab row (m-major)
+    static constexpr int SB = BN + 4;        // LDS pitch of a B slab row (k-major)
+    static constexpr int AQ = BK / 4;        // float4 per A slab row
+    static constexpr int BQ = BN / 4;        // float4 per B slab row
+    static constexpr int A4 = BM * AQ;       // float4 per A slab
+    static constexpr int B4 = BK * BQ;       // float4 per B slab
+    static constexpr int NA = (A4 + NT - 1) / NT;  // A float4 per thread (last may idle)
+    static constexpr int NB = (B4 + NT - 1) / NT;
+    static constexpr int LDS_A = BM * SA;    // floats per A buffer
+    static constexpr int LDS_B = BK * SB;
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert(BK % 16 == 0, "BK must be a multiple of 16");
-    static_assert((BM * AQ) % NT == 0 && (BK * BQ) % NT == 0, "slab must split evenly");
     static_assert(BN % 16 == 0, "B pitch needs BN % 16 == 0 for conflict-free reads");
+};
 
-    __shared__ __attribute__((aligned(16))) float As[2][BM * SA];
-    __shared__ __attribute__((aligned(16))) float Bs[2][BK * SB];
-
-    int tm, tn;
-    tile_of_block(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
+// The slab pipeline and epilogue of one workgroup.  EDGE selects masked
+// loads of rows/columns (tiles crossing the matrix border or unaligned
+// operands); with EDGE false only a ragged last K slab is masked.
+template <int BM, int BN, int BK, int WM, int WN, bool AVEC, bool BVEC, bool EDGE>
+__device__ __forceinline__ void mfma_tile_body(const GemmArgs &g, int m0, int n0, float *As,
+                                               float *Bs)
+{
+    using T = MfmaTile<BM, BN, BK, WM, WN>;
+    constexpr int NT = T::NT, TM = T::TM, TN = T::TN, FM = T::FM, FN = T::FN;
+    constexpr int SA = T::SA, SB = T::SB, AQ = T::AQ, BQ = T::BQ, NA = T::NA, NB = T::NB;
     const int M = g.M, N = g.N, K = g.K;
 
     const int tid = threadIdx.x;
@@ -101,45 +109,69 @@ mfma_tile_kernel(GemmArgs g)
     const int lm = lane & 15;  // row (A) / column (B, D) inside a 16-block
     const int lg = lane >> 4;  // k group (A, B) / row group (D)
 
-    // Where this thread's slab loads come from and go to.
-    int a_row[NA], a_col[NA];
-    bool a_ok[NA];
+    // Where this thread's slab loads come from (global) and go to (LDS).
+    int a_lds[NA], b_lds[NB], a_col[NA], b_row[NB], b_col[NB];
+    bool a_ok[NA], a_use[NA], b_ok[NB], b_use[NB];
     const float *a_src[NA];
+    const float *b_src[NB];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         const int f = tid + i * NT;
-        a_row[i] = f / AQ;
-        a_col[i] = (f % AQ) * 4;
-        a_ok[i] = m0 + a_row[i] < M;
-        a_src[i] = g.A + (int64_t)(m0 + a_row[i]) * g.lda + a_col[i];
+        a_use[i] = (T::A4 % NT == 0) || f < T::A4;
+        const int r = (a_use[i] ? f : 0) / AQ;
+        a_col[i] = ((a_use[i] ? f : 0) % AQ) * 4;
+        a_lds[i] = r * SA + a_col[i];
+        a_ok[i] = m0 + r < M;
+        a_src[i] = g.A + (int64_t)(m0 + r) * g.lda + a_col[i];
     }
-    int b_row[NB], b_col[NB];
-    const float *b_src[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         const int f = tid + i * NT;
-        b_row[i] = f / BQ;
-        b_col[i] = (f % BQ) * 4;
+        b_use[i] = (T::B4 % NT == 0) || f < T::B4;
+        b_row[i] = (b_use[i] ? f : 0) / BQ;
+        b_col[i] = ((b_use[i] ? f : 0) % BQ) * 4;
+        b_lds[i] = b_row[i] * SB + b_col[i];
+        b_ok[i] = n0 + b_col[i] < N;
         b_src[i] = g.B + (int64_t)b_row[i] * g.ldb + n0 + b_col[i];
     }
 
     f32x4 ra[NA], rb[NB];
-    auto fetch = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < NA; ++i)
-            ra[i] = load4_masked<AVEC>(a_src[i] + k0, a_ok[i], k0 + a_col[i], K);
+    // Unmasked fetch: tile inside C, aligned operands, full K slab.
+    auto fetch_fast = [&](int k0) {
         const int64_t boff = (int64_t)k0 * g.ldb;
 #pragma unroll
+        for (int i = 0; i < NA; ++i)
+            if (a_use[i]) ra[i] = *reinterpret_cast<const f32x4 *>(a_src[i] + k0);
+#pragma unroll
         for (int i = 0; i < NB; ++i)
-            rb[i] = load4_masked<BVEC>(b_src[i] + boff, k0 + b_row[i] < K, n0 + b_col[i], N);
+            if (b_use[i]) rb[i] = *reinterpret_cast<const f32x4 *>(b_src[i] + boff);
     };
-    auto stash = [&](int buf) {
+    auto fetch_masked = [&](int k0) {
+        const int64_t boff = (int64_t)k0 * g.ldb;
 #pragma unroll
         for (int i = 0; i < NA; ++i)
-            *reinterpret_cast<f32x4 *>(&As[buf][a_row[i] * SA + a_col[i]]) = ra[i];
+            if (a_use[i]) ra[i] = load4_masked<AVEC>(a_src[i] + k0, a_ok[i], k0 + a_col[i], K);
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            *reinterpret_cast<f32x4 *>(&Bs[buf][b_row[i] * SB + b_col[i]]) = rb[i];
+            if (b_use[i])
+                rb[i] = load4_masked<BVEC>(b_src[i] + boff, k0 + b_row[i] < K && b_ok[i],
+                                           n0 + b_col[i], N);
+    };
+    auto fetch = [&](int k0) {
+        if (!EDGE && k0 + BK <= K)
+            fetch_fast(k0);
+        else
+            fetch_masked(k0);
+    };
+    auto stash = [&](int buf) {
+        float *as = As + buf * T::LDS_A;
+        float *bs = Bs + buf * T::LDS_B;
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+            if (a_use[i]) *reinterpret_cast<f32x4 *>(as + a_lds[i]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            if (b_use[i]) *reinterpret_cast<f32x4 *>(bs + b_lds[i]) = rb[i];
     };
 
     f32x4 acc[FM][FN];
@@ -149,9 +181,11 @@ mfma_tile_kernel(GemmArgs g)
         for (int fn = 0; fn < FN; ++fn)
             acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    const int a_frag = (wr * TM + lm) * SA + 4 * lg;
+    const int b_frag = (4 * lg) * SB + wc * TN + lm;
     auto compute = [&](int buf) {
-        const float *as = &As[buf][(wr * TM + lm) * SA + 4 * lg];
-        const float *bs = &Bs[buf][(4 * lg) * SB + wc * TN + lm];
+        const float *as = As + buf * T::LDS_A + a_frag;
+        const float *bs = Bs + buf * T::LDS_B + b_frag;
 #pragma unroll
         for (int q = 0; q < BK / 16; ++q) {
             f32x4 af[FM];
@@ -195,12 +229,12 @@ mfma_tile_kernel(GemmArgs g)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = m0 + wr * TM + fm * 16 + 4 * lg + i;
-            if (row >= M) continue;
+            if (EDGE && row >= M) continue;
             float *crow = g.C + (int64_t)row * g.ldc;
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
                 const int col = n0 + wc * TN + fn * 16 + lm;
-                if (col < N) {
+                if (!EDGE || col < N) {
                     float v = alpha * acc[fm][fn][i];
                     if (beta != 0.f) v = fmaf(beta, crow[col], v);
                     crow[col] = v;
@@ -208,6 +242,27 @@ mfma_tile_kernel(GemmArgs g)
             }
         }
     }
+}
+
+// WPE: waves per SIMD the register allocation must allow (the kernel is
+// meant to run OCC = WPE * 4 / (WM*WN) workgroups per CU).
+template <int BM, int BN, int BK, int WM, int WN, int WPE, bool AVEC, bool BVEC>
+__global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+mfma_tile_kernel(GemmArgs g)
+{
+    using T = MfmaTile<BM, BN, BK, WM, WN>;
+    __shared__ __attribute__((aligned(16))) float As[2 * T::LDS_A];
+    __shared__ __attribute__((aligned(16))) float Bs[2 * T::LDS_B];
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const bool interior = AVEC && BVEC && m0 + BM <= g.M && n0 + BN <= g.N;
+    if (interior)
+        mfma_tile_body<BM, BN, BK, WM, WN, AVEC, BVEC, false>(g, m0, n0, As, Bs);
+    else
+        mfma_tile_body<BM, BN, BK, WM, WN, AVEC, BVEC, true>(g, m0, n0, As, Bs);
 }
 
 }  // namespace sgemm

@@ -33,25 +33,28 @@ struct TileConfig {
     KernelFn fn[2][2];   // [A 128-bit loads][B 128-bit loads]
 };
 
-#define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, EFF)                                  \
-    {"mfma", BM, BN, BK, WM, WN, WM * WN * 64, OCC, EFF,                                 \
-     {{mfma_tile_kernel<BM, BN, BK, WM, WN, false, false>,                                \
-       mfma_tile_kernel<BM, BN, BK, WM, WN, false, true>},                                \
-      {mfma_tile_kernel<BM, BN, BK, WM, WN, true, false>,                                 \
-       mfma_tile_kernel<BM, BN, BK, WM, WN, true, true>}}}
+// WPE (waves per SIMD) = OCC workgroups per CU x waves per workgroup / 4 SIMDs.
+#define SGEMM_MFMA_WPE(WM, WN, OCC) ((OCC) * (WM) * (WN) / 4)
+#define SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, AV, BV) \
+    mfma_tile_kernel<BM, BN, BK, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), AV, BV>
+#define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, EFF)                          \
+    {"mfma", BM, BN, BK, WM, WN, WM * WN * 64, OCC, EFF,                         \
+     {{SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, false, false),                 \
+       SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, false, true)},                 \
+      {SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, true, false),                  \
+       SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, true, true)}}}
 
-// The MFMA tile table.  Occupancy follows from LDS use (2 slabs of
-// BM*(BK+4) + BK*(BN+4) floats) and from the accumulator registers;
-// efficiency is the measured fraction of peak a CU reaches on a full tile.
+// The MFMA tile table.  Occupancy (workgroups per CU) is what LDS (two
+// slabs of BM*(BK+4) + BK*(BN+4) floats) and the register budget it implies
+// allow; efficiency is the fraction of peak a CU reaches on a full tile.
 const TileConfig kMfmaTiles[] = {
-    SGEMM_MFMA_ENTRY(160, 160, 32, 2, 2, 1, 0.90),
-    SGEMM_MFMA_ENTRY(128, 128, 32, 2, 2, 2, 0.85),
+    SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 0.90),
+    SGEMM_MFMA_ENTRY(128, 128, 16, 2, 2, 2, 0.85),
     SGEMM_MFMA_ENTRY(64, 64, 32, 2, 2, 4, 0.60),
     SGEMM_MFMA_ENTRY(32, 256, 32, 1, 4, 2, 0.50),
-    SGEMM_MFMA_ENTRY(64, 256, 32, 1, 4, 2, 0.60),
+    SGEMM_MFMA_ENTRY(64, 256, 16, 1, 4, 2, 0.60),
 };
 
-// Four waves of 64 threads, as 16 x 16 threads with 8 x 8 outputs each.
 const TileConfig kValuTile = {"valu", 128, 128, 8, 2, 2, 256, 2, 0.45,
                               {{valu_tile_kernel<false, false>, valu_tile_kernel<false, true>},
                                {valu_tile_kernel<true, false>, valu_tile_kernel<true, true>}}};
