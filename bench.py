@@ -114,7 +114,7 @@ def cpu_baseline(case, A, B, C, budget_s):
 def bench_im2col(sg, stream, reps):
     """Each im2col shape: median time of `reps` launches, caches flushed between."""
     import torch
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     out = []
     for case in workloads.SKINNY + workloads.MID:
         log("im2col", case.name)
@@ -125,7 +125,7 @@ def bench_im2col(sg, stream, reps):
         assert rc == 0, sg.sgemm_status_string(rc)
         times = []
         for _ in range(reps):
-            flush.fill_(1.0)
+            flush.sum()  # evict the caches without leaving dirty lines behind
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)

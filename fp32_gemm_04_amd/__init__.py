@@ -19,8 +19,10 @@ LIBRARY = os.path.join(_HERE, "libsgemm.so")
 SGEMM_VARIANT_AUTO = 0
 SGEMM_VARIANT_MFMA = 1
 SGEMM_VARIANT_VALU = 2
+SGEMM_VARIANT_SKINNY = 3
 SGEMM_VARIANT_MFMA_TILE = 16
 SGEMM_ERR_BAD_VARIANT = -100
+SGEMM_ERR_VARIANT_SHAPE = -101
 
 EXPORTS = ("sgemm_f32", "sgemm_f32_variant", "sgemm_plan", "sgemm_num_mfma_tiles",
            "sgemm_status_string")

@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "sgemm.hip")]
-DEPENDS = [os.path.join(HERE, "csrc", f) for f in ("common.hpp", "mfma_tile.hpp", "valu_tile.hpp")]
+DEPENDS = [os.path.join(HERE, "csrc", f) for f in ("common.hpp", "mfma_tile.hpp", "skinny.hpp", "valu_tile.hpp")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libsgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

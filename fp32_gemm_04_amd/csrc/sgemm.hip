@@ -15,6 +15,7 @@
 #include "../../include/sgemm.h"
 #include "common.hpp"
 #include "mfma_tile.hpp"
+#include "skinny.hpp"
 #include "valu_tile.hpp"
 
 namespace sgemm {
@@ -132,6 +133,7 @@ constexpr int kNumMfmaTiles = (int)(sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]));
 bool valid_variant(int v)
 {
     return v == SGEMM_VARIANT_AUTO || v == SGEMM_VARIANT_MFMA || v == SGEMM_VARIANT_VALU ||
+           v == SGEMM_VARIANT_SKINNY ||
            (v >= SGEMM_VARIANT_MFMA_TILE && v < SGEMM_VARIANT_MFMA_TILE + kNumMfmaTiles);
 }
 
@@ -162,6 +164,100 @@ hipError_t device_cus(int *cus)
 
 bool is_vec_ok(const void *p, int ld) { return ((uintptr_t)p & 15u) == 0 && (ld & 3) == 0; }
 
+// The skinny streaming kernel: waves per workgroup, waves per SIMD the
+// registers allow, k steps per chunk.  A wave holds MB x Q = 4
+// accumulators of 32 x 32 whatever M is: Q = 4 column blocks (128-column
+// strips) for M <= 32, Q = 2 (64-column strips) for M <= 64.
+constexpr int kSkinnyWaves = 4;
+constexpr int kSkinnyWpe = 3;
+constexpr int kSkinnyKc = 8;
+
+int skinny_q(int M) { return M <= 32 ? 4 : 2; }
+
+bool skinny_fits(int M, int K) { return M <= 64 && K <= kSkinnyMaxK; }
+
+// The fast skinny kernel addresses B and C by 32-bit byte offsets from the
+// matrix base and moves 128 bits at a time.
+bool skinny_fast_ok(int M, int N, int K, const void *B, int ldb, const void *C, int ldc)
+{
+    const int q = skinny_q(M);
+    const int64_t b_bytes = ((int64_t)K * ldb + N) * 4;
+    const int64_t c_bytes = ((int64_t)M * ldc + N) * 4;
+    const bool aligned = ((uintptr_t)B % (4 * q)) == 0 && ((uintptr_t)C % (4 * q)) == 0 &&
+                         ldb % q == 0 && ldc % q == 0;
+    return aligned && b_bytes < (1ll << 32) && c_bytes < (1ll << 32);
+}
+
+// Shape-driven choice: the streaming kernel when A is small and there are
+// enough 128-column strips to give every wave of the chip several.
+bool use_skinny(int variant, int M, int N, int K, int num_cus)
+{
+    if (variant == SGEMM_VARIANT_SKINNY) return true;
+    if (variant != SGEMM_VARIANT_AUTO) return false;
+    const int64_t strips = ((int64_t)N + 32 * skinny_q(M) - 1) / (32 * skinny_q(M));
+    return skinny_fits(M, K) && strips >= (int64_t)num_cus * 8;
+}
+
+struct SkinnyLaunch {
+    int begin, end, blocks, strips_per_wave;
+};
+
+struct SkinnyPlan {
+    int mb, q, kh, pitch, lds_bytes;
+    SkinnyLaunch fast, masked;  // strips for each kernel (empty if begin == end)
+};
+
+// Strips [begin, end) spread over workgroups of kSkinnyWaves waves.
+SkinnyLaunch skinny_split(int begin, int end, int num_cus)
+{
+    SkinnyLaunch l;
+    l.begin = begin;
+    l.end = end;
+    const int64_t strips = end - begin;
+    // Several strips per wave only when there are many more strips than
+    // resident waves (about 6 rounds of waves remain for load balance).
+    const int64_t resident_waves = (int64_t)num_cus * 4 * kSkinnyWpe;
+    int64_t spw = strips / (resident_waves * 6);
+    if (spw < 1) spw = 1;
+    l.strips_per_wave = (int)spw;
+    const int64_t per_block = (int64_t)kSkinnyWaves * spw;
+    l.blocks = (int)((strips + per_block - 1) / per_block);
+    return l;
+}
+
+SkinnyPlan plan_skinny(int M, int N, int K, bool fast, int num_cus)
+{
+    SkinnyPlan p;
+    p.mb = M <= 32 ? 1 : 2;
+    p.q = skinny_q(M);
+    p.kh = (K + 1) / 2;
+    p.pitch = skinny_pitch(p.kh, kSkinnyKc);
+    p.lds_bytes = 2 * p.mb * 32 * p.pitch * (int)sizeof(float);
+    const int strip = 32 * p.q;
+    const int nstrips = (int)(((int64_t)N + strip - 1) / strip);
+    const int nfull = fast ? N / strip : 0;
+    p.fast = skinny_split(0, nfull, num_cus);
+    p.masked = skinny_split(nfull, nstrips, num_cus);
+    return p;
+}
+
+template <int MB, int Q>
+int launch_skinny(const GemmArgs &g, const SkinnyPlan &p, hipStream_t stream)
+{
+    const dim3 block(kSkinnyWaves * 64);
+    if (p.fast.end > p.fast.begin)
+        hipLaunchKernelGGL((skinny_kernel<MB, Q, kSkinnyWaves, kSkinnyWpe, kSkinnyKc, true>),
+                           dim3(p.fast.blocks), block, p.lds_bytes, stream, g, p.kh, p.pitch,
+                           p.fast.begin, p.fast.end, p.fast.strips_per_wave);
+    if (p.masked.end > p.masked.begin)
+        hipLaunchKernelGGL((skinny_kernel<MB, Q, kSkinnyWaves, kSkinnyWpe, kSkinnyKc, false>),
+                           dim3(p.masked.blocks), block, p.lds_bytes, stream, g, p.kh, p.pitch,
+                           p.masked.begin, p.masked.end, p.masked.strips_per_wave);
+    return (int)hipGetLastError();
+}
+
+
+
 int launch(int variant, int M, int N, int K, float alpha, const float *A, int lda,
            const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream)
 {
@@ -179,11 +275,12 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
         return (int)hipGetLastError();
     }
 
+    if (variant == SGEMM_VARIANT_SKINNY && !skinny_fits(M, K)) return SGEMM_ERR_VARIANT_SHAPE;
+
     int cus = 0;
     const hipError_t e = device_cus(&cus);
     if (e != hipSuccess) return (int)e;
 
-    const TileConfig *c = select_tile(variant, M, N, K, cus);
     GemmArgs g;
     g.A = A;
     g.B = B;
@@ -196,6 +293,15 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
     g.K = K;
     g.alpha = alpha;
     g.beta = beta;
+
+    if (use_skinny(variant, M, N, K, cus)) {
+        const bool fast = skinny_fast_ok(M, N, K, B, ldb, C, ldc);
+        const SkinnyPlan p = plan_skinny(M, N, K, fast, cus);
+        g.tiles_m = g.tiles_n = g.group_m = 1;
+        return p.mb == 1 ? launch_skinny<1, 4>(g, p, stream) : launch_skinny<2, 2>(g, p, stream);
+    }
+
+    const TileConfig *c = select_tile(variant, M, N, K, cus);
     g.tiles_m = (int)ceil_div(M, c->bm);
     g.tiles_n = (int)ceil_div(N, c->bn);
     g.group_m = group_rows(*c, g.tiles_m, g.tiles_n, cus);
@@ -238,6 +344,19 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
         std::snprintf(text, sizeof text, "none");
     } else if (K == 0 || alpha == 0.0f) {
         std::snprintf(text, sizeof text, "scale m=%d n=%d", M, N);
+    } else if (variant == SGEMM_VARIANT_SKINNY && !skinny_fits(M, K)) {
+        return SGEMM_ERR_VARIANT_SHAPE;
+    } else if (use_skinny(variant, M, N, K, num_cus)) {
+        // Plans assume 16-byte aligned bases, as the description says.
+        const bool fast = skinny_fast_ok(M, N, K, nullptr, ldb, nullptr, ldc);
+        const SkinnyPlan p = plan_skinny(M, N, K, fast, num_cus);
+        std::snprintf(text, sizeof text,
+                      "skinny mb=%d q=%d kc=%d kh=%d pitch=%d waves=%d fast=%d+%d masked=%d+%d "
+                      "spw=%d lds=%d",
+                      p.mb, p.q, kSkinnyKc, p.kh, p.pitch, kSkinnyWaves,
+                      p.fast.blocks * (p.fast.end > p.fast.begin), p.fast.end - p.fast.begin,
+                      p.masked.blocks * (p.masked.end > p.masked.begin),
+                      p.masked.end - p.masked.begin, p.fast.strips_per_wave, p.lds_bytes);
     } else {
         const TileConfig *c = select_tile(variant, M, N, K, num_cus);
         const int tiles_m = (int)ceil_div(M, c->bm);
@@ -272,6 +391,7 @@ extern "C" const char *sgemm_status_string(int status)
     case -11: return "invalid ldc (< max(1, N))";
     case -12: return "invalid plan arguments (num_cus < 1 or no buffer)";
     case SGEMM_ERR_BAD_VARIANT: return "unknown kernel variant";
+    case SGEMM_ERR_VARIANT_SHAPE: return "the forced kernel variant cannot run this shape";
     default: break;
     }
     if (status > 0) return hipGetErrorString((hipError_t)status);

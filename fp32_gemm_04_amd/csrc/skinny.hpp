@@ -1,0 +1,240 @@
+// Streaming kernel for skinny products: M <= 64 rows, small K (<= 240),
+// very many columns N -- the im2col convolution shapes of the
+// UNIVERSAL_SGEMM_CUDA README ("Results" section: (32, 1605632, 27),
+// (64, 1605632, 147), (64, 559104, 147)).  There the whole of A is a few
+// tens of KB while B and C are hundreds of MB, so the product is bound by
+// HBM (or sits at the ridge between HBM and the matrix cores), and the
+// kernel is built to move every byte of B and C through HBM exactly once,
+// with wide accesses and many of them in flight:
+//
+//   * A is copied once per workgroup into LDS and stays there.
+//   * Each wave owns strips of 32*Q columns of C and computes all M rows of
+//     a strip with v_mfma_f32_32x32x2_f32: MB 32-row blocks times Q column
+//     blocks, one 16-float accumulator each per lane (MB*Q = 4 keeps the
+//     accumulators at 64 registers: Q = 4 for M <= 32, Q = 2 for M <= 64).
+//   * Column block q of a strip holds the columns n0 + Q*j + q
+//     (j = 0..31): with that interleaving one Q-wide load of B[k][n0+Q*j ..]
+//     by lane j gives the B operand of all Q column blocks, so B comes
+//     straight from HBM into registers in 32*Q*4-byte row segments per
+//     half-wave, with no LDS round trip and no barrier in the loop; and the
+//     Q accumulators of a lane hold Q adjacent columns, so C is written with
+//     Q-wide stores.  B is read with non-temporal loads (each element is
+//     used by one wave only), which measured faster than caching it.
+//   * The k index is split between the half-waves: lane group h = l/32
+//     takes k = h*kh + s at step s (kh = ceil(K/2)).  The contraction is
+//     order-free, and this makes a lane's A values for consecutive steps
+//     contiguous in LDS, so one 128-bit LDS read feeds four steps.
+//   * B is fetched in chunks of KC steps, the next chunk's loads issued
+//     before the current chunk's MFMAs (register double buffer).
+//
+// MFMA layout (v_mfma_f32_32x32x2_f32, lane l): A operand A[l%32][k = l/32],
+// B operand B[k = l/32][l%32], D[8*(r/4) + 4*(l/32) + r%4][l%32], r = 0..15.
+//
+// LDS layout of A (floats): As[h][row][s] = A[row][h*kh + s] (0 outside A),
+// row pitch SAK (kh rounded up to the chunk size, SAK/4 odd so that 16
+// consecutive rows fall on distinct bank groups for 128-bit reads).
+#pragma once
+
+#include "common.hpp"
+
+namespace sgemm {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kSkinnyMaxK = 240;  // keeps the A copy within 64 KB of LDS
+
+// Row pitch (floats) of the LDS copy of A for a given kh = ceil(K/2) and
+// chunk size kc.
+__host__ __device__ inline int skinny_pitch(int kh, int kc)
+{
+    int p = (kh + kc - 1) / kc * kc;
+    if ((p / 4) % 2 == 0) p += 4;
+    return p;
+}
+
+// acc += A(:, steps c .. c+STEPS) x b, for the MB row blocks and Q column
+// blocks (STEPS <= KC, a multiple of 4).  Steps past the end of K carry
+// zeros in both A (LDS padding) and b, so a last chunk may run whole.
+template <int MB, int Q, int KC, int STEPS, typename VQ>
+__device__ __forceinline__ void skinny_mma(f32x16 (&acc)[MB][Q], const VQ (&b)[KC],
+                                           const float *a_lane, int sak, int c)
+{
+    static_assert(STEPS % 4 == 0 && STEPS <= KC, "bad step count");
+    f32x4 a4[MB][STEPS / 4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < STEPS / 4; ++i)
+            a4[mb][i] = *reinterpret_cast<const f32x4 *>(a_lane + mb * 32 * sak + c + 4 * i);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int q = 0; q < Q; ++q)
+                acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[mb][s / 4][s % 4], b[s][q],
+                                                                  acc[mb][q], 0, 0, 0);
+}
+
+// MB: 32-row blocks of A (1 or 2); Q: column blocks per strip (strip width
+// 32*Q).  WAVES per workgroup, WPE waves per SIMD the register budget must
+// allow, KC k-steps per chunk (multiple of 4).  The workgroups cover strips
+// [strip_begin, strip_end), strips_per_wave consecutive strips per wave.
+// FAST: every strip lies inside B and C, whose rows are aligned to the
+// access width, and the byte offsets of B and C fit in 32 bits: all
+// accesses are Q-wide, addressed from the (wave-uniform) matrix base.
+// Otherwise every access is masked (the ragged last strip, unaligned
+// operands).
+template <int MB, int Q, int WAVES, int WPE, int KC, bool FAST>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+skinny_kernel(GemmArgs g, int kh, int sak, int strip_begin, int strip_end, int strips_per_wave)
+{
+    static_assert(KC % 4 == 0, "chunk must be a multiple of 4 steps");
+    typedef float VQ __attribute__((ext_vector_type(Q)));
+    extern __shared__ __attribute__((aligned(16))) float As[];
+    constexpr int ROWS = MB * 32;
+    constexpr int STRIP = 32 * Q;
+    const int M = g.M, N = g.N, K = g.K;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+
+    // 1. A -> LDS, split by k half; zero outside A and past kh.  Loads are
+    // issued in batches of 8 independent ones per thread, so the copy costs
+    // a few L2 round trips rather than one per element.
+    {
+        constexpr int NT = WAVES * 64;
+        constexpr int BATCH = 8;
+        const int total = 2 * ROWS * sak;
+        for (int base = threadIdx.x; base < total; base += NT * BATCH) {
+            float v[BATCH];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const int idx = base + u * NT;
+                const int r = idx / sak;
+                const int s = idx - r * sak;
+                const int h = r / ROWS;
+                const int m = r - h * ROWS;
+                const int k = h * kh + s;
+                v[u] = (idx < total && m < M && s < kh && k < K) ? g.A[(int64_t)m * g.lda + k]
+                                                                 : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u)
+                if (base + u * NT < total) As[base + u * NT] = v[u];
+        }
+    }
+    __syncthreads();
+
+    const int j = lane & 31;    // column group of the strip / row of the A operand
+    const int h = lane >> 5;    // which half of K this lane feeds
+    const int k_lane = h * kh;  // first k of this lane's half
+    const float *a_lane = As + (h * ROWS + j) * sak;
+    // Chunks whose steps are all valid for both halves come first; the
+    // last chunk (steps [kh_full, kh) and zero padding) is masked.
+    const int kh_full = (kh - 1) / KC * KC;
+    const int64_t ldb = g.ldb;
+    const uint32_t ldb4 = (uint32_t)(ldb * 4);
+    const char *bbase = reinterpret_cast<const char *>(g.B);
+    const float alpha = g.alpha, beta = g.beta;
+
+    const int first = strip_begin + (blockIdx.x * WAVES + wave) * strips_per_wave;
+    for (int t = 0; t < strips_per_wave; ++t) {
+        const int strip = first + t;
+        if (strip >= strip_end) break;
+        const int n = strip * STRIP + Q * j;  // this lane's first column
+
+        // b[s] = B[k_lane + c + s][n .. n+Q-1], zero outside B; `masked`:
+        // the steps may lie past kh or K.
+        const uint32_t boff = (uint32_t)(((int64_t)k_lane * ldb + n) * 4);
+        auto fill = [&](VQ(&b)[KC], int c, bool masked) {
+#pragma unroll
+            for (int s = 0; s < KC; ++s) {
+                const bool k_ok = !masked || (c + s < kh && k_lane + c + s < K);
+                VQ v;
+#pragma unroll
+                for (int q = 0; q < Q; ++q) v[q] = 0.f;
+                if (FAST) {
+                    if (k_ok)
+                        v = __builtin_nontemporal_load(reinterpret_cast<const VQ *>(
+                            bbase + (boff + (uint32_t)(c + s) * ldb4)));
+                } else if (k_ok) {
+                    const float *p = g.B + (int64_t)(k_lane + c + s) * ldb + n;
+#pragma unroll
+                    for (int q = 0; q < Q; ++q)
+                        if (n + q < N) v[q] = p[q];
+                }
+                b[s] = v;
+            }
+        };
+
+        f32x16 acc[MB][Q];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int q = 0; q < Q; ++q)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[mb][q][r] = 0.f;
+
+        // The loads of chunk c + KC are issued before the MFMAs of chunk c.
+        // Inside the loop every load is unmasked, so no load sits behind a
+        // branch and the wait before the MFMAs of chunk c covers only the
+        // loads of chunk c.
+        VQ bc[KC], bn[KC];
+        if (kh_full > 0) {
+            fill(bc, 0, false);
+            int c = 0;
+            for (; c + KC < kh_full; c += KC) {
+                fill(bn, c + KC, false);
+                // Keep the prefetch at the top of the loop body: without
+                // this the scheduler sinks the loads next to their use in
+                // the following iteration and nothing overlaps.
+                __builtin_amdgcn_sched_barrier(0);
+                skinny_mma<MB, Q, KC, KC>(acc, bc, a_lane, sak, c);
+#pragma unroll
+                for (int s = 0; s < KC; ++s) bc[s] = bn[s];
+            }
+            fill(bn, kh_full, true);
+            __builtin_amdgcn_sched_barrier(0);
+            skinny_mma<MB, Q, KC, KC>(acc, bc, a_lane, sak, c);
+            skinny_mma<MB, Q, KC, KC>(acc, bn, a_lane, sak, kh_full);
+        } else {
+            fill(bc, 0, true);
+            skinny_mma<MB, Q, KC, KC>(acc, bc, a_lane, sak, 0);
+        }
+
+        // Epilogue: row r of block mb, columns n .. n+Q-1.
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = mb * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                if (row >= M) continue;
+                VQ v;
+#pragma unroll
+                for (int q = 0; q < Q; ++q) v[q] = alpha * acc[mb][q][r];
+                if (FAST) {
+                    VQ *pc = reinterpret_cast<VQ *>(reinterpret_cast<char *>(g.C) +
+                                                    (uint32_t)(((int64_t)row * g.ldc + n) * 4));
+                    if (beta != 0.f) {
+                        const VQ old = *pc;
+#pragma unroll
+                        for (int q = 0; q < Q; ++q) v[q] = fmaf(beta, old[q], v[q]);
+                    }
+                    *pc = v;
+                } else {
+                    float *pc = g.C + (int64_t)row * g.ldc + n;
+#pragma unroll
+                    for (int q = 0; q < Q; ++q) {
+                        if (n + q < N) {
+                            float o = v[q];
+                            if (beta != 0.f) o = fmaf(beta, pc[q], o);
+                            pc[q] = o;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace sgemm

@@ -24,6 +24,9 @@ enum sgemm_variant {
     SGEMM_VARIANT_AUTO = 0, /* shape-driven selection (what sgemm_f32 does) */
     SGEMM_VARIANT_MFMA = 1, /* fp32 matrix-core tile kernel, tile chosen by shape */
     SGEMM_VARIANT_VALU = 2, /* vector-FMA register-tile kernel (8x8 per thread) */
+    SGEMM_VARIANT_SKINNY = 3, /* streaming kernel for M <= 64, K <= 240 (A resident
+                               * in LDS, B and C streamed once); other shapes
+                               * return SGEMM_ERR_VARIANT_SHAPE */
     /* SGEMM_VARIANT_MFMA_TILE + i forces entry i of the MFMA tile table
      * (0 <= i < sgemm_num_mfma_tiles()), bypassing the selector; sgemm_plan
      * names the tile.  For tests and tuning. */
@@ -31,7 +34,8 @@ enum sgemm_variant {
 };
 
 /* Status values other than 0 and the hipError_t codes. */
-#define SGEMM_ERR_BAD_VARIANT (-100)
+#define SGEMM_ERR_BAD_VARIANT (-100)   /* variant value unknown */
+#define SGEMM_ERR_VARIANT_SHAPE (-101) /* variant cannot run this shape */
 
 /*
  * sgemm_f32 -- C <- alpha * A * B + beta * C, all row-major fp32.
@@ -90,7 +94,9 @@ int sgemm_f32(int M, int N, int K, float alpha, const float *A, int lda,
  * picks one kernel of the optimisation ladder per run; it exists to
  * benchmark and test each family on its own.  SGEMM_VARIANT_AUTO behaves
  * exactly like sgemm_f32.  Returns SGEMM_ERR_BAD_VARIANT for an unknown
- * variant (checked first), otherwise exactly what sgemm_f32 returns.
+ * variant (checked first), then the argument checks of sgemm_f32, then
+ * SGEMM_ERR_VARIANT_SHAPE if the forced kernel cannot run this shape;
+ * otherwise exactly what sgemm_f32 returns.
  */
 int sgemm_f32_variant(int variant, int M, int N, int K, float alpha,
                       const float *A, int lda, const float *B, int ldb,
@@ -104,9 +110,9 @@ int sgemm_f32_variant(int variant, int M, int N, int K, float alpha,
  *   "mfma bm=160 bn=160 bk=32 waves=2x2 vecA=1 vecB=1 grid=1024"
  * into buf (at most buflen bytes, truncated if needed).  The leading word
  * names the kernel: "none" (nothing to do), "scale" (K == 0 or alpha == 0),
- * "mfma" or "valu".  Returns 0, or the same negative codes as sgemm_f32
- * (pointer checks excepted), SGEMM_ERR_BAD_VARIANT, or -12 when num_cus < 1
- * or buf is NULL with buflen > 0.
+ * "mfma", "valu" or "skinny".  Returns 0, or the same negative codes as
+ * sgemm_f32_variant (pointer checks excepted), or -12 when num_cus < 1 or
+ * buf is NULL with buflen > 0.
  */
 int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, int ldc,
                float alpha, int num_cus, char *buf, int buflen);

@@ -86,7 +86,7 @@ def test_hip_failure_is_a_positive_code():
 def test_bad_variant():
     names = ("M", "N", "K", "alpha", "A", "lda", "B", "ldb", "beta", "C", "ldc")
     args = dict(zip(names, GOOD))
-    for v in (-1, 3, 15, sg.SGEMM_VARIANT_MFMA_TILE + sg.sgemm_num_mfma_tiles()):
+    for v in (-1, 4, 15, sg.SGEMM_VARIANT_MFMA_TILE + sg.sgemm_num_mfma_tiles()):
         assert sg.sgemm_f32_variant(v, *[args[n] for n in names], 0) == sg.SGEMM_ERR_BAD_VARIANT
         assert sg.sgemm_plan(v, 4, 5, 6, 6, 5, 5, 1.0, 256)[0] == sg.SGEMM_ERR_BAD_VARIANT
 
@@ -106,24 +106,37 @@ def test_plan_quick_paths():
 
 
 def test_plan_covers_every_output_tile():
-    for M, N, K in [(5120, 5120, 5120), (32, 1605632, 27), (64, 559104, 147),
-                    (384, 14161, 1152), (1, 1, 1), (257, 129, 3)]:
+    for M, N, K in [(5120, 5120, 5120), (384, 14161, 1152), (1, 1, 1), (257, 129, 3)]:
         p = plan(M, N, K)
         bm, bn = int(p["bm"]), int(p["bn"])
         assert int(p["grid"]) == -(-M // bm) * -(-N // bn)
 
 
-def test_plan_uses_mfma_for_every_headline_shape():
-    for M, N, K in [(5120, 5120, 5120), (1024, 1024, 1024), (32, 1605632, 27),
-                    (64, 1605632, 147), (384, 14161, 1152), (256, 50176, 1024)]:
+def test_plan_kernel_per_headline_shape():
+    for M, N, K in [(5120, 5120, 5120), (1024, 1024, 1024), (384, 14161, 1152),
+                    (256, 43264, 1152), (256, 50176, 1024)]:
         assert plan(M, N, K)["kind"] == "mfma"
+    for M, N, K in [(32, 1605632, 27), (64, 1605632, 147), (64, 559104, 147)]:
+        assert plan(M, N, K)["kind"] == "skinny"
     assert plan(5120, 5120, 5120, variant=sg.SGEMM_VARIANT_VALU)["kind"] == "valu"
+
+
+def test_plan_skinny_details():
+    p = plan(64, 1605632, 147)
+    assert p["mb"] == "2" and p["kh"] == "74"
+    p = plan(32, 1605632, 27)
+    assert p["mb"] == "1" and p["kh"] == "14"
+    # small N stays on the tile kernels unless forced
+    assert plan(64, 1000, 27)["kind"] == "mfma"
+    assert plan(64, 1000, 27, variant=sg.SGEMM_VARIANT_SKINNY)["kind"] == "skinny"
+    rc, _ = sg.sgemm_plan(sg.SGEMM_VARIANT_SKINNY, 65, 10, 10, 10, 10, 10, 1.0, 256)
+    assert rc == sg.SGEMM_ERR_VARIANT_SHAPE
 
 
 def test_plan_vector_paths_follow_leading_dimensions():
     p = plan(384, 14161, 1152)
     assert p["vecA"] == "1" and p["vecB"] == "0"  # N = 14161 is odd
-    p = plan(32, 1605632, 27)
+    p = plan(320, 1024, 27)
     assert p["vecA"] == "0" and p["vecB"] == "1"  # K = 27 is odd
 
 

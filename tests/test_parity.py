@@ -26,7 +26,14 @@ def _need_gpu():
     import fp32_gemm_04_amd  # noqa: F401  (fails loudly if the library is missing)
 
 
+def _fits(variant, M, K):
+    """The forced skinny kernel only takes M <= 64 and K <= 240."""
+    return variant != 3 or (M <= 64 and K <= 240)
+
+
 def _full_check(A, B, C, alpha, beta, variant=0, exact=False, **kw):
+    if not _fits(variant, A.shape[0], A.shape[1]):
+        return None
     out, dC = run(A, B, C, alpha, beta, variant=variant, **kw)
     ref, t = oracle.sgemm(A, B, C, alpha, beta)
     if exact:
@@ -37,7 +44,7 @@ def _full_check(A, B, C, alpha, beta, variant=0, exact=False, **kw):
     return out
 
 
-FAMILIES = [0, 2] + [16 + i for i in range(5)]
+FAMILIES = [0, 2, 3] + [16 + i for i in range(5)]
 
 
 # ---------------------------------------------------------------- workloads
@@ -188,7 +195,7 @@ def test_beta_zero_ignores_nan_in_c():
     C = np.full((M, N), np.nan, np.float32)
     for variant in FAMILIES:
         out = _full_check(A, B, C, 2.0, 0.0, variant, exact=True)
-        assert not np.isnan(out).any()
+        assert out is None or not np.isnan(out).any()
 
 
 def test_alpha_zero_and_k_zero_scale_c():
@@ -232,12 +239,36 @@ def test_page3_constant_case():
 def test_one_hot_rows(variant):
     """A = e_i e_k^T copies row k of B into row i of C: pins row/column indexing
     at tile boundaries."""
-    M, N, K = 333, 289, 97
+    M, N, K = (333, 289, 97) if variant != 3 else (61, 289, 97)
     B = workloads.uniform(K, N, 12)
-    for i, k in [(0, 0), (M - 1, K - 1), (159, 31), (160, 32), (255, 64), (128, 96)]:
+    for i, k in [(0, 0), (M - 1, K - 1), (59, 31), (33, 48), (40, 49), (31, 96)] + \
+            ([(159, 31), (160, 32), (255, 64), (128, 96)] if variant != 3 else []):
         A = np.zeros((M, K), np.float32)
         A[i, k] = 1.0
         out, _ = run(A, B, None, 1.0, 0.0, variant=variant, name="one-hot %d %d" % (i, k))
         expect = np.zeros((M, N), np.float32)
         expect[i] = B[k]
         assert_bits_equal(out, expect, "one-hot (%d, %d)" % (i, k))
+
+
+def test_skinny_variant_rejects_large_shapes():
+    import fp32_gemm_04_amd as sg
+    rc, _ = sg.sgemm_plan(3, 65, 100, 10, 10, 100, 100, 1.0, 256)
+    assert rc == sg.SGEMM_ERR_VARIANT_SHAPE
+    rc, _ = sg.sgemm_plan(3, 64, 100, 241, 241, 100, 100, 1.0, 256)
+    assert rc == sg.SGEMM_ERR_VARIANT_SHAPE
+
+
+SKINNY_SHAPES = [(32, 1, 27), (1, 33, 1), (32, 33, 2), (64, 95, 147), (33, 1000, 27),
+                 (64, 4097, 240), (17, 3333, 239), (64, 64, 148), (2, 70, 3)]
+
+
+@pytest.mark.parametrize("M,N,K", SKINNY_SHAPES)
+def test_skinny_kernel_shapes(M, N, K):
+    A = workloads.integers(M, K, M * 7 + K)
+    B = workloads.integers(K, N, N * 3 + K)
+    C = workloads.integers(M, N, M + N)
+    _full_check(A, B, C, 1.5, -0.5, 3, exact=True)
+    Au = workloads.uniform(M, K, M * 7 + K)
+    Bu = workloads.uniform(K, N, N * 3 + K)
+    _full_check(Au, Bu, None, 1.0, 0.0, 3)
