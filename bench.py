@@ -149,6 +149,27 @@ def bench_im2col(sg, stream, reps):
     return out
 
 
+def traffic_probe(sg, case, call_args, stream):
+    """Launch sequence for the HBM-traffic counter passes (run under rocprofv3
+    --pmc FETCH_SIZE, then WRITE_SIZE): three plain copies of 1 GiB, whose
+    true read and write bytes are known, then three headline SGEMM launches.
+    The copy's counter values give the scale from counter to bytes."""
+    import torch
+    n = (1 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        rc = sg.sgemm_f32(*call_args)
+        if rc != 0:
+            raise RuntimeError(sg.sgemm_status_string(rc))
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": True, "copy_bytes_each_way": n * 4,
+                      "source_hash": source_hash()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +180,9 @@ def main():
     ap.add_argument("--im2col-reps", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU reference work")
     ap.add_argument("--variant", type=int, default=0, help="force a kernel family (tuning)")
+    ap.add_argument("--no-valu", action="store_true", help="skip the VALU-kernel comparison")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only run the launch sequence for the HBM-traffic counter passes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -178,6 +202,10 @@ def main():
     stream = torch.cuda.current_stream()
     call_args = (case.M, case.N, case.K, case.alpha, dA.data_ptr(), case.K, dB.data_ptr(),
                  case.N, case.beta, dC.data_ptr(), case.N, stream.cuda_stream)
+
+    if args.traffic_probe:
+        traffic_probe(sg, case, call_args, stream)
+        return 0
 
     def step():
         rc = sg.sgemm_f32_variant(args.variant, *call_args)
@@ -207,6 +235,21 @@ def main():
                    "beta": case.beta, "device": props.name},
         "roofline": roofline,
     }
+    if not args.no_valu:
+        # The vector-FMA register-tile kernel on the same workload, for comparison.
+        def valu_step():
+            rc = sg.sgemm_f32_variant(sg.SGEMM_VARIANT_VALU, *call_args)
+            if rc != 0:
+                raise RuntimeError(sg.sgemm_status_string(rc))
+        log("timing the VALU kernel")
+        vms = time_steps(valu_step, max(3, args.steps // 5), 3, stream)
+        vtf = case.flops / (vms * 1e-3) / 1e12
+        result["valu_comparison"] = {
+            "kernel": sg.sgemm_plan(sg.SGEMM_VARIANT_VALU, case.M, case.N, case.K, case.K, case.N,
+                                    case.N, case.alpha, props.multi_processor_count)[1],
+            "tflops": round(vtf, 3), "ms_per_step": round(vms, 4),
+            "frac_fp32_peak": round(vtf / PEAK_FP32_TFLOPS, 4),
+            "mfma_over_valu": round(tflops / vtf, 3)}
     if not args.no_im2col:
         result["im2col"] = bench_im2col(sg, stream, args.im2col_reps)
     if not args.no_cpu:

@@ -164,15 +164,19 @@ hipError_t device_cus(int *cus)
 
 bool is_vec_ok(const void *p, int ld) { return ((uintptr_t)p & 15u) == 0 && (ld & 3) == 0; }
 
-// The skinny streaming kernel: waves per workgroup, waves per SIMD the
-// registers allow, k steps per chunk.  A wave holds MB x Q = 4
-// accumulators of 32 x 32 whatever M is: Q = 4 column blocks (128-column
-// strips) for M <= 32, Q = 2 (64-column strips) for M <= 64.
+// The skinny streaming kernel: waves per workgroup; per column-block count
+// Q, waves per SIMD and k steps per chunk (a step is Q registers of B per
+// lane; one chunk of loads is in flight while the previous chunk's MFMAs
+// run).  A wave holds MB x Q = 4 accumulators of 32 x 32 whatever M is:
+// Q = 4 (128-column strips) for M <= 32, Q = 2 (64-column strips) for
+// M <= 64.  The pairs below were the fastest of a measured grid
+// (2 or 3 waves per SIMD x 8 to 32 steps): the Q = 4 kernel spills at 3.
 constexpr int kSkinnyWaves = 4;
-constexpr int kSkinnyWpe = 3;
-constexpr int kSkinnyKc = 8;
+constexpr int kSkinnyWpe4 = 2, kSkinnyKc4 = 8;
+constexpr int kSkinnyWpe2 = 3, kSkinnyKc2 = 8;
 
 int skinny_q(int M) { return M <= 32 ? 4 : 2; }
+int skinny_kc(int M) { return M <= 32 ? kSkinnyKc4 : kSkinnyKc2; }
 
 bool skinny_fits(int M, int K) { return M <= 64 && K <= kSkinnyMaxK; }
 
@@ -208,7 +212,7 @@ struct SkinnyPlan {
 };
 
 // Strips [begin, end) spread over workgroups of kSkinnyWaves waves.
-SkinnyLaunch skinny_split(int begin, int end, int num_cus)
+SkinnyLaunch skinny_split(int begin, int end, int wpe, int num_cus)
 {
     SkinnyLaunch l;
     l.begin = begin;
@@ -216,7 +220,7 @@ SkinnyLaunch skinny_split(int begin, int end, int num_cus)
     const int64_t strips = end - begin;
     // Several strips per wave only when there are many more strips than
     // resident waves (about 6 rounds of waves remain for load balance).
-    const int64_t resident_waves = (int64_t)num_cus * 4 * kSkinnyWpe;
+    const int64_t resident_waves = (int64_t)num_cus * 4 * wpe;
     int64_t spw = strips / (resident_waves * 6);
     if (spw < 1) spw = 1;
     l.strips_per_wave = (int)spw;
@@ -231,26 +235,27 @@ SkinnyPlan plan_skinny(int M, int N, int K, bool fast, int num_cus)
     p.mb = M <= 32 ? 1 : 2;
     p.q = skinny_q(M);
     p.kh = (K + 1) / 2;
-    p.pitch = skinny_pitch(p.kh, kSkinnyKc);
+    p.pitch = skinny_pitch(p.kh, skinny_kc(M));
     p.lds_bytes = 2 * p.mb * 32 * p.pitch * (int)sizeof(float);
     const int strip = 32 * p.q;
     const int nstrips = (int)(((int64_t)N + strip - 1) / strip);
     const int nfull = fast ? N / strip : 0;
-    p.fast = skinny_split(0, nfull, num_cus);
-    p.masked = skinny_split(nfull, nstrips, num_cus);
+    const int wpe = p.q == 4 ? kSkinnyWpe4 : kSkinnyWpe2;
+    p.fast = skinny_split(0, nfull, wpe, num_cus);
+    p.masked = skinny_split(nfull, nstrips, wpe, num_cus);
     return p;
 }
 
-template <int MB, int Q>
+template <int MB, int Q, int WPE, int KC>
 int launch_skinny(const GemmArgs &g, const SkinnyPlan &p, hipStream_t stream)
 {
     const dim3 block(kSkinnyWaves * 64);
     if (p.fast.end > p.fast.begin)
-        hipLaunchKernelGGL((skinny_kernel<MB, Q, kSkinnyWaves, kSkinnyWpe, kSkinnyKc, true>),
+        hipLaunchKernelGGL((skinny_kernel<MB, Q, kSkinnyWaves, WPE, KC, true>),
                            dim3(p.fast.blocks), block, p.lds_bytes, stream, g, p.kh, p.pitch,
                            p.fast.begin, p.fast.end, p.fast.strips_per_wave);
     if (p.masked.end > p.masked.begin)
-        hipLaunchKernelGGL((skinny_kernel<MB, Q, kSkinnyWaves, kSkinnyWpe, kSkinnyKc, false>),
+        hipLaunchKernelGGL((skinny_kernel<MB, Q, kSkinnyWaves, WPE, KC, false>),
                            dim3(p.masked.blocks), block, p.lds_bytes, stream, g, p.kh, p.pitch,
                            p.masked.begin, p.masked.end, p.masked.strips_per_wave);
     return (int)hipGetLastError();
@@ -298,7 +303,8 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
         const bool fast = skinny_fast_ok(M, N, K, B, ldb, C, ldc);
         const SkinnyPlan p = plan_skinny(M, N, K, fast, cus);
         g.tiles_m = g.tiles_n = g.group_m = 1;
-        return p.mb == 1 ? launch_skinny<1, 4>(g, p, stream) : launch_skinny<2, 2>(g, p, stream);
+        return p.mb == 1 ? launch_skinny<1, 4, kSkinnyWpe4, kSkinnyKc4>(g, p, stream)
+                         : launch_skinny<2, 2, kSkinnyWpe2, kSkinnyKc2>(g, p, stream);
     }
 
     const TileConfig *c = select_tile(variant, M, N, K, cus);
@@ -353,7 +359,7 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
         std::snprintf(text, sizeof text,
                       "skinny mb=%d q=%d kc=%d kh=%d pitch=%d waves=%d fast=%d+%d masked=%d+%d "
                       "spw=%d lds=%d",
-                      p.mb, p.q, kSkinnyKc, p.kh, p.pitch, kSkinnyWaves,
+                      p.mb, p.q, skinny_kc(M), p.kh, p.pitch, kSkinnyWaves,
                       p.fast.blocks * (p.fast.end > p.fast.begin), p.fast.end - p.fast.begin,
                       p.masked.blocks * (p.masked.end > p.masked.begin),
                       p.masked.end - p.masked.begin, p.fast.strips_per_wave, p.lds_bytes);

@@ -60,20 +60,48 @@ __device__ __forceinline__ void skinny_mma(f32x16 (&acc)[MB][Q], const VQ (&b)[K
                                            const float *a_lane, int sak, int c)
 {
     static_assert(STEPS % 4 == 0 && STEPS <= KC, "bad step count");
-    f32x4 a4[MB][STEPS / 4];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < STEPS / 4; ++i)
-            a4[mb][i] = *reinterpret_cast<const f32x4 *>(a_lane + mb * 32 * sak + c + 4 * i);
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s)
+    for (int i = 0; i < STEPS / 4; ++i) {
+        // A for 4 steps per row block: one 128-bit LDS read each.
+        f32x4 a4[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
+            a4[mb] = *reinterpret_cast<const f32x4 *>(a_lane + mb * 32 * sak + c + 4 * i);
 #pragma unroll
-            for (int q = 0; q < Q; ++q)
-                acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[mb][s / 4][s % 4], b[s][q],
-                                                                  acc[mb][q], 0, 0, 0);
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+                    acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        a4[mb][s], b[4 * i + s][q], acc[mb][q], 0, 0, 0);
+    }
+}
+
+// As skinny_mma for the last chunk, which holds cnt <= KC valid steps: the
+// MFMAs run in groups of 4 steps and a group wholly past cnt is skipped
+// (cnt is wave-uniform, so this is a branch, not a mask).
+template <int MB, int Q, int KC, typename VQ>
+__device__ __forceinline__ void skinny_mma_tail(f32x16 (&acc)[MB][Q], const VQ (&b)[KC],
+                                                const float *a_lane, int sak, int c, int cnt)
+{
+#pragma unroll
+    for (int i = 0; i < KC / 4; ++i) {
+        if (4 * i < cnt) {
+            f32x4 a4[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                a4[mb] = *reinterpret_cast<const f32x4 *>(a_lane + mb * 32 * sak + c + 4 * i);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int q = 0; q < Q; ++q)
+                        acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            a4[mb][s], b[4 * i + s][q], acc[mb][q], 0, 0, 0);
+        }
+    }
 }
 
 // MB: 32-row blocks of A (1 or 2); Q: column blocks per strip (strip width
@@ -145,7 +173,9 @@ skinny_kernel(GemmArgs g, int kh, int sak, int strip_begin, int strip_end, int s
 
         // b[s] = B[k_lane + c + s][n .. n+Q-1], zero outside B; `masked`:
         // the steps may lie past kh or K.
-        const uint32_t boff = (uint32_t)(((int64_t)k_lane * ldb + n) * 4);
+        // FAST loads are never behind a branch: a step past kh or K reads a
+        // clamped, valid row of B and is then replaced by zero, so the
+        // compiler can count outstanding loads exactly.
         auto fill = [&](VQ(&b)[KC], int c, bool masked) {
 #pragma unroll
             for (int s = 0; s < KC; ++s) {
@@ -154,9 +184,14 @@ skinny_kernel(GemmArgs g, int kh, int sak, int strip_begin, int strip_end, int s
 #pragma unroll
                 for (int q = 0; q < Q; ++q) v[q] = 0.f;
                 if (FAST) {
-                    if (k_ok)
-                        v = __builtin_nontemporal_load(reinterpret_cast<const VQ *>(
-                            bbase + (boff + (uint32_t)(c + s) * ldb4)));
+                    int row = k_lane + c + s;
+                    if (masked) row = row < K ? row : K - 1;
+                    v = __builtin_nontemporal_load(reinterpret_cast<const VQ *>(
+                        bbase + (uint32_t)(((int64_t)row * ldb + n) * 4)));
+                    if (masked && !k_ok) {
+#pragma unroll
+                        for (int q = 0; q < Q; ++q) v[q] = 0.f;
+                    }
                 } else if (k_ok) {
                     const float *p = g.B + (int64_t)(k_lane + c + s) * ldb + n;
 #pragma unroll
@@ -196,10 +231,10 @@ skinny_kernel(GemmArgs g, int kh, int sak, int strip_begin, int strip_end, int s
             fill(bn, kh_full, true);
             __builtin_amdgcn_sched_barrier(0);
             skinny_mma<MB, Q, KC, KC>(acc, bc, a_lane, sak, c);
-            skinny_mma<MB, Q, KC, KC>(acc, bn, a_lane, sak, kh_full);
+            skinny_mma_tail<MB, Q, KC>(acc, bn, a_lane, sak, kh_full, kh - kh_full);
         } else {
             fill(bc, 0, true);
-            skinny_mma<MB, Q, KC, KC>(acc, bc, a_lane, sak, 0);
+            skinny_mma_tail<MB, Q, KC>(acc, bc, a_lane, sak, 0, kh);
         }
 
         // Epilogue: row r of block mb, columns n .. n+Q-1.
