@@ -203,7 +203,7 @@ bool use_skinny(int variant, int M, int N, int K, int num_cus)
 }
 
 struct SkinnyLaunch {
-    int begin, end, blocks, strips_per_wave;
+    int begin, end, blocks;
 };
 
 struct SkinnyPlan {
@@ -211,21 +211,20 @@ struct SkinnyPlan {
     SkinnyLaunch fast, masked;  // strips for each kernel (empty if begin == end)
 };
 
-// Strips [begin, end) spread over workgroups of kSkinnyWaves waves.
+// Strips [begin, end) over a grid that stays resident: at most as many
+// workgroups as fit on the chip at once (wpe waves per SIMD), so the copy of
+// A into LDS is paid once per workgroup; the kernel gives each wave a
+// contiguous share.
 SkinnyLaunch skinny_split(int begin, int end, int wpe, int num_cus)
 {
     SkinnyLaunch l;
     l.begin = begin;
     l.end = end;
     const int64_t strips = end - begin;
-    // Several strips per wave only when there are many more strips than
-    // resident waves (about 6 rounds of waves remain for load balance).
-    const int64_t resident_waves = (int64_t)num_cus * 4 * wpe;
-    int64_t spw = strips / (resident_waves * 6);
-    if (spw < 1) spw = 1;
-    l.strips_per_wave = (int)spw;
-    const int64_t per_block = (int64_t)kSkinnyWaves * spw;
-    l.blocks = (int)((strips + per_block - 1) / per_block);
+    const int64_t resident_blocks = (int64_t)num_cus * 4 * wpe / kSkinnyWaves;
+    int64_t blocks = (strips + kSkinnyWaves - 1) / kSkinnyWaves;
+    if (blocks > resident_blocks) blocks = resident_blocks;
+    l.blocks = (int)(blocks > 0 ? blocks : 1);
     return l;
 }
 
@@ -253,11 +252,11 @@ int launch_skinny(const GemmArgs &g, const SkinnyPlan &p, hipStream_t stream)
     if (p.fast.end > p.fast.begin)
         hipLaunchKernelGGL((skinny_kernel<MB, Q, kSkinnyWaves, WPE, KC, true>),
                            dim3(p.fast.blocks), block, p.lds_bytes, stream, g, p.kh, p.pitch,
-                           p.fast.begin, p.fast.end, p.fast.strips_per_wave);
+                           p.fast.begin, p.fast.end);
     if (p.masked.end > p.masked.begin)
         hipLaunchKernelGGL((skinny_kernel<MB, Q, kSkinnyWaves, WPE, KC, false>),
                            dim3(p.masked.blocks), block, p.lds_bytes, stream, g, p.kh, p.pitch,
-                           p.masked.begin, p.masked.end, p.masked.strips_per_wave);
+                           p.masked.begin, p.masked.end);
     return (int)hipGetLastError();
 }
 
@@ -358,11 +357,11 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
         const SkinnyPlan p = plan_skinny(M, N, K, fast, num_cus);
         std::snprintf(text, sizeof text,
                       "skinny mb=%d q=%d kc=%d kh=%d pitch=%d waves=%d fast=%d+%d masked=%d+%d "
-                      "spw=%d lds=%d",
+                      "lds=%d",
                       p.mb, p.q, skinny_kc(M), p.kh, p.pitch, kSkinnyWaves,
                       p.fast.blocks * (p.fast.end > p.fast.begin), p.fast.end - p.fast.begin,
                       p.masked.blocks * (p.masked.end > p.masked.begin),
-                      p.masked.end - p.masked.begin, p.fast.strips_per_wave, p.lds_bytes);
+                      p.masked.end - p.masked.begin, p.lds_bytes);
     } else {
         const TileConfig *c = select_tile(variant, M, N, K, num_cus);
         const int tiles_m = (int)ceil_div(M, c->bm);

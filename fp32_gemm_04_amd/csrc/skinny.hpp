@@ -106,8 +106,10 @@ __device__ __forceinline__ void skinny_mma_tail(f32x16 (&acc)[MB][Q], const VQ (
 
 // MB: 32-row blocks of A (1 or 2); Q: column blocks per strip (strip width
 // 32*Q).  WAVES per workgroup, WPE waves per SIMD the register budget must
-// allow, KC k-steps per chunk (multiple of 4).  The workgroups cover strips
-// [strip_begin, strip_end), strips_per_wave consecutive strips per wave.
+// allow, KC k-steps per chunk (multiple of 4).  The grid is sized to stay
+// resident (the A copy is paid once per workgroup) and covers strips
+// [strip_begin, strip_end): wave w of W takes the contiguous range
+// [w*S/W, (w+1)*S/W), so the waves' loads differ by at most one strip.
 // FAST: every strip lies inside B and C, whose rows are aligned to the
 // access width, and the byte offsets of B and C fit in 32 bits: all
 // accesses are Q-wide, addressed from the (wave-uniform) matrix base.
@@ -115,7 +117,7 @@ __device__ __forceinline__ void skinny_mma_tail(f32x16 (&acc)[MB][Q], const VQ (
 // operands).
 template <int MB, int Q, int WAVES, int WPE, int KC, bool FAST>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-skinny_kernel(GemmArgs g, int kh, int sak, int strip_begin, int strip_end, int strips_per_wave)
+skinny_kernel(GemmArgs g, int kh, int sak, int strip_begin, int strip_end)
 {
     static_assert(KC % 4 == 0, "chunk must be a multiple of 4 steps");
     typedef float VQ __attribute__((ext_vector_type(Q)));
@@ -127,11 +129,11 @@ skinny_kernel(GemmArgs g, int kh, int sak, int strip_begin, int strip_end, int s
     const int wave = threadIdx.x >> 6;
 
     // 1. A -> LDS, split by k half; zero outside A and past kh.  Loads are
-    // issued in batches of 8 independent ones per thread, so the copy costs
+    // issued in batches of 16 independent ones per thread, so the copy costs
     // a few L2 round trips rather than one per element.
     {
         constexpr int NT = WAVES * 64;
-        constexpr int BATCH = 8;
+        constexpr int BATCH = 16;
         const int total = 2 * ROWS * sak;
         for (int base = threadIdx.x; base < total; base += NT * BATCH) {
             float v[BATCH];
@@ -165,10 +167,12 @@ skinny_kernel(GemmArgs g, int kh, int sak, int strip_begin, int strip_end, int s
     const char *bbase = reinterpret_cast<const char *>(g.B);
     const float alpha = g.alpha, beta = g.beta;
 
-    const int first = strip_begin + (blockIdx.x * WAVES + wave) * strips_per_wave;
-    for (int t = 0; t < strips_per_wave; ++t) {
-        const int strip = first + t;
-        if (strip >= strip_end) break;
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES;
+    const int64_t w = (int64_t)blockIdx.x * WAVES + wave;
+    const int64_t nstrip = strip_end - strip_begin;
+    const int s_first = strip_begin + (int)(w * nstrip / nwaves);
+    const int s_last = strip_begin + (int)((w + 1) * nstrip / nwaves);
+    for (int strip = s_first; strip < s_last; ++strip) {
         const int n = strip * STRIP + Q * j;  // this lane's first column
 
         // b[s] = B[k_lane + c + s][n .. n+Q-1], zero outside B; `masked`:
