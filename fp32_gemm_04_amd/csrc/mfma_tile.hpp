@@ -11,9 +11,10 @@
 //
 // One workgroup computes one BM x BN tile of C:
 //   1. K is walked in slabs of BK.  The A slab (BM x BK) and B slab
-//      (BK x BN) are fetched from HBM with 128-bit loads when alignment
-//      allows (32-bit otherwise), zero-filled outside the matrix, and kept
-//      in registers until the current slab's math is done (prefetch).
+//      (BK x BN) are fetched from HBM with 128-bit loads (32-bit ones only
+//      where a row ends inside the quad), zero-filled outside the matrix,
+//      and kept in registers until the current slab's math is done
+//      (prefetch).
 //   2. They are written to one of two LDS buffers (ping-pong), so one
 //      barrier per slab suffices: the buffer being written was last read
 //      before the previous barrier.
@@ -21,9 +22,9 @@
 //      independent 16x16x4 MFMAs per k-step into FM x FN accumulators.
 //   4. Epilogue: C = alpha*acc + beta*C, with C not read when beta == 0,
 //      stores masked to the M x N window.
-// Workgroups whose tile lies wholly inside C with 16-byte aligned operands
-// take an unmasked copy of the loop (only a ragged last K slab is masked);
-// edge tiles take the fully masked copy.
+// Workgroups whose tile lies wholly inside C take an unmasked copy of the
+// loop (only a ragged last K slab is masked), with 128-bit loads even when
+// rows are only 4-byte aligned; edge tiles take the fully masked copy.
 //
 // MFMA operand layout (v_mfma_f32_16x16x4_f32, 64 lanes, lane l):
 //   A operand: one float, A[row = l%16][k = l/16]
@@ -67,6 +68,18 @@ __device__ __forceinline__ f32x4 load4_masked(const float *__restrict__ p, bool 
     return v;
 }
 
+// Four consecutive floats p[0..3].  ALIGNED: p is 16-byte aligned.
+// Otherwise p need only be 4-byte aligned: the copy still compiles to one
+// 128-bit global load, which gfx950 serves at any dword alignment.
+template <bool ALIGNED>
+__device__ __forceinline__ f32x4 load4(const float *__restrict__ p)
+{
+    if (ALIGNED) return *reinterpret_cast<const f32x4 *>(p);
+    f32x4 v;
+    __builtin_memcpy(&v, p, sizeof v);
+    return v;
+}
+
 template <int BM, int BN, int BK, int WM, int WN>
 struct MfmaTile {
     static constexpr int NT = WM * WN * 64;  // threads per workgroup
@@ -90,8 +103,8 @@ struct MfmaTile {
 };
 
 // The slab pipeline and epilogue of one workgroup.  EDGE selects masked
-// loads of rows/columns (tiles crossing the matrix border or unaligned
-// operands); with EDGE false only a ragged last K slab is masked.
+// loads of rows/columns (tiles crossing the matrix border); with EDGE false
+// only a ragged last K slab is masked.
 template <int BM, int BN, int BK, int WM, int WN, bool AVEC, bool BVEC, bool EDGE>
 __device__ __forceinline__ void mfma_tile_body(const GemmArgs &g, int m0, int n0, float *As,
                                                float *Bs)
@@ -136,15 +149,15 @@ __device__ __forceinline__ void mfma_tile_body(const GemmArgs &g, int m0, int n0
     }
 
     f32x4 ra[NA], rb[NB];
-    // Unmasked fetch: tile inside C, aligned operands, full K slab.
+    // Unmasked fetch: tile inside C, full K slab.
     auto fetch_fast = [&](int k0) {
         const int64_t boff = (int64_t)k0 * g.ldb;
 #pragma unroll
         for (int i = 0; i < NA; ++i)
-            if (a_use[i]) ra[i] = *reinterpret_cast<const f32x4 *>(a_src[i] + k0);
+            if (a_use[i]) ra[i] = load4<AVEC>(a_src[i] + k0);
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            if (b_use[i]) rb[i] = *reinterpret_cast<const f32x4 *>(b_src[i] + boff);
+            if (b_use[i]) rb[i] = load4<BVEC>(b_src[i] + boff);
     };
     auto fetch_masked = [&](int k0) {
         const int64_t boff = (int64_t)k0 * g.ldb;
@@ -258,7 +271,7 @@ mfma_tile_kernel(GemmArgs g)
     tile_of_block(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
     const int m0 = tm * BM;
     const int n0 = tn * BN;
-    const bool interior = AVEC && BVEC && m0 + BM <= g.M && n0 + BN <= g.N;
+    const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
     if (interior)
         mfma_tile_body<BM, BN, BK, WM, WN, AVEC, BVEC, false>(g, m0, n0, As, Bs);
     else
