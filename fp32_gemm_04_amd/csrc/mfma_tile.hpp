@@ -17,7 +17,8 @@
 //      (prefetch).
 //   2. They are written to one of two LDS buffers (ping-pong), so one
 //      barrier per slab suffices: the buffer being written was last read
-//      before the previous barrier.
+//      before the previous barrier.  The write is issued inside the slab's
+//      MFMA sequence (after its first k-step), not after it.
 //   3. Each wave reads its MFMA operands from LDS and issues FM x FN
 //      independent 16x16x4 MFMAs per k-step into FM x FN accumulators.
 //   4. Epilogue: C = alpha*acc + beta*C, with C not read when beta == 0,
@@ -196,7 +197,13 @@ __device__ __forceinline__ void mfma_tile_body(const GemmArgs &g, int m0, int n0
 
     const int a_frag = (wr * TM + lm) * SA + 4 * lg;
     const int b_frag = (4 * lg) * SB + wc * TN + lm;
-    auto compute = [&](int buf) {
+    // compute(buf, hook): the slab's MFMAs; hook() runs just before the
+    // MFMAs of k-step 1 of the last 16-wide chunk.  The caller stores the
+    // prefetched next slab to LDS there, so those writes finish while the
+    // remaining MFMAs run and the barrier after the slab does not wait on
+    // them (measured: 114 -> 121 TFLOPS at 5120^3 against storing after the
+    // whole slab).
+    auto compute = [&](int buf, auto hook) {
         const float *as = As + buf * T::LDS_A + a_frag;
         const float *bs = Bs + buf * T::LDS_B + b_frag;
 #pragma unroll
@@ -212,13 +219,15 @@ __device__ __forceinline__ void mfma_tile_body(const GemmArgs &g, int m0, int n0
                 for (int fn = 0; fn < FN; ++fn)
                     bf[s][fn] = bs[(16 * q + s) * SB + fn * 16];
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+            for (int s = 0; s < 4; ++s) {
+                if (q == BK / 16 - 1 && s == 1) hook();
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
                     for (int fn = 0; fn < FN; ++fn)
                         acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(
                             af[fm][s], bf[s][fn], acc[fm][fn], 0, 0, 0);
+            }
         }
     };
 
@@ -230,8 +239,7 @@ __device__ __forceinline__ void mfma_tile_body(const GemmArgs &g, int m0, int n0
         const int cur = t & 1;
         const bool more = t + 1 < nslab;
         if (more) fetch((t + 1) * BK);
-        compute(cur);
-        if (more) stash(cur ^ 1);
+        compute(cur, [&] { if (more) stash(cur ^ 1); });
         __syncthreads();
     }
 
