@@ -22,6 +22,13 @@ struct GemmArgs {
     int group_m;           // tile rows per raster group (L2 reuse)
 };
 
+// Host-side handle of a tile kernel: all of them take the argument block.
+typedef void (*KernelFn)(GemmArgs);
+
+// Direct-load MFMA kernel for a tile shape and waves-per-SIMD target, or
+// null if none is built for it (defined in mfma_dl.hip).
+KernelFn direct_kernel(int bm, int bn, int wm, int wn, int wpe);
+
 // Number of XCDs (accelerator complex dies) on MI355X.  The hardware hands
 // consecutive workgroup ids to the XCDs in turn, and each XCD has its own L2.
 constexpr int kNumXcd = 8;

@@ -1,0 +1,265 @@
+// fp32 MFMA tile kernel with direct global -> LDS slab loads (gfx950).
+//
+// Same mathematics as mfma_tile.hpp (one workgroup per BM x BN tile of C,
+// K in 16-wide slabs, v_mfma_f32_16x16x4_f32 with lane group g taking
+// k = 4g + s at step s), but the slabs travel from HBM to LDS with
+// global_load_lds_dwordx4: lane l of the instruction writes its 16 bytes
+// to LDS at M0 + 16 l, so no registers hold slab data and no LDS store
+// instructions are issued.  The registers this frees hold a second set of
+// MFMA operands, so a wave reads slab t+1's operands while slab t's last
+// MFMAs run.
+//
+// Used for tiles that lie wholly inside C when K is a multiple of 16 and A
+// and B rows are 16-byte aligned; other tiles of the same launch run the
+// masked register-staged path of mfma_tile.hpp.
+//
+// LDS: three buffers of (BM + BN) / 16 chunks of 1 KB (256 floats).  The
+// position of every float inside a chunk is chosen so that each MFMA
+// operand read of a wave is one contiguous run of LDS:
+//   A chunk cm (rows 16 cm .. 16 cm + 15 of the tile), 16-byte slot j holds
+//     A[16 cm + j % 16][k0 + 4 (j / 16) .. + 3]; lane l's 128-bit operand
+//     read for block cm is slot l, i.e. the wave reads 1 KB in order.
+//   B chunk cb (columns 16 cb .. 16 cb + 15), float e = 64 s + 16 g + c
+//     holds B[k0 + 4 g + s][16 cb + c]; at step s lane l reads float
+//     64 s + l, i.e. the wave reads 256 contiguous bytes.
+// Both patterns touch every bank once, so operand reads are conflict-free.
+//
+// Pipeline of slab t (its operands already in registers):
+//   k-steps 0, 1: MFMAs only.
+//   Wait until this wave's loads of slab t+1 have landed; barrier.
+//   k-steps 2, 3: MFMAs, with slab t+1's operand reads placed one per MFMA
+//     (in the order the next slab first uses them) and then the loads of
+//     slab t+3 into slab t's buffer spread evenly over the rest.  Every
+//     wave took slab t's operands into registers before the barrier, so
+//     the buffer is free.
+// A slab's loads are issued two slabs before its operands are read.  The
+// spacing matters: issued back to back right after the barrier, the reads
+// and loads stall the wave's MFMA issue (measured at 5120^3: 125 TFLOPS
+// clustered, 140 TFLOPS spread).
+#pragma once
+
+#include <type_traits>
+
+#include "mfma_tile.hpp"
+
+namespace sgemm {
+
+typedef __attribute__((address_space(3))) float lds_float;
+
+// Lane l's 16 bytes at src go to LDS bytes [lds + 16 l, lds + 16 l + 16).
+// lds must be the same for the whole wave.  Completion is tracked with the
+// vector memory counter (vmcnt).  An LDS DMA needs one wait state after the
+// M0 write (the s_nop).
+__device__ __forceinline__ void load_lds16(const float *src, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector memory loads are in flight,
+// then meet the workgroup at a barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+template <int BM, int BN, int WM, int WN>
+struct MfmaDl {
+    static constexpr int NW = WM * WN;
+    static constexpr int FM = BM / WM / 16;        // 16x16 blocks per wave along M
+    static constexpr int FN = BN / WN / 16;        // ... along N
+    static constexpr int CA = BM / 16;             // A chunks per slab
+    static constexpr int CB = BN / 16;             // B chunks per slab
+    static constexpr int L = (CA + CB) / NW;       // loads per wave per slab
+    static constexpr int BUF = (CA + CB) * 256;    // floats per LDS buffer
+    static constexpr int NBUF = 3;
+    static constexpr int LDS = NBUF * BUF;         // floats of LDS
+    // Second half of a slab: 2 FM FN MFMAs carry R operand reads, then L
+    // loads every STRIDE MFMAs.
+    static constexpr int R = FM + 2 * FN;
+    static constexpr int STRIDE = (2 * FM * FN - R) / (L + 1);
+    static_assert((CA + CB) % NW == 0, "slab chunks must split evenly over the waves");
+    static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile must be 16-aligned");
+    static_assert(STRIDE >= 1, "too few MFMAs per slab to carry the reads and loads");
+    static_assert(L * (NBUF - 1) <= 63, "loads in flight must fit the vmcnt field");
+};
+
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, float *lds)
+{
+    using D = MfmaDl<BM, BN, WM, WN>;
+    constexpr int NW = D::NW, FM = D::FM, FN = D::FN, CA = D::CA, L = D::L, BUF = D::BUF;
+    constexpr int NBUF = D::NBUF, R = D::R, STRIDE = D::STRIDE;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    const int nslab = g.K / 16;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave / WN;
+    const int wc = wave % WN;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_float *)lds;
+
+    // Load i of this wave fills chunk c = wave + i * NW of every slab: A
+    // block c if c < CA, else B block c - CA.
+    const float *src[L];
+    uint32_t dst[L];
+    bool is_a[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const int c = wave + i * NW;
+        dst[i] = (uint32_t)c * 1024u;
+        is_a[i] = c < CA;
+        if (c < CA) {
+            src[i] = g.A + (int64_t)(m0 + 16 * c + (lane & 15)) * g.lda + 4 * (lane >> 4);
+        } else {
+            const int k = 4 * ((lane >> 2) & 3) + (lane >> 4);
+            src[i] = g.B + (int64_t)k * g.ldb + n0 + 16 * (c - CA) + 4 * (lane & 3);
+        }
+    }
+    const int64_t a_step = 16, b_step = 16 * g.ldb;
+    // Load i of the next unissued slab into the buffer at byte offset bb.
+    auto load = [&](int i, uint32_t bb) {
+        load_lds16(src[i], bb + dst[i]);
+        src[i] += is_a[i] ? a_step : b_step;
+    };
+    auto buffer_bytes = [&](int buf) { return lds_base + (uint32_t)buf * (BUF * 4); };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Operand sets: A as one f32x4 per 16-row block (element s for k-step
+    // s), B as one float per k-step and 16-column block.
+    f32x4 afs[2][FM];
+    float bfs[2][4][FN];
+    // Operand read number r (0 .. R-1) of the slab in buffer buf, in order
+    // of first use: A blocks, then B k-steps 0-1, then B k-steps 2-3.
+    auto read_op = [&](int r, int buf, f32x4 (&af)[FM], float (&bf)[4][FN]) {
+        const float *base = lds + buf * BUF;
+        if (r < FM) {
+            af[r] = *reinterpret_cast<const f32x4 *>(base + (wr * FM + r) * 256 + 4 * lane);
+        } else {
+            const int h = (r - FM) / FN, fn = (r - FM) % FN;
+            const float *bs = base + (CA + wc * FN + fn) * 256 + 128 * h + lane;
+            bf[2 * h][fn] = bs[0];
+            bf[2 * h + 1][fn] = bs[64];
+        }
+    };
+    // k-steps s0..s1-1; hook(n) runs before the n-th MFMA of the call.
+    auto ksteps = [&](int s0, int s1, const f32x4 (&af)[FM], const float (&bf)[4][FN],
+                      auto hook) {
+#pragma unroll
+        for (int s = s0; s < s1; ++s)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    hook(((s - s0) * FM + fm) * FN + fn);
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[fm][s], bf[s][fn],
+                                                                       acc[fm][fn], 0, 0, 0);
+                }
+    };
+    auto no_hook = [](int) {};
+
+    // Slab t from buffer buf with operands in set P; slab t+1's operands go
+    // to set P ^ 1.  After the last slab the reads fetch a stale buffer (in
+    // bounds; the values go unused) so that no branch separates the reads
+    // from the waits the compiler places for them.
+    auto slab = [&](auto P, int t, int buf) {
+        constexpr int p = decltype(P)::value;
+        ksteps(0, 2, afs[p], bfs[p], no_hook);
+        __builtin_amdgcn_sched_barrier(0);
+        // In flight: slab t+1's loads, then slab t+2's (if any).
+        if (t + 2 < nslab)
+            wait_vm_barrier<L>();
+        else
+            wait_vm_barrier<0>();
+        const bool more = t + NBUF < nslab;
+        const int nb = buf + 1 == NBUF ? 0 : buf + 1;
+        const uint32_t bb = buffer_bytes(buf);
+        ksteps(2, 4, afs[p], bfs[p], [&](int n) {
+            if (n < R) {
+                read_op(n, nb, afs[p ^ 1], bfs[p ^ 1]);
+                // Keep the compiler from gathering the reads into one burst.
+                __builtin_amdgcn_sched_barrier(0);
+            } else if (n > R && (n - R) % STRIDE == 0 && (n - R) / STRIDE <= L) {
+                if (more) load((n - R) / STRIDE - 1, bb);
+            }
+        });
+    };
+
+    // Prologue: slabs 0 .. NBUF-1 in flight, wait for slab 0.
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b)
+        if (b < nslab) {
+#pragma unroll
+            for (int i = 0; i < L; ++i) load(i, buffer_bytes(b));
+        }
+    if (nslab > 2)
+        wait_vm_barrier<2 * L>();
+    else if (nslab > 1)
+        wait_vm_barrier<L>();
+    else
+        wait_vm_barrier<0>();
+#pragma unroll
+    for (int r = 0; r < R; ++r) read_op(r, 0, afs[0], bfs[0]);
+
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    int buf = 0;
+    for (int t = 0; t < nslab; t += 2) {
+        slab(P0{}, t, buf);
+        buf = buf + 1 == NBUF ? 0 : buf + 1;
+        if (t + 1 < nslab) {
+            slab(P1{}, t + 1, buf);
+            buf = buf + 1 == NBUF ? 0 : buf + 1;
+        }
+    }
+
+    // Epilogue: C = alpha*acc + beta*C (the tile is inside C).
+    const float alpha = g.alpha, beta = g.beta;
+    const int lm = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + wr * TM + fm * 16 + 4 * lg + i;
+            float *crow = g.C + (int64_t)row * g.ldc + n0 + wc * TN + lm;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                float v = alpha * acc[fm][fn][i];
+                if (beta != 0.f) v = fmaf(beta, crow[fn * 16], v);
+                crow[fn * 16] = v;
+            }
+        }
+    }
+}
+
+// Interior tiles take the direct-load body, border tiles the masked
+// register-staged one; both share the LDS array.
+template <int BM, int BN, int WM, int WN, int WPE>
+__global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+mfma_dl_kernel(GemmArgs g)
+{
+    using T = MfmaTile<BM, BN, 16, WM, WN>;
+    constexpr int DL = MfmaDl<BM, BN, WM, WN>::LDS;
+    constexpr int RG = 2 * (T::LDS_A + T::LDS_B);
+    __shared__ __attribute__((aligned(16))) float lds[DL > RG ? DL : RG];
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    if (m0 + BM <= g.M && n0 + BN <= g.N)
+        mfma_dl_body<BM, BN, WM, WN>(g, m0, n0, lds);
+    else
+        mfma_tile_body<BM, BN, 16, WM, WN, 2, true, true, true>(g, m0, n0, lds, lds + 2 * T::LDS_A);
+}
+
+}  // namespace sgemm

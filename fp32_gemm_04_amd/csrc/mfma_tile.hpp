@@ -88,7 +88,7 @@ struct MfmaTile {
     static constexpr int TN = BN / WN;       // wave sub-tile columns
     static constexpr int FM = TM / 16;       // 16x16 MFMA blocks per wave, along M
     static constexpr int FN = TN / 16;       // ... along N
-    static constexpr int SA = BK + 4;        // LDS pitch of an A slab row (m-major)
+    static constexpr int SA = BK + 8;        // LDS pitch of an A slab row (m-major)
     static constexpr int SB = BN + 4;        // LDS pitch of a B slab row (k-major)
     static constexpr int AQ = BK / 4;        // float4 per A slab row
     static constexpr int BQ = BN / 4;        // float4 per B slab row
@@ -101,12 +101,13 @@ struct MfmaTile {
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert(BK % 16 == 0, "BK must be a multiple of 16");
     static_assert(BN % 16 == 0, "B pitch needs BN % 16 == 0 for conflict-free reads");
+    static_assert(BM % 16 == 0 && A4 % 64 == 0 && B4 % 64 == 0, "slab loads go in chunks of 64");
 };
 
 // The slab pipeline and epilogue of one workgroup.  EDGE selects masked
 // loads of rows/columns (tiles crossing the matrix border); with EDGE false
 // only a ragged last K slab is masked.
-template <int BM, int BN, int BK, int WM, int WN, bool AVEC, bool BVEC, bool EDGE>
+template <int BM, int BN, int BK, int WM, int WN, int ST, bool AVEC, bool BVEC, bool EDGE>
 __device__ __forceinline__ void mfma_tile_body(const GemmArgs &g, int m0, int n0, float *As,
                                                float *Bs)
 {
@@ -124,29 +125,47 @@ __device__ __forceinline__ void mfma_tile_body(const GemmArgs &g, int m0, int n0
     const int lg = lane >> 4;  // k group (A, B) / row group (D)
 
     // Where this thread's slab loads come from (global) and go to (LDS).
-    int a_lds[NA], b_lds[NB], a_col[NA], b_row[NB], b_col[NB];
-    bool a_ok[NA], a_use[NA], b_ok[NB], b_use[NB];
+    // Load i of a wave covers chunk c = wave + i * (NT / 64) of 64 float4.
+    // The chunk count divides by 64, so whether a load is used is the same
+    // for every lane of a wave (a scalar branch, no per-lane masking).
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    bool a_use[NA], b_use[NB];
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+        a_use[i] = (T::A4 % NT == 0) || wave_s + i * (NT / 64) < T::A4 / 64;
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+        b_use[i] = (T::B4 % NT == 0) || wave_s + i * (NT / 64) < T::B4 / 64;
+    // A chunk: 16 rows x 4 float4; lane -> row lane % 16, float4 lane / 16,
+    // so the LDS store has the bank pattern of the fragment read below.
+    // B: float4 f = tid + i * NT in row-major order over the BK x BN slab.
+    // (Recomputed where needed rather than kept live across the K loop.)
+    auto a_rc = [&](int i, int &r, int &c) {
+        const int ch = a_use[i] ? wave_s + i * (NT / 64) : 0;
+        r = 16 * (ch / (AQ / 4)) + lm;
+        c = 4 * (4 * (ch % (AQ / 4)) + lg);
+    };
+    auto b_rc = [&](int i, int &r, int &c) {
+        const int f = b_use[i] ? tid + i * NT : 0;
+        r = f / BQ;
+        c = (f % BQ) * 4;
+    };
+    int a_lds[NA], b_lds[NB];
     const float *a_src[NA];
     const float *b_src[NB];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-        const int f = tid + i * NT;
-        a_use[i] = (T::A4 % NT == 0) || f < T::A4;
-        const int r = (a_use[i] ? f : 0) / AQ;
-        a_col[i] = ((a_use[i] ? f : 0) % AQ) * 4;
-        a_lds[i] = r * SA + a_col[i];
-        a_ok[i] = m0 + r < M;
-        a_src[i] = g.A + (int64_t)(m0 + r) * g.lda + a_col[i];
+        int r, c;
+        a_rc(i, r, c);
+        a_lds[i] = r * SA + c;
+        a_src[i] = g.A + (int64_t)(m0 + r) * g.lda + c;
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-        const int f = tid + i * NT;
-        b_use[i] = (T::B4 % NT == 0) || f < T::B4;
-        b_row[i] = (b_use[i] ? f : 0) / BQ;
-        b_col[i] = ((b_use[i] ? f : 0) % BQ) * 4;
-        b_lds[i] = b_row[i] * SB + b_col[i];
-        b_ok[i] = n0 + b_col[i] < N;
-        b_src[i] = g.B + (int64_t)b_row[i] * g.ldb + n0 + b_col[i];
+        int r, c;
+        b_rc(i, r, c);
+        b_lds[i] = r * SB + c;
+        b_src[i] = g.B + (int64_t)r * g.ldb + n0 + c;
     }
 
     f32x4 ra[NA], rb[NB];
@@ -164,12 +183,18 @@ __device__ __forceinline__ void mfma_tile_body(const GemmArgs &g, int m0, int n0
         const int64_t boff = (int64_t)k0 * g.ldb;
 #pragma unroll
         for (int i = 0; i < NA; ++i)
-            if (a_use[i]) ra[i] = load4_masked<AVEC>(a_src[i] + k0, a_ok[i], k0 + a_col[i], K);
+            if (a_use[i]) {
+                int r, c;
+                a_rc(i, r, c);
+                ra[i] = load4_masked<AVEC>(a_src[i] + k0, m0 + r < M, k0 + c, K);
+            }
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            if (b_use[i])
-                rb[i] = load4_masked<BVEC>(b_src[i] + boff, k0 + b_row[i] < K && b_ok[i],
-                                           n0 + b_col[i], N);
+            if (b_use[i]) {
+                int r, c;
+                b_rc(i, r, c);
+                rb[i] = load4_masked<BVEC>(b_src[i] + boff, k0 + r < K, n0 + c, N);
+            }
     };
     auto fetch = [&](int k0) {
         if (!EDGE && k0 + BK <= K)
@@ -234,13 +259,90 @@ __device__ __forceinline__ void mfma_tile_body(const GemmArgs &g, int m0, int n0
     const int nslab = (K + BK - 1) / BK;
     fetch(0);
     stash(0);
-    __syncthreads();
-    for (int t = 0; t < nslab; ++t) {
-        const int cur = t & 1;
-        const bool more = t + 1 < nslab;
-        if (more) fetch((t + 1) * BK);
-        compute(cur, [&] { if (more) stash(cur ^ 1); });
+    if constexpr (ST == 2) {
         __syncthreads();
+        for (int t = 0; t < nslab; ++t) {
+            const int cur = t & 1;
+            const bool more = t + 1 < nslab;
+            if (more) fetch((t + 1) * BK);
+            compute(cur, [&] { if (more) stash(cur ^ 1); });
+            __syncthreads();
+        }
+    } else if constexpr (ST == 0) {
+        // Fragment prefetch (BK = 16): while slab t's last two k-steps run,
+        // the wave already reads slab t + 1's MFMA operands from LDS into a
+        // second register set, so a slab starts with its operands in
+        // registers.  The barrier sits after k-step 1, behind MFMAs still in
+        // flight.  Two LDS buffers: slab t + 1 is stored to buffer (t+1) & 1
+        // after k-step 0 of slab t; that buffer held slab t - 1, whose
+        // operands every wave had in registers before reaching the previous
+        // barrier.
+        static_assert(BK == 16, "fragment prefetch is written for 16-wide slabs");
+        if (nslab > 1) fetch(BK);
+        __syncthreads();
+        f32x4 af0[FM], af1[FM];
+        float bf0[4][FN], bf1[4][FN];
+        auto read_frags = [&](int buf, f32x4 (&af)[FM], float (&bf)[4][FN]) {
+            const float *as = As + buf * T::LDS_A + a_frag;
+            const float *bs = Bs + buf * T::LDS_B + b_frag;
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                af[fm] = *reinterpret_cast<const f32x4 *>(as + fm * 16 * SA);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    bf[s][fn] = bs[s * SB + fn * 16];
+        };
+        auto ksteps = [&](int s0, int s1, const f32x4 (&af)[FM], const float (&bf)[4][FN]) {
+#pragma unroll
+            for (int s = s0; s < s1; ++s)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            af[fm][s], bf[s][fn], acc[fm][fn], 0, 0, 0);
+        };
+        auto slab = [&](int t, const f32x4 (&af)[FM], const float (&bf)[4][FN],
+                        f32x4 (&afn)[FM], float (&bfn)[4][FN]) {
+            const bool more = t + 1 < nslab;
+            ksteps(0, 1, af, bf);
+            if (more) stash((t + 1) & 1);
+            if (t + 2 < nslab) fetch((t + 2) * BK);
+            ksteps(1, 2, af, bf);
+            __syncthreads();
+            if (more) read_frags((t + 1) & 1, afn, bfn);
+            ksteps(2, 4, af, bf);
+        };
+        read_frags(0, af0, bf0);
+        for (int t = 0; t < nslab; t += 2) {
+            slab(t, af0, bf0, af1, bf1);
+            if (t + 1 < nslab) slab(t + 1, af1, bf1, af0, bf0);
+        }
+    } else {
+        // Three LDS buffers; slab t is read from buffer t % 3.  While slab t
+        // runs, the registers hold slab t + 1, fetched one whole slab
+        // earlier: they go to buffer (t + 1) % 3 inside slab t's MFMA
+        // sequence and are then refilled with slab t + 2.  That buffer was
+        // last read in slab t - 2, which every wave left before the barrier
+        // that ended it.
+        if (nslab > 1) fetch(BK);
+        __syncthreads();
+        int cur = 0;
+        for (int t = 0; t < nslab; ++t) {
+            const int nxt = cur == 2 ? 0 : cur + 1;
+            const bool more = t + 1 < nslab;
+            const bool more2 = t + 2 < nslab;
+            compute(cur, [&] {
+                if (more) {
+                    stash(nxt);
+                    if (more2) fetch((t + 2) * BK);
+                }
+            });
+            __syncthreads();
+            cur = nxt;
+        }
     }
 
     // Epilogue: C = alpha*acc + beta*C over the valid window.
@@ -267,13 +369,16 @@ __device__ __forceinline__ void mfma_tile_body(const GemmArgs &g, int m0, int n0
 
 // WPE: waves per SIMD the register allocation must allow (the kernel is
 // meant to run OCC = WPE * 4 / (WM*WN) workgroups per CU).
-template <int BM, int BN, int BK, int WM, int WN, int WPE, bool AVEC, bool BVEC>
+// ST: LDS buffers per operand (2 or 3), i.e. pipeline stages.
+template <int BM, int BN, int BK, int WM, int WN, int WPE, int ST, bool AVEC, bool BVEC>
 __global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 mfma_tile_kernel(GemmArgs g)
 {
     using T = MfmaTile<BM, BN, BK, WM, WN>;
-    __shared__ __attribute__((aligned(16))) float As[2 * T::LDS_A];
-    __shared__ __attribute__((aligned(16))) float Bs[2 * T::LDS_B];
+    static_assert(ST == 0 || ST == 2 || ST == 3, "pipeline: 0 fragment prefetch, 2 or 3 LDS stages");
+    constexpr int NBUF = ST == 3 ? 3 : 2;
+    __shared__ __attribute__((aligned(16))) float As[NBUF * T::LDS_A];
+    __shared__ __attribute__((aligned(16))) float Bs[NBUF * T::LDS_B];
 
     int tm, tn;
     tile_of_block(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
@@ -281,9 +386,9 @@ mfma_tile_kernel(GemmArgs g)
     const int n0 = tn * BN;
     const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
     if (interior)
-        mfma_tile_body<BM, BN, BK, WM, WN, AVEC, BVEC, false>(g, m0, n0, As, Bs);
+        mfma_tile_body<BM, BN, BK, WM, WN, ST, AVEC, BVEC, false>(g, m0, n0, As, Bs);
     else
-        mfma_tile_body<BM, BN, BK, WM, WN, AVEC, BVEC, true>(g, m0, n0, As, Bs);
+        mfma_tile_body<BM, BN, BK, WM, WN, ST, AVEC, BVEC, true>(g, m0, n0, As, Bs);
 }
 
 }  // namespace sgemm

@@ -21,8 +21,6 @@
 namespace sgemm {
 namespace {
 
-typedef void (*KernelFn)(GemmArgs);
-
 // One entry of the tile table.
 struct TileConfig {
     const char *family;  // "mfma" or "valu"
@@ -32,33 +30,38 @@ struct TileConfig {
     int occupancy;       // workgroups that fit on one CU (LDS/registers)
     double efficiency;   // fraction of the CU's fp32 peak a full tile reaches
     KernelFn fn[2][2];   // [A 128-bit loads][B 128-bit loads]
+    KernelFn dl;         // direct-to-LDS variant (K % 16 == 0, aligned rows) or null
 };
 
 // WPE (waves per SIMD) = OCC workgroups per CU x waves per workgroup / 4 SIMDs.
 #define SGEMM_MFMA_WPE(WM, WN, OCC) ((OCC) * (WM) * (WN) / 4)
-#define SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, AV, BV) \
-    mfma_tile_kernel<BM, BN, BK, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), AV, BV>
-#define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, EFF)                          \
+#define SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, AV, BV) \
+    mfma_tile_kernel<BM, BN, BK, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), ST, AV, BV>
+#define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, ST, EFF, DL)                  \
     {"mfma", BM, BN, BK, WM, WN, WM * WN * 64, OCC, EFF,                         \
-     {{SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, false, false),                 \
-       SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, false, true)},                 \
-      {SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, true, false),                  \
-       SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, true, true)}}}
+     {{SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, false),             \
+       SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, true)},             \
+      {SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, false),              \
+       SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, true)}},             \
+     DL}
+#define SGEMM_DL_KERNEL(BM, BN, WM, WN, OCC) \
+    direct_kernel(BM, BN, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC))
 
 // The MFMA tile table.  Occupancy (workgroups per CU) is what LDS (two
 // slabs of BM*(BK+4) + BK*(BN+4) floats) and the register budget it implies
 // allow; efficiency is the fraction of peak a CU reaches on a full tile.
 const TileConfig kMfmaTiles[] = {
-    SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 0.90),
-    SGEMM_MFMA_ENTRY(128, 128, 16, 2, 2, 2, 0.85),
-    SGEMM_MFMA_ENTRY(64, 64, 32, 2, 2, 4, 0.60),
-    SGEMM_MFMA_ENTRY(32, 256, 32, 1, 4, 2, 0.50),
-    SGEMM_MFMA_ENTRY(64, 256, 16, 1, 4, 2, 0.60),
+    SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 3, 0.90, SGEMM_DL_KERNEL(160, 160, 2, 2, 2)),
+    SGEMM_MFMA_ENTRY(128, 128, 16, 2, 2, 2, 3, 0.85, SGEMM_DL_KERNEL(128, 128, 2, 2, 2)),
+    SGEMM_MFMA_ENTRY(64, 64, 32, 2, 2, 4, 2, 0.60, nullptr),
+    SGEMM_MFMA_ENTRY(32, 256, 32, 1, 4, 2, 2, 0.50, nullptr),
+    SGEMM_MFMA_ENTRY(64, 256, 16, 1, 4, 2, 3, 0.60, SGEMM_DL_KERNEL(64, 256, 1, 4, 2)),
 };
 
 const TileConfig kValuTile = {"valu", 128, 128, 8, 2, 2, 256, 2, 0.45,
                               {{valu_tile_kernel<false, false>, valu_tile_kernel<false, true>},
-                               {valu_tile_kernel<true, false>, valu_tile_kernel<true, true>}}};
+                               {valu_tile_kernel<true, false>, valu_tile_kernel<true, true>}},
+                              nullptr};
 
 constexpr double kHbmBytesPerCuCycle = 8.0e12 / (256 * 2.4e9);  // MI355X HBM share
 constexpr double kFlopsPerCuCycle = 256.0;                      // fp32 MFMA per CU
@@ -313,7 +316,8 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
     const int64_t blocks = (int64_t)g.tiles_m * g.tiles_n;
     if (blocks > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
     const int threads = c->threads;
-    const KernelFn fn = c->fn[is_vec_ok(A, lda)][is_vec_ok(B, ldb)];
+    const bool avec = is_vec_ok(A, lda), bvec = is_vec_ok(B, ldb);
+    const KernelFn fn = c->dl && avec && bvec && K % 16 == 0 ? c->dl : c->fn[avec][bvec];
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), 0, stream, g);
     return (int)hipGetLastError();
 }
@@ -366,11 +370,13 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
         const TileConfig *c = select_tile(variant, M, N, K, num_cus);
         const int tiles_m = (int)ceil_div(M, c->bm);
         const int tiles_n = (int)ceil_div(N, c->bn);
+        const bool dl = c->dl && (lda & 3) == 0 && (ldb & 3) == 0 && K % 16 == 0;
         std::snprintf(text, sizeof text,
-                      "%s bm=%d bn=%d bk=%d waves=%dx%d vecA=%d vecB=%d grid=%lld group=%d",
-                      c->family, c->bm, c->bn, c->bk, c->wm, c->wn, (lda & 3) == 0,
+                      "%s bm=%d bn=%d bk=%d waves=%dx%d vecA=%d vecB=%d grid=%lld group=%d "
+                      "load=%s",
+                      c->family, c->bm, c->bn, dl ? 16 : c->bk, c->wm, c->wn, (lda & 3) == 0,
                       (ldb & 3) == 0, (long long)tiles_m * tiles_n,
-                      group_rows(*c, tiles_m, tiles_n, num_cus));
+                      group_rows(*c, tiles_m, tiles_n, num_cus), dl ? "direct" : "regs");
     }
     if (buflen > 0) {
         std::strncpy(buf, text, (size_t)buflen - 1);

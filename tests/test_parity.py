@@ -176,6 +176,46 @@ def test_padded_leading_dimensions(variant):
                     lds=(K + pads[0], N + pads[1], N + pads[2]))
 
 
+# K a multiple of 16 with 16-byte aligned rows: interior tiles of the 160,
+# 128 and 64x256 families take the direct global -> LDS path, border tiles
+# of the same launch the register-staged one.  K = 16 .. 64 covers one to
+# four slabs (every prologue case of the three-buffer pipeline); K = 80 an
+# odd slab count; ldb is rounded up to a multiple of 4 so that ragged N
+# still gives aligned B rows.
+DIRECT_SHAPES = [(160, 160, 16), (320, 320, 32), (321, 319, 48), (333, 517, 64),
+                 (256, 512, 80), (480, 160, 1024)]
+DIRECT_FAMILIES = [16, 17, 20]
+
+
+def _plan_load(variant, M, N, K, lda, ldb, ldc):
+    import fp32_gemm_04_amd as sg
+    rc, text = sg.sgemm_plan(variant, M, N, K, lda, ldb, ldc, 1.0, 256)
+    assert rc == 0
+    return dict(kv.split("=") for kv in text.split()[1:]).get("load")
+
+
+@pytest.mark.parametrize("variant", [0] + DIRECT_FAMILIES)
+def test_direct_load_path_integer_exact(variant):
+    for M, N, K in DIRECT_SHAPES:
+        A = workloads.integers(M, K, 17 * M + K)
+        B = workloads.integers(K, N, 19 * N + K)
+        C = workloads.integers(M, N, 23 * M + N)
+        nb = -(-N // 4) * 4  # B rows 16-byte aligned even for ragged N
+        for lds in [(K, nb, N), (K + 8, nb + 4, N + 12)]:
+            if variant in DIRECT_FAMILIES:
+                assert _plan_load(variant, M, N, K, *lds) == "direct"
+            _full_check(A, B, C, 1.5, 0.5, variant, exact=True, lds=lds)
+
+
+@pytest.mark.parametrize("variant", DIRECT_FAMILIES)
+def test_direct_load_path_uniform(variant):
+    for M, N, K in DIRECT_SHAPES[1::2]:
+        A = workloads.uniform(M, K, 29 * M + K)
+        B = workloads.uniform(K, N, 31 * N + K)
+        C = workloads.uniform(M, N, 37 * M + N)
+        _full_check(A, B, C, -0.75, 1.25, variant)
+
+
 @pytest.mark.parametrize("variant", FAMILIES)
 def test_misaligned_bases(variant):
     """Base pointers off 16-byte alignment take the 32-bit load paths."""
