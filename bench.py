@@ -35,7 +35,7 @@ import workloads  # noqa: E402
 METRIC = "SGEMM TFLOPS at 5120³ + im2col shapes; % of FP32 peak / HBM roofline"
 PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 matrix (and packed vector) peak
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_tile_5120.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_dl_5120.json")
 
 
 def log(*a):
