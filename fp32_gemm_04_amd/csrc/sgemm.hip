@@ -16,9 +16,13 @@
 #include "common.hpp"
 #include "mfma_tile.hpp"
 #include "skinny.hpp"
+#include "stream16.hpp"
 #include "valu_tile.hpp"
 
 namespace sgemm {
+
+__device__ float g_stream_zero16[4] = {0.f, 0.f, 0.f, 0.f};
+
 namespace {
 
 // One entry of the tile table.
@@ -205,6 +209,33 @@ bool use_skinny(int variant, int M, int N, int K, int num_cus)
     return skinny_fits(M, K) && strips >= (int64_t)num_cus * 8;
 }
 
+// The 16x16x4 streaming kernel takes the HBM-bound skinny shapes (M <= 32)
+// whose B and C rows are 16-byte aligned and whose N is a multiple of its
+// 64-column strip; the other skinny shapes run skinny_kernel.
+constexpr int kStreamWpe = 2;  // waves per SIMD (four-wave workgroups)
+
+bool stream16_ok(int M, int N, int K, const void *B, int ldb, const void *C, int ldc)
+{
+    return M <= 32 && K <= kSkinnyMaxK && N % 64 == 0 && is_vec_ok(B, ldb) &&
+           is_vec_ok(C, ldc);
+}
+
+int stream16_grid(int N, int num_cus)
+{
+    const int nstrip = N / 64;
+    const int slots = num_cus * kStreamWpe;
+    return nstrip < slots ? nstrip : slots;
+}
+
+template <int FM>
+int launch_stream16(const GemmArgs &g, int num_cus, hipStream_t stream)
+{
+    const size_t lds = (size_t)16 * FM * stream_pitch(g.K) * sizeof(float);
+    hipLaunchKernelGGL((stream16_kernel<FM, 8, 4, kStreamWpe>), dim3(stream16_grid(g.N, num_cus)),
+                       dim3(256), lds, stream, g, 0, g.N / 64);
+    return (int)hipGetLastError();
+}
+
 struct SkinnyLaunch {
     int begin, end, blocks;
 };
@@ -301,6 +332,11 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
     g.alpha = alpha;
     g.beta = beta;
 
+    if (use_skinny(variant, M, N, K, cus) && stream16_ok(M, N, K, B, ldb, C, ldc)) {
+        g.tiles_m = g.tiles_n = g.group_m = 1;
+        return M <= 16 ? launch_stream16<1>(g, cus, stream) : launch_stream16<2>(g, cus, stream);
+    }
+
     if (use_skinny(variant, M, N, K, cus)) {
         const bool fast = skinny_fast_ok(M, N, K, B, ldb, C, ldc);
         const SkinnyPlan p = plan_skinny(M, N, K, fast, cus);
@@ -355,6 +391,11 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
         std::snprintf(text, sizeof text, "scale m=%d n=%d", M, N);
     } else if (variant == SGEMM_VARIANT_SKINNY && !skinny_fits(M, K)) {
         return SGEMM_ERR_VARIANT_SHAPE;
+    } else if (use_skinny(variant, M, N, K, num_cus) &&
+               stream16_ok(M, N, K, nullptr, ldb, nullptr, ldc)) {
+        // Plans assume 16-byte aligned bases, as the description says.
+        std::snprintf(text, sizeof text, "stream16 fm=%d strip=64 kc=8 strips=%d grid=%d",
+                      M <= 16 ? 1 : 2, N / 64, stream16_grid(N, num_cus));
     } else if (use_skinny(variant, M, N, K, num_cus)) {
         // Plans assume 16-byte aligned bases, as the description says.
         const bool fast = skinny_fast_ok(M, N, K, nullptr, ldb, nullptr, ldc);

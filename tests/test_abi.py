@@ -116,7 +116,8 @@ def test_plan_kernel_per_headline_shape():
     for M, N, K in [(5120, 5120, 5120), (1024, 1024, 1024), (384, 14161, 1152),
                     (256, 43264, 1152), (256, 50176, 1024)]:
         assert plan(M, N, K)["kind"] == "mfma"
-    for M, N, K in [(32, 1605632, 27), (64, 1605632, 147), (64, 559104, 147)]:
+    assert plan(32, 1605632, 27)["kind"] == "stream16"
+    for M, N, K in [(64, 1605632, 147), (64, 559104, 147)]:
         assert plan(M, N, K)["kind"] == "skinny"
     assert plan(5120, 5120, 5120, variant=sg.SGEMM_VARIANT_VALU)["kind"] == "valu"
 
@@ -125,6 +126,12 @@ def test_plan_skinny_details():
     p = plan(64, 1605632, 147)
     assert p["mb"] == "2" and p["kh"] == "74"
     p = plan(32, 1605632, 27)
+    assert p["fm"] == "2" and int(p["strips"]) == 1605632 // 64 and int(p["grid"]) == 2 * 256
+    assert plan(16, 6400, 5, variant=sg.SGEMM_VARIANT_SKINNY)["fm"] == "1"
+    # M <= 32 streams through stream16 only with N % 64 == 0 and aligned rows
+    assert plan(32, 1605632 + 4, 27, variant=sg.SGEMM_VARIANT_SKINNY)["kind"] == "skinny"
+    assert plan(32, 6400, 27, ldb=6401, variant=sg.SGEMM_VARIANT_SKINNY)["kind"] == "skinny"
+    p = plan(32, 1000, 27, variant=sg.SGEMM_VARIANT_SKINNY)
     assert p["mb"] == "1" and p["kh"] == "14"
     # small N stays on the tile kernels unless forced
     assert plan(64, 1000, 27)["kind"] == "mfma"

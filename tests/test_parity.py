@@ -299,6 +299,29 @@ def test_skinny_variant_rejects_large_shapes():
     assert rc == sg.SGEMM_ERR_VARIANT_SHAPE
 
 
+# Skinny shapes with M <= 32, N % 64 == 0 and aligned rows take the 16x16x4
+# streaming kernel: one or two 16-row blocks; K = 1 .. 240 (partial last
+# step, partial last 16-wide chunk); 4100 strips for 2048 resident waves, so
+# waves stream across strip boundaries.
+STREAM16_SHAPES = [(32, 64, 147), (17, 1024, 27), (32, 4096, 240), (16, 640, 100),
+                   (1, 128, 1), (9, 192, 5), (32, 262400, 27), (32, 262400, 147)]
+
+
+@pytest.mark.parametrize("M,N,K", STREAM16_SHAPES)
+def test_stream16_shapes(M, N, K):
+    import fp32_gemm_04_amd as sg
+    rc, text = sg.sgemm_plan(3, M, N, K, K, N, N, 1.0, 256)
+    assert rc == 0 and text.startswith("stream16")
+    A = workloads.integers(M, K, M * 11 + K)
+    B = workloads.integers(K, N, N * 13 + K)
+    C = workloads.integers(M, N, 3 * M + N)
+    _full_check(A, B, C, 1.5, -0.5, 3, exact=True)
+    _full_check(A, B, C, 1.0, 2.0, 3, exact=True, lds=(K + 5, N + 64, N + 4))
+    Au = workloads.uniform(M, K, M * 11 + K)
+    Bu = workloads.uniform(K, N, N * 13 + K)
+    _full_check(Au, Bu, None, 1.0, 0.0, 3)
+
+
 SKINNY_SHAPES = [(32, 1, 27), (1, 33, 1), (32, 33, 2), (64, 95, 147), (33, 1000, 27),
                  (64, 4097, 240), (17, 3333, 239), (64, 64, 148), (2, 70, 3)]
 
