@@ -32,71 +32,83 @@ struct TileConfig {
     int wm, wn;          // wave grid inside the workgroup
     int threads;         // workgroup size the kernel is compiled for
     int occupancy;       // workgroups that fit on one CU (LDS/registers)
-    double efficiency;   // fraction of the CU's fp32 peak a full tile reaches
+    double efficiency;   // fraction of the CU's fp32 peak, register-staged path
     KernelFn fn[2][2];   // [A 128-bit loads][B 128-bit loads]
     KernelFn dl;         // direct-to-LDS variant (K % 16 == 0, aligned rows) or null
+    double dl_efficiency;  // ... when the direct-load variant runs
 };
 
 // WPE (waves per SIMD) = OCC workgroups per CU x waves per workgroup / 4 SIMDs.
 #define SGEMM_MFMA_WPE(WM, WN, OCC) ((OCC) * (WM) * (WN) / 4)
 #define SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, AV, BV) \
     mfma_tile_kernel<BM, BN, BK, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), ST, AV, BV>
-#define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, ST, EFF, DL)                  \
+#define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, ST, EFF, DL, DLEFF)           \
     {"mfma", BM, BN, BK, WM, WN, WM * WN * 64, OCC, EFF,                         \
      {{SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, false),             \
        SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, true)},             \
       {SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, false),              \
        SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, true)}},             \
-     DL}
+     DL, DLEFF}
 #define SGEMM_DL_KERNEL(BM, BN, WM, WN, OCC) \
     direct_kernel(BM, BN, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC))
 
-// The MFMA tile table.  Occupancy (workgroups per CU) is what LDS (two
-// slabs of BM*(BK+4) + BK*(BN+4) floats) and the register budget it implies
-// allow; efficiency is the fraction of peak a CU reaches on a full tile.
+// The MFMA tile table.  Occupancy (workgroups per CU) is what LDS and the
+// register budget allow.  Efficiencies are the fractions of the CU's fp32
+// peak measured with every CU holding `occupancy` workgroups (5120^3,
+// 4096^3, 2048^3, the im2col mid shapes): register-staged path, then
+// direct-load path.
 const TileConfig kMfmaTiles[] = {
-    SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 3, 0.90, SGEMM_DL_KERNEL(160, 160, 2, 2, 2)),
-    SGEMM_MFMA_ENTRY(128, 128, 16, 2, 2, 2, 3, 0.85, SGEMM_DL_KERNEL(128, 128, 2, 2, 2)),
-    SGEMM_MFMA_ENTRY(64, 64, 32, 2, 2, 4, 2, 0.60, nullptr),
-    SGEMM_MFMA_ENTRY(32, 256, 32, 1, 4, 2, 2, 0.50, nullptr),
-    SGEMM_MFMA_ENTRY(64, 256, 16, 1, 4, 2, 3, 0.60, SGEMM_DL_KERNEL(64, 256, 1, 4, 2)),
+    SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 3, 0.77, SGEMM_DL_KERNEL(160, 160, 2, 2, 2), 0.88),
+    SGEMM_MFMA_ENTRY(128, 128, 16, 2, 2, 2, 3, 0.82, SGEMM_DL_KERNEL(128, 128, 2, 2, 2), 0.90),
+    SGEMM_MFMA_ENTRY(64, 64, 32, 2, 2, 4, 2, 0.70, nullptr, 0.0),
+    SGEMM_MFMA_ENTRY(32, 256, 32, 1, 4, 2, 2, 0.50, nullptr, 0.0),
+    SGEMM_MFMA_ENTRY(64, 256, 16, 1, 4, 2, 3, 0.60, SGEMM_DL_KERNEL(64, 256, 1, 4, 2), 0.90),
 };
 
 const TileConfig kValuTile = {"valu", 128, 128, 8, 2, 2, 256, 2, 0.45,
                               {{valu_tile_kernel<false, false>, valu_tile_kernel<false, true>},
                                {valu_tile_kernel<true, false>, valu_tile_kernel<true, true>}},
-                              nullptr};
+                              nullptr, 0.0};
 
 constexpr double kHbmBytesPerCuCycle = 8.0e12 / (256 * 2.4e9);  // MI355X HBM share
 constexpr double kFlopsPerCuCycle = 256.0;                      // fp32 MFMA per CU
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Rough time (in CU cycles) of running the problem with tile config c:
-// whole rounds of resident workgroups times the per-tile compute time, but
-// never less than the time to move the operands through HBM once.
-double estimate_cycles(const TileConfig &c, int M, int N, int K, int num_cus)
+// Rough time (in CU cycles) of running the problem with tile config c: the
+// work of the most loaded CU (ceil(tiles / CUs) tiles; a partial tile costs
+// a whole one) at the entry's efficiency (that of the register-staged path
+// when partial tiles exist), lowered when a CU holds fewer
+// workgroups than its occupancy (fewer waves to hide latency); never less
+// than the time to move the operands through HBM once.  `direct`: the
+// operands allow the direct-load path.
+double estimate_cycles(const TileConfig &c, int M, int N, int K, int num_cus, bool direct)
 {
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
-    const int64_t slots = (int64_t)num_cus * c.occupancy;
-    const int64_t rounds = ceil_div(tiles, slots);
-    const double kpad = (double)ceil_div(K, c.bk) * c.bk;
-    const double tile_cycles = 2.0 * c.bm * c.bn * kpad / (kFlopsPerCuCycle * c.efficiency);
-    // A round runs `occupancy` tiles per CU side by side, sharing its MFMA pipes.
-    const double compute = (double)rounds * tile_cycles * c.occupancy;
+    const int64_t per_cu = ceil_div(tiles, num_cus);
+    const bool dl = direct && c.dl != nullptr;
+    const int bk = dl ? 16 : c.bk;
+    double eff = dl ? c.dl_efficiency : c.efficiency;
+    // Partial tiles at the right or bottom edge run the masked register-staged
+    // body; a CU that holds one sets the pace (measured at 2304^3: the 160 tile
+    // with a 64-wide edge reaches 52 TFLOPS, the 64 tile without edges 98).
+    if ((M % c.bm != 0 || N % c.bn != 0) && c.efficiency < eff) eff = c.efficiency;
+    if (per_cu < c.occupancy) eff *= 0.85;
+    const double kpad = (double)ceil_div(K, bk) * bk;
+    const double compute = (double)per_cu * 2.0 * c.bm * c.bn * kpad / (kFlopsPerCuCycle * eff);
     const double bytes = 4.0 * ((double)M * K + (double)K * N + (double)M * N);
     const double memory = bytes / (kHbmBytesPerCuCycle * num_cus);
     return compute > memory ? compute : memory;
 }
 
-const TileConfig *select_tile(int variant, int M, int N, int K, int num_cus)
+const TileConfig *select_tile(int variant, int M, int N, int K, int num_cus, bool direct)
 {
     if (variant == SGEMM_VARIANT_VALU) return &kValuTile;
     if (variant >= SGEMM_VARIANT_MFMA_TILE) return &kMfmaTiles[variant - SGEMM_VARIANT_MFMA_TILE];
     const TileConfig *best = nullptr;
     double best_cycles = 0.0;
     for (const TileConfig &c : kMfmaTiles) {
-        const double cyc = estimate_cycles(c, M, N, K, num_cus);
+        const double cyc = estimate_cycles(c, M, N, K, num_cus, direct);
         if (best == nullptr || cyc < best_cycles) {
             best = &c;
             best_cycles = cyc;
@@ -345,15 +357,16 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
                          : launch_skinny<2, 2, kSkinnyWpe2, kSkinnyKc2>(g, p, stream);
     }
 
-    const TileConfig *c = select_tile(variant, M, N, K, cus);
+    const bool avec = is_vec_ok(A, lda), bvec = is_vec_ok(B, ldb);
+    const bool direct = avec && bvec && K % 16 == 0;
+    const TileConfig *c = select_tile(variant, M, N, K, cus, direct);
     g.tiles_m = (int)ceil_div(M, c->bm);
     g.tiles_n = (int)ceil_div(N, c->bn);
     g.group_m = group_rows(*c, g.tiles_m, g.tiles_n, cus);
     const int64_t blocks = (int64_t)g.tiles_m * g.tiles_n;
     if (blocks > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
     const int threads = c->threads;
-    const bool avec = is_vec_ok(A, lda), bvec = is_vec_ok(B, ldb);
-    const KernelFn fn = c->dl && avec && bvec && K % 16 == 0 ? c->dl : c->fn[avec][bvec];
+    const KernelFn fn = c->dl && direct ? c->dl : c->fn[avec][bvec];
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), 0, stream, g);
     return (int)hipGetLastError();
 }
@@ -408,10 +421,11 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
                       p.masked.blocks * (p.masked.end > p.masked.begin),
                       p.masked.end - p.masked.begin, p.lds_bytes);
     } else {
-        const TileConfig *c = select_tile(variant, M, N, K, num_cus);
+        const bool direct = (lda & 3) == 0 && (ldb & 3) == 0 && K % 16 == 0;
+        const TileConfig *c = select_tile(variant, M, N, K, num_cus, direct);
         const int tiles_m = (int)ceil_div(M, c->bm);
         const int tiles_n = (int)ceil_div(N, c->bn);
-        const bool dl = c->dl && (lda & 3) == 0 && (ldb & 3) == 0 && K % 16 == 0;
+        const bool dl = c->dl && direct;
         std::snprintf(text, sizeof text,
                       "%s bm=%d bn=%d bk=%d waves=%dx%d vecA=%d vecB=%d grid=%lld group=%d "
                       "load=%s",
