@@ -25,17 +25,17 @@
 // Both patterns touch every bank once, so operand reads are conflict-free.
 //
 // Pipeline of slab t (its operands already in registers):
-//   k-steps 0, 1: MFMAs only.
+//   k-steps 0, 1: MFMAs, with the loads of slab t+2 spread over them, into
+//     the buffer slab t-1 used (every wave took slab t-1's operands into
+//     registers before the previous barrier, so the buffer is free).
 //   Wait until this wave's loads of slab t+1 have landed; barrier.
-//   k-steps 2, 3: MFMAs, with slab t+1's operand reads placed one per MFMA
-//     (in the order the next slab first uses them) and then the loads of
-//     slab t+3 into slab t's buffer spread evenly over the rest.  Every
-//     wave took slab t's operands into registers before the barrier, so
-//     the buffer is free.
-// A slab's loads are issued two slabs before its operands are read.  The
-// spacing matters: issued back to back right after the barrier, the reads
-// and loads stall the wave's MFMA issue (measured at 5120^3: 125 TFLOPS
-// clustered, 140 TFLOPS spread).
+//   k-steps 2, 3: MFMAs, with slab t+1's operand reads placed one per MFMA,
+//     in the order the next slab first uses them.
+// A slab's loads are issued about one and a half slabs before its operands
+// are read.  The spacing matters: issued back to back right after the
+// barrier, reads and loads stall the wave's MFMA issue (measured at 5120^3:
+// 125 TFLOPS clustered, 140 with reads and loads spread over the second
+// half, 143 with the loads moved to the first half).
 #pragma once
 
 #include <type_traits>
@@ -77,13 +77,13 @@ struct MfmaDl {
     static constexpr int BUF = (CA + CB) * 256;    // floats per LDS buffer
     static constexpr int NBUF = 3;
     static constexpr int LDS = NBUF * BUF;         // floats of LDS
-    // Second half of a slab: 2 FM FN MFMAs carry R operand reads, then L
-    // loads every STRIDE MFMAs.
+    // The first half of a slab (2 FM FN MFMAs) carries L loads, one every
+    // STRIDE MFMAs; the second half R operand reads, one per MFMA.
     static constexpr int R = FM + 2 * FN;
-    static constexpr int STRIDE = (2 * FM * FN - R) / (L + 1);
+    static constexpr int STRIDE = 2 * FM * FN / (L + 1);
     static_assert((CA + CB) % NW == 0, "slab chunks must split evenly over the waves");
     static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile must be 16-aligned");
-    static_assert(STRIDE >= 1, "too few MFMAs per slab to carry the reads and loads");
+    static_assert(STRIDE >= 1 && R <= 2 * FM * FN, "too few MFMAs per slab for the reads and loads");
     static_assert(L * (NBUF - 1) <= 63, "loads in flight must fit the vmcnt field");
 };
 
@@ -92,7 +92,7 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
 {
     using D = MfmaDl<BM, BN, WM, WN>;
     constexpr int NW = D::NW, FM = D::FM, FN = D::FN, CA = D::CA, L = D::L, BUF = D::BUF;
-    constexpr int NBUF = D::NBUF, R = D::R, STRIDE = D::STRIDE;
+    constexpr int NBUF = D::NBUF, R = D::R, S1 = D::STRIDE;
     constexpr int TM = BM / WM, TN = BN / WN;
     const int nslab = g.K / 16;
 
@@ -173,23 +173,27 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
     // from the waits the compiler places for them.
     auto slab = [&](auto P, int t, int buf) {
         constexpr int p = decltype(P)::value;
-        ksteps(0, 2, afs[p], bfs[p], no_hook);
+        // First half: the loads of slab t+2 into the buffer slab t-1 used
+        // (every wave passed barrier t-1 with its operands in registers).
+        const bool more = t >= 1 && t + 2 < nslab;
+        const uint32_t bb = buffer_bytes(buf == 0 ? NBUF - 1 : buf - 1);
+        ksteps(0, 2, afs[p], bfs[p], [&](int n) {
+            if (n > 0 && n % S1 == 0 && n / S1 <= L) {
+                if (more) load(n / S1 - 1, bb);
+            }
+        });
         __builtin_amdgcn_sched_barrier(0);
         // In flight: slab t+1's loads, then slab t+2's (if any).
         if (t + 2 < nslab)
             wait_vm_barrier<L>();
         else
             wait_vm_barrier<0>();
-        const bool more = t + NBUF < nslab;
         const int nb = buf + 1 == NBUF ? 0 : buf + 1;
-        const uint32_t bb = buffer_bytes(buf);
         ksteps(2, 4, afs[p], bfs[p], [&](int n) {
             if (n < R) {
                 read_op(n, nb, afs[p ^ 1], bfs[p ^ 1]);
                 // Keep the compiler from gathering the reads into one burst.
                 __builtin_amdgcn_sched_barrier(0);
-            } else if (n > R && (n - R) % STRIDE == 0 && (n - R) / STRIDE <= L) {
-                if (more) load((n - R) / STRIDE - 1, bb);
             }
         });
     };
@@ -207,6 +211,7 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
         wait_vm_barrier<L>();
     else
         wait_vm_barrier<0>();
+    // (slab 0 issues no loads: slabs 1 and 2 are already in flight)
 #pragma unroll
     for (int r = 0; r < R; ++r) read_op(r, 0, afs[0], bfs[0]);
 
