@@ -286,7 +286,10 @@ SkinnyPlan plan_skinny(int M, int N, int K, bool fast, int num_cus)
     const int nstrips = (int)(((int64_t)N + strip - 1) / strip);
     const int nfull = fast ? N / strip : 0;
     const int wpe = p.q == 4 ? kSkinnyWpe4 : kSkinnyWpe2;
-    p.fast = skinny_split(0, nfull, wpe, num_cus);
+    // The fast kernel: one workgroup of 4 wpe waves per CU.
+    p.fast.begin = 0;
+    p.fast.end = nfull;
+    p.fast.blocks = nfull < num_cus ? (nfull > 0 ? nfull : 1) : num_cus;
     p.masked = skinny_split(nfull, nstrips, wpe, num_cus);
     return p;
 }
@@ -296,8 +299,8 @@ int launch_skinny(const GemmArgs &g, const SkinnyPlan &p, hipStream_t stream)
 {
     const dim3 block(kSkinnyWaves * 64);
     if (p.fast.end > p.fast.begin)
-        hipLaunchKernelGGL((skinny_kernel<MB, Q, kSkinnyWaves, WPE, KC, true>),
-                           dim3(p.fast.blocks), block, p.lds_bytes, stream, g, p.kh, p.pitch,
+        hipLaunchKernelGGL((skinny_kernel<MB, Q, 4 * WPE, WPE, KC, true>), dim3(p.fast.blocks),
+                           dim3(4 * WPE * 64), p.lds_bytes, stream, g, p.kh, p.pitch,
                            p.fast.begin, p.fast.end);
     if (p.masked.end > p.masked.begin)
         hipLaunchKernelGGL((skinny_kernel<MB, Q, kSkinnyWaves, WPE, KC, false>),
@@ -414,11 +417,12 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
         const bool fast = skinny_fast_ok(M, N, K, nullptr, ldb, nullptr, ldc);
         const SkinnyPlan p = plan_skinny(M, N, K, fast, num_cus);
         std::snprintf(text, sizeof text,
-                      "skinny mb=%d q=%d kc=%d kh=%d pitch=%d waves=%d fast=%d+%d masked=%d+%d "
+                      "skinny mb=%d q=%d kc=%d kh=%d pitch=%d fast=%dx%d+%d masked=%dx%d+%d "
                       "lds=%d",
-                      p.mb, p.q, skinny_kc(M), p.kh, p.pitch, kSkinnyWaves,
-                      p.fast.blocks * (p.fast.end > p.fast.begin), p.fast.end - p.fast.begin,
-                      p.masked.blocks * (p.masked.end > p.masked.begin),
+                      p.mb, p.q, skinny_kc(M), p.kh, p.pitch,
+                      p.fast.blocks * (p.fast.end > p.fast.begin),
+                      4 * (p.q == 4 ? kSkinnyWpe4 : kSkinnyWpe2), p.fast.end - p.fast.begin,
+                      p.masked.blocks * (p.masked.end > p.masked.begin), kSkinnyWaves,
                       p.masked.end - p.masked.begin, p.lds_bytes);
     } else {
         const bool direct = (lda & 3) == 0 && (ldb & 3) == 0 && K % 16 == 0;

@@ -60,13 +60,20 @@ __device__ __forceinline__ void skinny_mma(f32x16 (&acc)[MB][Q], const VQ (&b)[K
                                            const float *a_lane, int sak, int c)
 {
     static_assert(STEPS % 4 == 0 && STEPS <= KC, "bad step count");
+    // A for 4 steps per row block is one 128-bit LDS read; the next group's
+    // reads are issued before the current group's MFMAs.
+    f32x4 a4[2][MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        a4[0][mb] = *reinterpret_cast<const f32x4 *>(a_lane + mb * 32 * sak + c);
 #pragma unroll
     for (int i = 0; i < STEPS / 4; ++i) {
-        // A for 4 steps per row block: one 128-bit LDS read each.
-        f32x4 a4[MB];
+        if (i + 1 < STEPS / 4) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            a4[mb] = *reinterpret_cast<const f32x4 *>(a_lane + mb * 32 * sak + c + 4 * i);
+            for (int mb = 0; mb < MB; ++mb)
+                a4[(i + 1) & 1][mb] =
+                    *reinterpret_cast<const f32x4 *>(a_lane + mb * 32 * sak + c + 4 * (i + 1));
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -74,7 +81,7 @@ __device__ __forceinline__ void skinny_mma(f32x16 (&acc)[MB][Q], const VQ (&b)[K
 #pragma unroll
                 for (int q = 0; q < Q; ++q)
                     acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                        a4[mb][s], b[4 * i + s][q], acc[mb][q], 0, 0, 0);
+                        a4[i & 1][mb][s], b[4 * i + s][q], acc[mb][q], 0, 0, 0);
     }
 }
 
@@ -104,6 +111,33 @@ __device__ __forceinline__ void skinny_mma_tail(f32x16 (&acc)[MB][Q], const VQ (
     }
 }
 
+// Q floats of B at byte offset off from base (both 4Q-byte aligned),
+// non-temporal, issued by inline assembly so that the compiler does not
+// count it: the FAST path waits for its loads itself (skinny_wait).
+template <int Q, typename VQ>
+__device__ __forceinline__ VQ skinny_load(const char *base, uint32_t off)
+{
+    VQ v;
+    if constexpr (Q == 4)
+        asm volatile("global_load_dwordx4 %0, %1, %2 nt" : "=v"(v) : "v"(off), "s"(base) : "memory");
+    else
+        asm volatile("global_load_dwordx2 %0, %1, %2 nt" : "=v"(v) : "v"(off), "s"(base) : "memory");
+    return v;
+}
+
+// Wait until at most N vector memory operations of this wave are in
+// flight; the registers of b count as written here, so nothing that reads
+// them can be scheduled above the wait.
+template <int N, typename VQ>
+__device__ __forceinline__ void skinny_wait(VQ (&b)[8])
+{
+    asm volatile("s_waitcnt vmcnt(%8)"
+                 : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4]), "+v"(b[5]),
+                   "+v"(b[6]), "+v"(b[7])
+                 : "n"(N)
+                 : "memory");
+}
+
 // MB: 32-row blocks of A (1 or 2); Q: column blocks per strip (strip width
 // 32*Q).  WAVES per workgroup, WPE waves per SIMD the register budget must
 // allow, KC k-steps per chunk (multiple of 4).  The grid is sized to stay
@@ -127,6 +161,20 @@ skinny_kernel(GemmArgs g, int kh, int sak, int strip_begin, int strip_end)
     const int M = g.M, N = g.N, K = g.K;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+
+    // FAST runs one workgroup per CU, WAVES = 4 WPE waves, and balances the
+    // strips per SIMD (each SIMD has its own matrix core): a wave reads which
+    // SIMD it runs on and takes a rank among that SIMD's waves in LDS.
+    __shared__ int simd_waves[4];
+    int simd = 0, rank = 0;
+    if constexpr (FAST) {
+        if (threadIdx.x < 4) simd_waves[threadIdx.x] = 0;
+        __syncthreads();
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID, 4, 2)" : "=s"(simd));
+        int r = 0;
+        if (lane == 0) r = atomicAdd(&simd_waves[simd], 1);
+        rank = __shfl(r, 0);
+    }
 
     // 1. A -> LDS, split by k half; zero outside A and past kh.  Loads are
     // issued in batches of 16 independent ones per thread, so the copy costs
@@ -167,11 +215,173 @@ skinny_kernel(GemmArgs g, int kh, int sak, int strip_begin, int strip_end)
     const char *bbase = reinterpret_cast<const char *>(g.B);
     const float alpha = g.alpha, beta = g.beta;
 
-    const int64_t nwaves = (int64_t)gridDim.x * WAVES;
-    const int64_t w = (int64_t)blockIdx.x * WAVES + wave;
     const int64_t nstrip = strip_end - strip_begin;
-    const int s_first = strip_begin + (int)(w * nstrip / nwaves);
-    const int s_last = strip_begin + (int)((w + 1) * nstrip / nwaves);
+    int s_first, s_last;
+    if constexpr (FAST) {
+        // Workgroup b takes strips [b S / G, (b+1) S / G); within it, share
+        // t = (waves on lower-numbered SIMDs) + rank of the WAVES equal
+        // shares, so a SIMD's waves hold adjacent shares: with 3 waves per
+        // SIMD each SIMD gets a quarter of the workgroup's strips (+-1).  The
+        // shares are a permutation of 0..WAVES-1 whatever the placement.
+        int before = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (q < simd) before += simd_waves[q];
+        const int64_t t = before + rank;
+        const int64_t b0 = (int64_t)blockIdx.x * nstrip / gridDim.x;
+        const int64_t nb = ((int64_t)blockIdx.x + 1) * nstrip / gridDim.x - b0;
+        s_first = strip_begin + (int)(b0 + t * nb / WAVES);
+        s_last = strip_begin + (int)(b0 + (t + 1) * nb / WAVES);
+    } else {
+        const int64_t nwaves = (int64_t)gridDim.x * WAVES;
+        const int64_t w = (int64_t)blockIdx.x * WAVES + wave;
+        s_first = strip_begin + (int)(w * nstrip / nwaves);
+        s_last = strip_begin + (int)((w + 1) * nstrip / nwaves);
+    }
+
+    if constexpr (FAST) {
+        // The wave's strips as one stream of K chunks (nck per strip; the
+        // last chunk of a strip may hold steps past kh or rows past K: those
+        // read a clamped row and are zeroed once loaded).  Chunks rotate
+        // through three register sets, the loop unrolled by three so each set
+        // is a compile-time choice: while chunk i is multiplied, chunks i+1
+        // and i+2 are in flight, across strip boundaries too.  Chunk i:
+        //   wait for its loads (chunk i+1 stays in flight), write the C of a
+        //   strip finished by chunk i-1, issue chunk i+2, multiply.
+        // The C stores then sit between chunk i+1's loads and chunk i+2's,
+        // so the wait before chunk i+1 can leave chunk i+2 in flight (it may
+        // also wait for those stores, issued a whole chunk earlier).  The
+        // lambdas are forced inline: called with different register sets,
+        // an out-of-line copy would put the sets in scratch memory.
+        static_assert(KC == 8, "the explicit waits are written for chunks of 8 steps");
+        const int nck = (kh + KC - 1) / KC;
+        const int total = (s_last - s_first) * nck;
+        if (total == 0) return;
+        // The base of B in scalar registers (the loads' saddr operand).
+        const uint64_t bb = (uint64_t)(uintptr_t)bbase;
+        const char *bsc = reinterpret_cast<const char *>(
+            ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bb >> 32)) << 32) |
+            (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bb));
+        int sl = s_first, cl = 0;  // next chunk to load
+        auto fetch = [&](VQ(&b)[KC]) __attribute__((always_inline)) {
+            const uint32_t col = (uint32_t)(sl * STRIP + Q * j);
+#pragma unroll
+            for (int s = 0; s < KC; ++s) {
+                int row = k_lane + cl * KC + s;
+                row = row < K ? row : K - 1;
+                b[s] = skinny_load<Q, VQ>(bsc, (uint32_t)row * ldb4 + col * 4u);
+            }
+            if (++cl == nck) {
+                cl = 0;
+                ++sl;
+            }
+        };
+        f32x16 acc[MB][Q];
+        auto clear = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[mb][q][r] = 0.f;
+        };
+        clear();
+        // C as a wave-uniform base plus 32-bit offsets: a lane's offset for
+        // row block mb, accumulator register r is lane_off + rr * ldc4 with
+        // rr = 32 mb + 8 (r / 4) + r % 4 a constant, so each store costs one
+        // add and nothing per row is kept live across the loop (kept live,
+        // those values are spilled, and reloading a spill waits for every
+        // outstanding load, the prefetched chunks included).
+        // (Global address space spelled out: a generic pointer would make
+        // these flat stores, which also count against the LDS reads' waits.)
+        typedef __attribute__((address_space(1))) char gchar;
+        typedef __attribute__((address_space(1))) VQ gVQ;
+        const uint64_t cb = (uint64_t)(uintptr_t)g.C;
+        gchar *csc = (gchar *)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(cb >> 32))
+                                << 32) |
+                               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)cb));
+        const uint32_t ldc4 = (uint32_t)g.ldc * 4u;
+        // Every row of the row blocks exists and C is not read: no masks.
+        const bool plain = M == ROWS && beta == 0.f;
+        auto store = [&](int strip) __attribute__((always_inline)) {
+            const uint32_t lane_off =
+                (uint32_t)(strip * STRIP + Q * j) * 4u + (uint32_t)(4 * h) * ldc4;
+            if (plain) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const uint32_t rr = mb * 32 + 8 * (r / 4) + (r % 4);
+                        VQ v;
+#pragma unroll
+                        for (int q = 0; q < Q; ++q) v[q] = alpha * acc[mb][q][r];
+                        *(gVQ *)(csc + (lane_off + rr * ldc4)) = v;
+                    }
+                return;
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rr = mb * 32 + 8 * (r / 4) + (r % 4);
+                    if (rr + 4 * h >= M) continue;
+                    VQ v;
+#pragma unroll
+                    for (int q = 0; q < Q; ++q) v[q] = alpha * acc[mb][q][r];
+                    gVQ *pc = (gVQ *)(csc + (lane_off + (uint32_t)rr * ldc4));
+                    if (beta != 0.f) {
+                        const VQ old = *pc;
+#pragma unroll
+                        for (int q = 0; q < Q; ++q) v[q] = fmaf(beta, old[q], v[q]);
+                    }
+                    *pc = v;
+                }
+        };
+        int sc = s_first, cc = 0;  // chunk being multiplied
+        bool pending = false;
+        auto run = [&](VQ(&cur)[KC], VQ(&after_next)[KC], int i) __attribute__((always_inline)) {
+            if (i + 1 < total)
+                skinny_wait<KC>(cur);
+            else
+                skinny_wait<0>(cur);
+            if (pending) {
+                store(sc - 1);
+                clear();
+                pending = false;
+            }
+            if (i + 2 < total) fetch(after_next);
+            if (cc + 1 < nck) {
+                skinny_mma<MB, Q, KC, KC>(acc, cur, a_lane, sak, cc * KC);
+            } else {
+                // Last chunk of the strip: zero the steps past kh or K.
+#pragma unroll
+                for (int s = 0; s < KC; ++s) {
+                    const int step = cc * KC + s;
+                    if (!(step < kh && k_lane + step < K)) {
+#pragma unroll
+                        for (int q = 0; q < Q; ++q) cur[s][q] = 0.f;
+                    }
+                }
+                skinny_mma_tail<MB, Q, KC>(acc, cur, a_lane, sak, cc * KC, kh - cc * KC);
+            }
+            if (++cc == nck) {
+                cc = 0;
+                ++sc;
+                pending = true;
+            }
+        };
+        VQ b0[KC], b1[KC], b2[KC];
+        fetch(b0);
+        if (total > 1) fetch(b1);
+        for (int i = 0; i < total; i += 3) {
+            run(b0, b2, i);
+            if (i + 1 < total) run(b1, b0, i + 1);
+            if (i + 2 < total) run(b2, b1, i + 2);
+        }
+        if (pending) store(sc - 1);
+        return;
+    }
+
     for (int strip = s_first; strip < s_last; ++strip) {
         const int n = strip * STRIP + Q * j;  // this lane's first column
 
