@@ -61,4 +61,38 @@ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
     tn = in_group / rows;
 }
 
+// Balancing a kernel's work per SIMD, for kernels that run one workgroup
+// per CU whose 4 WPE waves fill it: each SIMD has its own matrix core, and
+// how the hardware places a workgroup's waves on the SIMDs is not fixed.  A
+// wave reads the SIMD it runs on (HW_ID) and takes a rank among that SIMD's
+// waves with an LDS counter; simd_share then numbers the waves SIMD by SIMD,
+// so waves on one SIMD hold adjacent shares of the workgroup's work.  The
+// numbering is a permutation of 0 .. waves-1 for any placement.
+struct SimdRank {
+    int simd, rank;
+};
+
+// counts: 4 ints of LDS.  Contains a barrier; the counts are final after the
+// caller's next barrier.
+__device__ __forceinline__ SimdRank simd_rank_begin(int *counts)
+{
+    if (threadIdx.x < 4) counts[threadIdx.x] = 0;
+    __syncthreads();
+    SimdRank r;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID, 4, 2)" : "=s"(r.simd));
+    int v = 0;
+    if ((threadIdx.x & 63) == 0) v = atomicAdd(&counts[r.simd], 1);
+    r.rank = __shfl(v, 0);
+    return r;
+}
+
+__device__ __forceinline__ int simd_share(const int *counts, SimdRank r)
+{
+    int before = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (q < r.simd) before += counts[q];
+    return before + r.rank;
+}
+
 }  // namespace sgemm

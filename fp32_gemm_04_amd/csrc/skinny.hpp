@@ -86,8 +86,9 @@ __device__ __forceinline__ void skinny_mma(f32x16 (&acc)[MB][Q], const VQ (&b)[K
 }
 
 // As skinny_mma for the last chunk, which holds cnt <= KC valid steps: the
-// MFMAs run in groups of 4 steps and a group wholly past cnt is skipped
-// (cnt is wave-uniform, so this is a branch, not a mask).
+// A operands are read in groups of 4 steps and the MFMAs of steps at or past
+// cnt are skipped (cnt is the same for the whole wave, so these are
+// branches, not masks; with K = 147 the last chunk holds 2 of its 8 steps).
 template <int MB, int Q, int KC, typename VQ>
 __device__ __forceinline__ void skinny_mma_tail(f32x16 (&acc)[MB][Q], const VQ (&b)[KC],
                                                 const float *a_lane, int sak, int c, int cnt)
@@ -101,12 +102,14 @@ __device__ __forceinline__ void skinny_mma_tail(f32x16 (&acc)[MB][Q], const VQ (
                 a4[mb] = *reinterpret_cast<const f32x4 *>(a_lane + mb * 32 * sak + c + 4 * i);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
+                if (4 * i + s < cnt) {
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
+                    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                    for (int q = 0; q < Q; ++q)
-                        acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            a4[mb][s], b[4 * i + s][q], acc[mb][q], 0, 0, 0);
+                        for (int q = 0; q < Q; ++q)
+                            acc[mb][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                a4[mb][s], b[4 * i + s][q], acc[mb][q], 0, 0, 0);
+                }
         }
     }
 }
@@ -142,13 +145,13 @@ __device__ __forceinline__ void skinny_wait(VQ (&b)[8])
 // 32*Q).  WAVES per workgroup, WPE waves per SIMD the register budget must
 // allow, KC k-steps per chunk (multiple of 4).  The grid is sized to stay
 // resident (the A copy is paid once per workgroup) and covers strips
-// [strip_begin, strip_end): wave w of W takes the contiguous range
-// [w*S/W, (w+1)*S/W), so the waves' loads differ by at most one strip.
+// [strip_begin, strip_end); each wave takes a contiguous range of them.
 // FAST: every strip lies inside B and C, whose rows are aligned to the
 // access width, and the byte offsets of B and C fit in 32 bits: all
-// accesses are Q-wide, addressed from the (wave-uniform) matrix base.
-// Otherwise every access is masked (the ragged last strip, unaligned
-// operands).
+// accesses are Q-wide, addressed from the (wave-uniform) matrix base.  It
+// runs one workgroup of WAVES = 4 WPE waves per CU, the ranges balanced per
+// SIMD.  Otherwise (the ragged last strip, unaligned operands) every access
+// is masked, and wave w of W takes [w S / W, (w+1) S / W).
 template <int MB, int Q, int WAVES, int WPE, int KC, bool FAST>
 __global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 skinny_kernel(GemmArgs g, int kh, int sak, int strip_begin, int strip_end)
@@ -162,19 +165,11 @@ skinny_kernel(GemmArgs g, int kh, int sak, int strip_begin, int strip_end)
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 
-    // FAST runs one workgroup per CU, WAVES = 4 WPE waves, and balances the
-    // strips per SIMD (each SIMD has its own matrix core): a wave reads which
-    // SIMD it runs on and takes a rank among that SIMD's waves in LDS.
+    // FAST runs one workgroup per CU, WAVES = 4 WPE waves, with the strips
+    // balanced per SIMD (simd_rank_begin).
     __shared__ int simd_waves[4];
-    int simd = 0, rank = 0;
-    if constexpr (FAST) {
-        if (threadIdx.x < 4) simd_waves[threadIdx.x] = 0;
-        __syncthreads();
-        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID, 4, 2)" : "=s"(simd));
-        int r = 0;
-        if (lane == 0) r = atomicAdd(&simd_waves[simd], 1);
-        rank = __shfl(r, 0);
-    }
+    SimdRank sr = {0, 0};
+    if constexpr (FAST) sr = simd_rank_begin(simd_waves);
 
     // 1. A -> LDS, split by k half; zero outside A and past kh.  Loads are
     // issued in batches of 16 independent ones per thread, so the copy costs
@@ -218,16 +213,10 @@ skinny_kernel(GemmArgs g, int kh, int sak, int strip_begin, int strip_end)
     const int64_t nstrip = strip_end - strip_begin;
     int s_first, s_last;
     if constexpr (FAST) {
-        // Workgroup b takes strips [b S / G, (b+1) S / G); within it, share
-        // t = (waves on lower-numbered SIMDs) + rank of the WAVES equal
-        // shares, so a SIMD's waves hold adjacent shares: with 3 waves per
-        // SIMD each SIMD gets a quarter of the workgroup's strips (+-1).  The
-        // shares are a permutation of 0..WAVES-1 whatever the placement.
-        int before = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (q < simd) before += simd_waves[q];
-        const int64_t t = before + rank;
+        // Workgroup b takes strips [b S / G, (b+1) S / G), cut into WAVES
+        // equal shares; with WPE waves on each SIMD holding adjacent shares,
+        // each SIMD gets a quarter of the workgroup's strips (+-1).
+        const int64_t t = simd_share(simd_waves, sr);
         const int64_t b0 = (int64_t)blockIdx.x * nstrip / gridDim.x;
         const int64_t nb = ((int64_t)blockIdx.x + 1) * nstrip / gridDim.x - b0;
         s_first = strip_begin + (int)(b0 + t * nb / WAVES);
