@@ -123,6 +123,14 @@ def bench_im2col(sg, stream, reps):
                 case.N, case.beta, dC.data_ptr(), case.N, stream.cuda_stream)
         rc = sg.sgemm_f32(*args)
         assert rc == 0, sg.sgemm_status_string(rc)
+        # Warm-up: the inputs were just drawn on the host, the GPU sat idle
+        # meanwhile and its clocks drop; a few launches are not enough for
+        # them to come back up.  Run the product back to back for ~0.1 s.
+        t_end = time.perf_counter() + 0.1
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                sg.sgemm_f32(*args)
+            torch.cuda.synchronize()
         times = []
         for _ in range(reps):
             flush.sum()  # evict the caches without leaving dirty lines behind
@@ -174,10 +182,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-reference baseline")
     ap.add_argument("--no-im2col", action="store_true", help="skip the im2col shapes")
-    ap.add_argument("--im2col-reps", type=int, default=10)
+    ap.add_argument("--im2col-reps", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU reference work")
     ap.add_argument("--variant", type=int, default=0, help="force a kernel family (tuning)")
     ap.add_argument("--no-valu", action="store_true", help="skip the VALU-kernel comparison")
