@@ -12,9 +12,13 @@ HBM before timing starts.  The line printed also carries:
     sample of the same product (the first rows of C);
   * im2col: the six convolution-as-GEMM shapes, each timed on its own with
     the memory-side caches flushed between launches, with TFLOPS and the
-    HBM bandwidth the algorithmic bytes imply.
+    HBM bandwidth the algorithmic bytes imply;
+  * valu_comparison and ladder: the vector-FMA kernels on the headline
+    workload, the register-tile comparison kernel and each rung of the
+    pages' SIMT optimisation ladder (naive ... double-buffered).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-im2col]
+                       [--no-valu] [--no-ladder]
 """
 from __future__ import annotations
 
@@ -33,7 +37,7 @@ import numpy as np  # noqa: E402
 import workloads  # noqa: E402
 
 METRIC = "SGEMM TFLOPS at 5120³ + im2col shapes; % of FP32 peak / HBM roofline"
-PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 matrix (and packed vector) peak
+PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 matrix peak, and its fp32 vector peak
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_dl_5120.json")
 
@@ -157,6 +161,35 @@ def bench_im2col(sg, stream, reps):
     return out
 
 
+def bench_ladder(sg, case, call_args, stream, mfma_tflops):
+    """Each rung of the pages' SIMT ladder (sgemm_f32_variant(SGEMM_VARIANT_LADDER + r))
+    on the headline workload: one untimed launch, then the median of a few
+    timed ones (the first rungs take a quarter of a second per launch)."""
+    import torch
+    out = []
+    for r, name in enumerate(sg.LADDER_RUNG_NAMES):
+        v = sg.SGEMM_VARIANT_LADDER + r
+        log("ladder rung", r, name)
+        rc = sg.sgemm_f32_variant(v, *call_args)
+        assert rc == 0, sg.sgemm_status_string(rc)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(3 if r < 2 else 9):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            sg.sgemm_f32_variant(v, *call_args)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        tf = case.flops / (ms * 1e-3) / 1e12
+        out.append({"rung": r, "name": name, "ms": round(ms, 3), "tflops": round(tf, 2),
+                    "frac_fp32_vector_peak": round(tf / PEAK_FP32_TFLOPS, 4),
+                    "mfma_over_rung": round(mfma_tflops / tf, 2)})
+    return out
+
+
 def traffic_probe(sg, case, call_args, stream):
     """Launch sequence for the HBM-traffic counter passes (run under rocprofv3
     --pmc FETCH_SIZE, then WRITE_SIZE): three plain copies of 1 GiB, whose
@@ -189,6 +222,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU reference work")
     ap.add_argument("--variant", type=int, default=0, help="force a kernel family (tuning)")
     ap.add_argument("--no-valu", action="store_true", help="skip the VALU-kernel comparison")
+    ap.add_argument("--no-ladder", action="store_true", help="skip the SIMT-ladder table")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the launch sequence for the HBM-traffic counter passes")
     args = ap.parse_args()
@@ -258,6 +292,8 @@ def main():
             "tflops": round(vtf, 3), "ms_per_step": round(vms, 4),
             "frac_fp32_peak": round(vtf / PEAK_FP32_TFLOPS, 4),
             "mfma_over_valu": round(tflops / vtf, 3)}
+    if not args.no_ladder:
+        result["ladder"] = bench_ladder(sg, case, call_args, stream, tflops)
     if not args.no_im2col:
         result["im2col"] = bench_im2col(sg, stream, args.im2col_reps)
     if not args.no_cpu:

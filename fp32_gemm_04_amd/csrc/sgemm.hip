@@ -18,6 +18,7 @@
 #include "skinny.hpp"
 #include "stream16.hpp"
 #include "valu_tile.hpp"
+#include "ladder.hpp"
 
 namespace sgemm {
 
@@ -149,11 +150,55 @@ int check_args(int M, int N, int K, float alpha, const void *A, int lda, const v
 
 constexpr int kNumMfmaTiles = (int)(sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]));
 
+bool is_ladder(int v)
+{
+    return v >= SGEMM_VARIANT_LADDER && v < SGEMM_VARIANT_LADDER + kLadderRungs;
+}
+
 bool valid_variant(int v)
 {
     return v == SGEMM_VARIANT_AUTO || v == SGEMM_VARIANT_MFMA || v == SGEMM_VARIANT_VALU ||
            v == SGEMM_VARIANT_SKINNY ||
-           (v >= SGEMM_VARIANT_MFMA_TILE && v < SGEMM_VARIANT_MFMA_TILE + kNumMfmaTiles);
+           (v >= SGEMM_VARIANT_MFMA_TILE && v < SGEMM_VARIANT_MFMA_TILE + kNumMfmaTiles) ||
+           is_ladder(v);
+}
+
+// The ladder rungs of ladder.hpp: name, output tile, threads per workgroup.
+// Rung 7 is the VALU register-tile kernel.
+struct LadderRung {
+    const char *name;
+    int tile_m, tile_n, threads;
+};
+const LadderRung kLadder[kLadderRungs] = {
+    {"naive", 16, 16, 256},     {"coalesced", 4, 64, 256}, {"lds", 32, 32, 1024},
+    {"tile1d", 64, 64, 512},    {"tile2d", 128, 128, 256}, {"regcache", 128, 128, 256},
+    {"vec4", 128, 128, 256},    {"dbuf", 128, 128, 256},
+};
+
+// Launch rungs 0-6 (rung 7 goes through the VALU tile path).
+int launch_ladder(int rung, GemmArgs g, bool avec, bool bvec, hipStream_t stream)
+{
+    const LadderRung &r = kLadder[rung];
+    g.tiles_m = (int)ceil_div(g.M, r.tile_m);
+    g.tiles_n = (int)ceil_div(g.N, r.tile_n);
+    g.group_m = 1;
+    const int64_t blocks = (int64_t)g.tiles_m * g.tiles_n;
+    if (blocks > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
+    KernelFn fn = nullptr;
+    switch (rung) {
+    case 0: fn = ladder_naive_kernel; break;
+    case 1: fn = ladder_coalesced_kernel; break;
+    case 2: fn = ladder_lds_kernel; break;
+    case 3: fn = ladder_tile1d_kernel; break;
+    case 4: fn = ladder_tile2d_kernel<false>; break;
+    case 5: fn = ladder_tile2d_kernel<true>; break;
+    default:
+        fn = avec ? (bvec ? ladder_vec4_kernel<true, true> : ladder_vec4_kernel<true, false>)
+                  : (bvec ? ladder_vec4_kernel<false, true> : ladder_vec4_kernel<false, false>);
+        break;
+    }
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(r.threads), 0, stream, g);
+    return (int)hipGetLastError();
 }
 
 // Per-device compute-unit count, queried once per device.
@@ -361,6 +406,11 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
     }
 
     const bool avec = is_vec_ok(A, lda), bvec = is_vec_ok(B, ldb);
+    if (is_ladder(variant)) {
+        const int rung = variant - SGEMM_VARIANT_LADDER;
+        if (rung < kLadderRungs - 1) return launch_ladder(rung, g, avec, bvec, stream);
+        variant = SGEMM_VARIANT_VALU;
+    }
     const bool direct = avec && bvec && K % 16 == 0;
     const TileConfig *c = select_tile(variant, M, N, K, cus, direct);
     g.tiles_m = (int)ceil_div(M, c->bm);
@@ -424,6 +474,11 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
                       4 * (p.q == 4 ? kSkinnyWpe4 : kSkinnyWpe2), p.fast.end - p.fast.begin,
                       p.masked.blocks * (p.masked.end > p.masked.begin), kSkinnyWaves,
                       p.masked.end - p.masked.begin, p.lds_bytes);
+    } else if (is_ladder(variant)) {
+        const LadderRung &r = kLadder[variant - SGEMM_VARIANT_LADDER];
+        std::snprintf(text, sizeof text, "ladder rung=%d name=%s tile=%dx%d threads=%d grid=%lld",
+                      variant - SGEMM_VARIANT_LADDER, r.name, r.tile_m, r.tile_n, r.threads,
+                      (long long)ceil_div(M, r.tile_m) * ceil_div(N, r.tile_n));
     } else {
         const bool direct = (lda & 3) == 0 && (ldb & 3) == 0 && K % 16 == 0;
         const TileConfig *c = select_tile(variant, M, N, K, num_cus, direct);

@@ -30,8 +30,26 @@ enum sgemm_variant {
     /* SGEMM_VARIANT_MFMA_TILE + i forces entry i of the MFMA tile table
      * (0 <= i < sgemm_num_mfma_tiles()), bypassing the selector; sgemm_plan
      * names the tile.  For tests and tuning. */
-    SGEMM_VARIANT_MFMA_TILE = 16
+    SGEMM_VARIANT_MFMA_TILE = 16,
+    /* SGEMM_VARIANT_LADDER + r forces rung r (0 <= r < SGEMM_LADDER_RUNGS)
+     * of the optimisation ladder the pages climb on SIMT cores, each rung a
+     * kernel of its own with vector FMAs (NVIDIA_SGEMM_PRACTICE README,
+     * kernels 1-7; UNIVERSAL_SGEMM_CUDA README, "Results" section, modes
+     * 0-4; cnblogs matmul_opt.cu, naive / optimized / advanced kernels):
+     *   0 naive: one thread per element of C, operands from global memory;
+     *   1 coalesced: lanes of a wave on consecutive columns;
+     *   2 lds: 32 x 32 tiles of A and B staged in LDS;
+     *   3 tile1d: 64 x 64 tile, 8 rows of C per thread;
+     *   4 tile2d: 128 x 128 tile, 8 x 8 block of C per thread;
+     *   5 regcache: as 4, operands copied to registers, outer product;
+     *   6 vec4: as 5, 128-bit loads, A slab stored k-major;
+     *   7 dbuf: as 6, double-buffered slabs (= SGEMM_VARIANT_VALU).
+     * Any shape runs.  For measurement beside the pages' tables; the
+     * selector never picks them. */
+    SGEMM_VARIANT_LADDER = 32
 };
+
+#define SGEMM_LADDER_RUNGS 8
 
 /* Status values other than 0 and the hipError_t codes. */
 #define SGEMM_ERR_BAD_VARIANT (-100)   /* variant value unknown */
@@ -110,7 +128,7 @@ int sgemm_f32_variant(int variant, int M, int N, int K, float alpha,
  *   "mfma bm=160 bn=160 bk=32 waves=2x2 vecA=1 vecB=1 grid=1024"
  * into buf (at most buflen bytes, truncated if needed).  The leading word
  * names the kernel: "none" (nothing to do), "scale" (K == 0 or alpha == 0),
- * "mfma", "valu" or "skinny".  Returns 0, or the same negative codes as
+ * "mfma", "valu", "skinny", "stream16" or "ladder".  Returns 0, or the same negative codes as
  * sgemm_f32_variant (pointer checks excepted), or -12 when num_cus < 1 or
  * buf is NULL with buflen > 0.
  */

@@ -86,7 +86,8 @@ def test_hip_failure_is_a_positive_code():
 def test_bad_variant():
     names = ("M", "N", "K", "alpha", "A", "lda", "B", "ldb", "beta", "C", "ldc")
     args = dict(zip(names, GOOD))
-    for v in (-1, 4, 15, sg.SGEMM_VARIANT_MFMA_TILE + sg.sgemm_num_mfma_tiles()):
+    for v in (-1, 4, 15, sg.SGEMM_VARIANT_MFMA_TILE + sg.sgemm_num_mfma_tiles(),
+              sg.SGEMM_VARIANT_LADDER - 1, sg.SGEMM_VARIANT_LADDER + sg.SGEMM_LADDER_RUNGS):
         assert sg.sgemm_f32_variant(v, *[args[n] for n in names], 0) == sg.SGEMM_ERR_BAD_VARIANT
         assert sg.sgemm_plan(v, 4, 5, 6, 6, 5, 5, 1.0, 256)[0] == sg.SGEMM_ERR_BAD_VARIANT
 
@@ -162,3 +163,21 @@ def test_forced_tiles():
         assert p["kind"] == "mfma"
         seen.add((p["bm"], p["bn"]))
     assert len(seen) == n
+
+
+def test_ladder_rungs():
+    """Each rung of the pages' SIMT ladder is its own kernel; the plan names
+    it and covers the output with its tile."""
+    for r, name in enumerate(sg.LADDER_RUNG_NAMES):
+        for M, N, K in [(5120, 5120, 5120), (33, 1605632, 27), (1, 1, 1)]:
+            p = plan(M, N, K, variant=sg.SGEMM_VARIANT_LADDER + r)
+            assert p["kind"] == "ladder" and p["rung"] == str(r) and p["name"] == name
+            tm, tn = (int(x) for x in p["tile"].split("x"))
+            assert int(p["grid"]) == -(-M // tm) * -(-N // tn)
+
+
+def test_ladder_constants_match_header():
+    text = open(HEADER).read()
+    assert re.search(r"SGEMM_VARIANT_LADDER\s*=\s*%d\b" % sg.SGEMM_VARIANT_LADDER, text)
+    assert re.search(r"#define SGEMM_LADDER_RUNGS %d\b" % sg.SGEMM_LADDER_RUNGS, text)
+    assert len(sg.LADDER_RUNG_NAMES) == sg.SGEMM_LADDER_RUNGS

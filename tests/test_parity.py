@@ -44,7 +44,9 @@ def _full_check(A, B, C, alpha, beta, variant=0, exact=False, **kw):
     return out
 
 
-FAMILIES = [0, 2, 3] + [16 + i for i in range(5)]
+# AUTO, VALU, SKINNY, the five forced MFMA tiles, and the eight rungs of the
+# pages' SIMT ladder (variant 32 + r).
+FAMILIES = [0, 2, 3] + [16 + i for i in range(5)] + [32 + r for r in range(8)]
 
 
 # ---------------------------------------------------------------- workloads
