@@ -22,6 +22,7 @@ SGEMM_VARIANT_VALU = 2
 SGEMM_VARIANT_SKINNY = 3
 SGEMM_VARIANT_MFMA_TILE = 16
 SGEMM_VARIANT_LADDER = 32
+SGEMM_VARIANT_STREAMK_TILE = 48
 SGEMM_LADDER_RUNGS = 8
 LADDER_RUNG_NAMES = ("naive", "coalesced", "lds", "tile1d", "tile2d", "regcache", "vec4", "dbuf")
 SGEMM_ERR_BAD_VARIANT = -100

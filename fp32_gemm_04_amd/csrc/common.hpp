@@ -25,9 +25,6 @@ struct GemmArgs {
 // Host-side handle of a tile kernel: all of them take the argument block.
 typedef void (*KernelFn)(GemmArgs);
 
-// Direct-load MFMA kernel for a tile shape and waves-per-SIMD target, or
-// null if none is built for it (defined in mfma_dl.hip).
-KernelFn direct_kernel(int bm, int bn, int wm, int wn, int wpe);
 
 // Number of XCDs (accelerator complex dies) on MI355X.  The hardware hands
 // consecutive workgroup ids to the XCDs in turn, and each XCD has its own L2.
@@ -60,6 +57,107 @@ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
     tm = first_m + in_group % rows;
     tn = in_group / rows;
 }
+
+// Stream-K.  When the output tiles do not fill whole rounds of resident
+// workgroups, the work is cut finer: a unit is one BK-deep k-iteration of one
+// tile, units are numbered tile by tile, and `workers` resident workgroups
+// take equal contiguous ranges of them, [w U / W, (w+1) U / W).  A worker's
+// range covers whole tiles, written to C as usual, plus at most a partial
+// tile at each end.  A partial tile's raw sum goes to the workspace, slot
+// 2 w for the worker's first segment and 2 w + 1 for its last; a second
+// kernel (the fixup) then adds a split tile's partials in worker order and
+// applies alpha and beta.  The result does not depend on timing, and no
+// workgroup waits for another.
+struct SkArgs {
+    float *ws;       // 2 * workers slots of BM * BN floats
+    int64_t units;   // tiles * iters
+    int iters;       // k-iterations per tile
+    int bk;          // k per iteration
+    int workers;     // resident workgroups (<= units)
+};
+
+__host__ __device__ inline int64_t sk_begin(int64_t w, int64_t units, int workers)
+{
+    return w * units / workers;
+}
+
+// The worker whose range holds unit u.
+__host__ __device__ inline int sk_worker_of(int64_t u, int64_t units, int workers)
+{
+    return (int)(((u + 1) * workers - 1) / units);
+}
+
+// Logical worker of workgroup bid: workgroups bid, bid + 8, ... run on one
+// XCD and take adjacent ranges, so the tiles they share meet in its L2.
+__device__ __forceinline__ int sk_logical_worker(int bid, int workers)
+{
+    const int q = workers / kNumXcd, r = workers % kNumXcd;
+    const int x = bid % kNumXcd, i = bid / kNumXcd;
+    return x * q + (x < r ? x : r) + i;
+}
+
+// Tile t of the grouped raster (group_m tile rows at a time).
+__host__ __device__ inline void sk_tile(int t, int tiles_m, int tiles_n, int group_m, int &tm,
+                                        int &tn)
+{
+    const int per_group = group_m * tiles_n;
+    const int group = t / per_group;
+    const int first_m = group * group_m;
+    const int rows = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+    const int in_group = t - group * per_group;
+    tm = first_m + in_group % rows;
+    tn = in_group / rows;
+}
+
+// Runs this workgroup's stream-K range: body(args, m0, n0) once per tile
+// segment, with args narrowed to the segment's k-range and, for a partial
+// tile, pointed at the workspace slot (row pitch BN, alpha 1, beta 0).
+template <int BM, int BN, typename Body>
+__device__ __forceinline__ void sk_run(const GemmArgs &g, const SkArgs &s, Body body)
+{
+    const int w = sk_logical_worker(blockIdx.x, s.workers);
+    int64_t u = sk_begin(w, s.units, s.workers);
+    const int64_t u1 = sk_begin(w + 1, s.units, s.workers);
+    bool first = true;
+    while (u < u1) {
+        const int t = (int)(u / s.iters);
+        const int it0 = (int)(u - (int64_t)t * s.iters);
+        const int64_t left = u1 - u;
+        const int it1 = left < (int64_t)(s.iters - it0) ? it0 + (int)left : s.iters;
+        int tm, tn;
+        sk_tile(t, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int k0 = it0 * s.bk;
+        const int k1 = it1 * s.bk < g.K ? it1 * s.bk : g.K;
+        GemmArgs a = g;
+        a.A = g.A + k0;
+        a.B = g.B + (int64_t)k0 * g.ldb;
+        a.K = k1 - k0;
+        if (it0 != 0 || it1 != s.iters) {
+            // Element (m0 + r, n0 + c) of the tile lands at slot[r * BN + c].
+            // Formed in integers: the shifted base itself lies outside the slot.
+            const float *slot = s.ws + (int64_t)(2 * w + (first ? 0 : 1)) * (BM * BN);
+            a.C = reinterpret_cast<float *>(reinterpret_cast<uintptr_t>(slot) -
+                                            (uintptr_t)((int64_t)m0 * BN + n0) * sizeof(float));
+            a.ldc = BN;
+            a.alpha = 1.f;
+            a.beta = 0.f;
+        }
+        body(a, m0, n0);
+        __syncthreads();  // the next segment reuses the LDS buffers
+        u += it1 - it0;
+        first = false;
+    }
+}
+
+// Host-side handles of the tile kernels: one output tile per workgroup, or a
+// stream-K range per workgroup.
+typedef void (*SkKernelFn)(GemmArgs, SkArgs);
+
+// Direct-load MFMA kernel for a tile shape and waves-per-SIMD target, or
+// null if none is built for it (defined in mfma_dl.hip); the stream-K form.
+KernelFn direct_kernel(int bm, int bn, int wm, int wn, int wpe);
+SkKernelFn direct_sk_kernel(int bm, int bn, int wm, int wn, int wpe);
 
 // Balancing a kernel's work per SIMD, for kernels that run one workgroup
 // per CU whose 4 WPE waves fill it: each SIMD has its own matrix core, and

@@ -1,6 +1,7 @@
 // The direct-load MFMA tile kernels, in a translation unit of their own so
 // that they can be compiled with the instruction scheduler that suits them
-// (see _build.py); the host side reaches them through direct_kernel().
+// (see _build.py); the host side reaches them through direct_kernel() and
+// direct_sk_kernel().
 #include "mfma_dl.hpp"
 
 namespace sgemm {
@@ -11,6 +12,15 @@ KernelFn direct_kernel(int bm, int bn, int wm, int wn, int wpe)
     if (bm == 160 && bn == 160 && wm == 2 && wn == 2) return mfma_dl_kernel<160, 160, 2, 2, 2>;
     if (bm == 128 && bn == 128 && wm == 2 && wn == 2) return mfma_dl_kernel<128, 128, 2, 2, 2>;
     if (bm == 64 && bn == 256 && wm == 1 && wn == 4) return mfma_dl_kernel<64, 256, 1, 4, 2>;
+    return nullptr;
+}
+
+SkKernelFn direct_sk_kernel(int bm, int bn, int wm, int wn, int wpe)
+{
+    if (wpe != 2) return nullptr;
+    if (bm == 160 && bn == 160 && wm == 2 && wn == 2) return mfma_dl_sk_kernel<160, 160, 2, 2, 2>;
+    if (bm == 128 && bn == 128 && wm == 2 && wn == 2) return mfma_dl_sk_kernel<128, 128, 2, 2, 2>;
+    if (bm == 64 && bn == 256 && wm == 1 && wn == 4) return mfma_dl_sk_kernel<64, 256, 1, 4, 2>;
     return nullptr;
 }
 

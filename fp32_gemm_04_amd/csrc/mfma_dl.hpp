@@ -267,4 +267,24 @@ mfma_dl_kernel(GemmArgs g)
         mfma_tile_body<BM, BN, 16, WM, WN, 2, true, true, true>(g, m0, n0, lds, lds + 2 * T::LDS_A);
 }
 
+// Stream-K form: this workgroup's range of tile segments (sk_run), each
+// through the same two bodies.
+template <int BM, int BN, int WM, int WN, int WPE>
+__global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+mfma_dl_sk_kernel(GemmArgs g, SkArgs s)
+{
+    using T = MfmaTile<BM, BN, 16, WM, WN>;
+    constexpr int DL = MfmaDl<BM, BN, WM, WN>::LDS;
+    constexpr int RG = 2 * (T::LDS_A + T::LDS_B);
+    __shared__ __attribute__((aligned(16))) float lds[DL > RG ? DL : RG];
+
+    sk_run<BM, BN>(g, s, [&](const GemmArgs &a, int m0, int n0) __attribute__((always_inline)) {
+        if (m0 + BM <= a.M && n0 + BN <= a.N)
+            mfma_dl_body<BM, BN, WM, WN>(a, m0, n0, lds);
+        else
+            mfma_tile_body<BM, BN, 16, WM, WN, 2, true, true, true>(a, m0, n0, lds,
+                                                                      lds + 2 * T::LDS_A);
+    });
+}
+
 }  // namespace sgemm

@@ -391,4 +391,22 @@ mfma_tile_kernel(GemmArgs g)
         mfma_tile_body<BM, BN, BK, WM, WN, ST, AVEC, BVEC, true>(g, m0, n0, As, Bs);
 }
 
+// Stream-K form: this workgroup's range of tile segments (sk_run).
+template <int BM, int BN, int BK, int WM, int WN, int WPE, int ST, bool AVEC, bool BVEC>
+__global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+mfma_tile_sk_kernel(GemmArgs g, SkArgs s)
+{
+    using T = MfmaTile<BM, BN, BK, WM, WN>;
+    constexpr int NBUF = ST == 3 ? 3 : 2;
+    __shared__ __attribute__((aligned(16))) float As[NBUF * T::LDS_A];
+    __shared__ __attribute__((aligned(16))) float Bs[NBUF * T::LDS_B];
+
+    sk_run<BM, BN>(g, s, [&](const GemmArgs &a, int m0, int n0) __attribute__((always_inline)) {
+        if (m0 + BM <= a.M && n0 + BN <= a.N)
+            mfma_tile_body<BM, BN, BK, WM, WN, ST, AVEC, BVEC, false>(a, m0, n0, As, Bs);
+        else
+            mfma_tile_body<BM, BN, BK, WM, WN, ST, AVEC, BVEC, true>(a, m0, n0, As, Bs);
+    });
+}
+
 }  // namespace sgemm

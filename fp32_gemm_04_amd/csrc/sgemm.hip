@@ -11,6 +11,8 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "../../include/sgemm.h"
 #include "common.hpp"
@@ -23,6 +25,54 @@
 namespace sgemm {
 
 __device__ float g_stream_zero16[4] = {0.f, 0.f, 0.f, 0.f};
+
+// Stream-K fixup.  Workgroup (x, y) handles elements [1024 y, 1024 (y+1))
+// of output tile x, four adjacent ones per thread (BN is a multiple of 4, so
+// they share a row).  A tile whose units all fall to one worker was written
+// in full and is skipped.  Otherwise its partial sums are added in worker
+// order, from the slot each worker used (2 w if the tile was its first
+// segment, 2 w + 1 if its last), and C is written as alpha * sum + beta * C
+// (C not read when beta == 0).  The slot list (one 64-bit division per
+// worker) is worked out once per workgroup, into LDS.
+constexpr int kSkMaxWorkers = 1024;  // 256 CUs x 4 workgroups
+constexpr int kSkFixupElems = 1024;  // elements per fixup workgroup
+
+__global__ void __launch_bounds__(256) sk_fixup_kernel(GemmArgs g, SkArgs s, int bm, int bn)
+{
+    __shared__ int slot_of[kSkMaxWorkers];
+    const int t = blockIdx.x;
+    const int e = (blockIdx.y * 256 + threadIdx.x) * 4;
+    const int64_t ua = (int64_t)t * s.iters;
+    const int wa = sk_worker_of(ua, s.units, s.workers);
+    const int wb = sk_worker_of(ua + s.iters - 1, s.units, s.workers);
+    if (wa == wb) return;
+    const int nw = wb - wa + 1;
+    for (int i = threadIdx.x; i < nw; i += blockDim.x) {
+        const int w = wa + i;
+        const int64_t b = sk_begin(w, s.units, s.workers);
+        slot_of[i] = 2 * w + (b >= ua ? 0 : 1);
+    }
+    __syncthreads();
+    if (e >= bm * bn) return;
+    int tm, tn;
+    sk_tile(t, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+    const int r = e / bn, c = e - r * bn;
+    const int row = tm * bm + r, col = tn * bn + c;
+    if (row >= g.M || col >= g.N) return;
+    const int64_t slot_floats = (int64_t)bm * bn;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < nw; ++i)
+        sum += *reinterpret_cast<const f32x4 *>(s.ws + slot_of[i] * slot_floats + e);
+    float *pc = g.C + (int64_t)row * g.ldc + col;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (col + q < g.N) {
+            float v = g.alpha * sum[q];
+            if (g.beta != 0.f) v = fmaf(g.beta, pc[q], v);
+            pc[q] = v;
+        }
+    }
+}
 
 namespace {
 
@@ -37,21 +87,32 @@ struct TileConfig {
     KernelFn fn[2][2];   // [A 128-bit loads][B 128-bit loads]
     KernelFn dl;         // direct-to-LDS variant (K % 16 == 0, aligned rows) or null
     double dl_efficiency;  // ... when the direct-load variant runs
+    SkKernelFn sk_fn[2][2];  // stream-K forms of fn and dl
+    SkKernelFn sk_dl;
 };
 
 // WPE (waves per SIMD) = OCC workgroups per CU x waves per workgroup / 4 SIMDs.
 #define SGEMM_MFMA_WPE(WM, WN, OCC) ((OCC) * (WM) * (WN) / 4)
 #define SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, AV, BV) \
     mfma_tile_kernel<BM, BN, BK, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), ST, AV, BV>
-#define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, ST, EFF, DL, DLEFF)           \
+#define SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, AV, BV) \
+    mfma_tile_sk_kernel<BM, BN, BK, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), ST, AV, BV>
+#define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, ST, EFF, DL, DLEFF, SKDL)     \
     {"mfma", BM, BN, BK, WM, WN, WM * WN * 64, OCC, EFF,                         \
      {{SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, false),             \
        SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, true)},             \
       {SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, false),              \
        SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, true)}},             \
-     DL, DLEFF}
+     DL, DLEFF,                                                                  \
+     {{SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, false),          \
+       SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, true)},          \
+      {SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, false),           \
+       SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, true)}},          \
+     SKDL}
 #define SGEMM_DL_KERNEL(BM, BN, WM, WN, OCC) \
     direct_kernel(BM, BN, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC))
+#define SGEMM_DL_SK_KERNEL(BM, BN, WM, WN, OCC) \
+    direct_sk_kernel(BM, BN, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC))
 
 // The MFMA tile table.  Occupancy (workgroups per CU) is what LDS and the
 // register budget allow.  Efficiencies are the fractions of the CU's fp32
@@ -59,17 +120,20 @@ struct TileConfig {
 // 4096^3, 2048^3, the im2col mid shapes): register-staged path, then
 // direct-load path.
 const TileConfig kMfmaTiles[] = {
-    SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 3, 0.77, SGEMM_DL_KERNEL(160, 160, 2, 2, 2), 0.88),
-    SGEMM_MFMA_ENTRY(128, 128, 16, 2, 2, 2, 3, 0.82, SGEMM_DL_KERNEL(128, 128, 2, 2, 2), 0.90),
-    SGEMM_MFMA_ENTRY(64, 64, 32, 2, 2, 4, 2, 0.70, nullptr, 0.0),
-    SGEMM_MFMA_ENTRY(32, 256, 32, 1, 4, 2, 2, 0.50, nullptr, 0.0),
-    SGEMM_MFMA_ENTRY(64, 256, 16, 1, 4, 2, 3, 0.60, SGEMM_DL_KERNEL(64, 256, 1, 4, 2), 0.90),
+    SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 3, 0.77, SGEMM_DL_KERNEL(160, 160, 2, 2, 2), 0.88,
+                     SGEMM_DL_SK_KERNEL(160, 160, 2, 2, 2)),
+    SGEMM_MFMA_ENTRY(128, 128, 16, 2, 2, 2, 3, 0.82, SGEMM_DL_KERNEL(128, 128, 2, 2, 2), 0.90,
+                     SGEMM_DL_SK_KERNEL(128, 128, 2, 2, 2)),
+    SGEMM_MFMA_ENTRY(64, 64, 32, 2, 2, 4, 2, 0.70, nullptr, 0.0, nullptr),
+    SGEMM_MFMA_ENTRY(32, 256, 32, 1, 4, 2, 2, 0.50, nullptr, 0.0, nullptr),
+    SGEMM_MFMA_ENTRY(64, 256, 16, 1, 4, 2, 3, 0.60, SGEMM_DL_KERNEL(64, 256, 1, 4, 2), 0.90,
+                     SGEMM_DL_SK_KERNEL(64, 256, 1, 4, 2)),
 };
 
 const TileConfig kValuTile = {"valu", 128, 128, 8, 2, 2, 256, 2, 0.45,
                               {{valu_tile_kernel<false, false>, valu_tile_kernel<false, true>},
                                {valu_tile_kernel<true, false>, valu_tile_kernel<true, true>}},
-                              nullptr, 0.0};
+                              nullptr, 0.0, {{nullptr, nullptr}, {nullptr, nullptr}}, nullptr};
 
 constexpr double kHbmBytesPerCuCycle = 8.0e12 / (256 * 2.4e9);  // MI355X HBM share
 constexpr double kFlopsPerCuCycle = 256.0;                      // fp32 MFMA per CU
@@ -102,22 +166,6 @@ double estimate_cycles(const TileConfig &c, int M, int N, int K, int num_cus, bo
     return compute > memory ? compute : memory;
 }
 
-const TileConfig *select_tile(int variant, int M, int N, int K, int num_cus, bool direct)
-{
-    if (variant == SGEMM_VARIANT_VALU) return &kValuTile;
-    if (variant >= SGEMM_VARIANT_MFMA_TILE) return &kMfmaTiles[variant - SGEMM_VARIANT_MFMA_TILE];
-    const TileConfig *best = nullptr;
-    double best_cycles = 0.0;
-    for (const TileConfig &c : kMfmaTiles) {
-        const double cyc = estimate_cycles(c, M, N, K, num_cus, direct);
-        if (best == nullptr || cyc < best_cycles) {
-            best = &c;
-            best_cycles = cyc;
-        }
-    }
-    return best;
-}
-
 // Tile rows per raster group: enough rows that the tiles one XCD holds at
 // once (its 32 CUs times occupancy) form a roughly square patch.
 int group_rows(const TileConfig &c, int tiles_m, int tiles_n, int num_cus)
@@ -128,6 +176,168 @@ int group_rows(const TileConfig &c, int tiles_m, int tiles_n, int num_cus)
     if (gm > tiles_m) gm = tiles_m;
     (void)tiles_n;
     return gm > 0 ? gm : 1;
+}
+
+// Stream-K plan for tile config c (see common.hpp), with its estimated time.
+struct SkPlan {
+    bool use;
+    SkArgs args;        // ws filled in at launch
+    int split_tiles;    // tiles whose units span more than one worker
+    int partials;       // partial tile segments written to the workspace
+    size_t ws_bytes;    // 2 * workers * BM * BN floats
+    double cycles;      // estimate, CU cycles
+};
+
+// Measured on MI355X (mid im2col shapes, 1024^3 to 4608^3): the stream-K
+// kernel's per-unit time is about 6% above one tile per workgroup (a pipeline
+// fill per segment), and the fixup pass moves its bytes at about 5.3 TB/s,
+// plus a launch.  Stream-K is taken only when its estimate is 5% below the
+// best one-tile-per-workgroup estimate.
+constexpr double kSkUnitOverhead = 1.06;
+constexpr double kSkFixupBytesPerCycle = 5.3e12 / 2.4e9;
+constexpr double kSkFixupLaunchCycles = 7200.0;
+constexpr double kSkMargin = 0.95;
+// Below this (one tile per workgroup, estimated) the fixup launch costs more
+// than stream-K saves (512^3 and 768^3 measured 9-25% slower with it).
+constexpr double kSkMinCycles = 60000.0;
+
+SkPlan plan_streamk(const TileConfig &c, int M, int N, int K, int num_cus, bool direct)
+{
+    SkPlan p = {};
+    if (c.sk_fn[0][0] == nullptr || K <= 0 || M <= 0 || N <= 0) return p;
+    const bool dl = direct && c.sk_dl != nullptr;
+    const int bk = dl ? 16 : c.bk;
+    const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
+    const int iters = (int)ceil_div(K, bk);
+    const int64_t units = tiles * iters;
+    if (tiles > 0x7fffffff || units <= 0) return p;
+    const int64_t slots = (int64_t)num_cus * c.occupancy;
+    const int64_t cap = slots < kSkMaxWorkers ? slots : kSkMaxWorkers;
+    const int workers = (int)(units < cap ? units : cap);
+    // Partial segments: a worker's first segment unless it starts a tile and
+    // covers all of it; its last (if another) unless it ends a tile.  Split
+    // tiles: tiles holding a worker boundary.
+    int partials = 0, split = 0;
+    int64_t last_split = -1;
+    for (int w = 0; w < workers; ++w) {
+        const int64_t b = sk_begin(w, units, workers), e = sk_begin(w + 1, units, workers);
+        const int64_t first_end = (b / iters + 1) * iters;
+        if (b % iters != 0 || e < first_end) ++partials;
+        if (e > first_end && e % iters != 0) ++partials;
+        if (w > 0 && b % iters != 0 && b / iters != last_split) {
+            ++split;
+            last_split = b / iters;
+        }
+    }
+    p.args.ws = nullptr;
+    p.args.units = units;
+    p.args.iters = iters;
+    p.args.bk = bk;
+    p.args.workers = workers;
+    p.split_tiles = split;
+    p.partials = partials;
+    p.ws_bytes = (size_t)2 * workers * c.bm * c.bn * sizeof(float);
+
+    double eff = dl ? c.dl_efficiency : c.efficiency;
+    if ((M % c.bm != 0 || N % c.bn != 0) && c.efficiency < eff) eff = c.efficiency;
+    const double unit_cycles = 2.0 * c.bm * c.bn * bk / (kFlopsPerCuCycle * eff);
+    const double compute = (double)units / num_cus * unit_cycles * kSkUnitOverhead;
+    const double bytes = 4.0 * ((double)M * K + (double)K * N + (double)M * N);
+    const double memory = bytes / (kHbmBytesPerCuCycle * num_cus);
+    // The fixup reads every partial and reads and writes C of the split tiles.
+    const double fix_bytes = ((double)partials + 2.0 * split) * c.bm * c.bn * 4.0;
+    const double fixup = split > 0 ? fix_bytes / kSkFixupBytesPerCycle + kSkFixupLaunchCycles : 0;
+    p.cycles = (compute > memory ? compute : memory) + fixup;
+    return p;
+}
+
+// The kernel a call runs: a tile config, one tile per workgroup or stream-K.
+struct Choice {
+    const TileConfig *c;
+    SkPlan sk;
+};
+
+Choice choose(int variant, int M, int N, int K, int num_cus, bool direct)
+{
+    Choice ch = {nullptr, {}};
+    if (variant == SGEMM_VARIANT_VALU) {
+        ch.c = &kValuTile;
+        return ch;
+    }
+    if (variant >= SGEMM_VARIANT_STREAMK_TILE) {
+        ch.c = &kMfmaTiles[variant - SGEMM_VARIANT_STREAMK_TILE];
+        ch.sk = plan_streamk(*ch.c, M, N, K, num_cus, direct);
+        ch.sk.use = ch.sk.args.workers > 0;
+        return ch;
+    }
+    if (variant >= SGEMM_VARIANT_MFMA_TILE) {
+        ch.c = &kMfmaTiles[variant - SGEMM_VARIANT_MFMA_TILE];
+        return ch;
+    }
+    double best = 0.0;
+    for (const TileConfig &c : kMfmaTiles) {
+        const double dp = estimate_cycles(c, M, N, K, num_cus, direct);
+        if (ch.c == nullptr || dp < best) {
+            ch = {&c, {}};
+            best = dp;
+        }
+    }
+    // Automatic stream-K only on the direct-load path: with unaligned
+    // operands the register-staged segments run below the efficiency the
+    // estimate assumes ((384, 14161, 1152) measured 4.5% slower with it).
+    if (!direct || best < kSkMinCycles) return ch;
+    for (const TileConfig &c : kMfmaTiles) {
+        if (c.sk_dl == nullptr) continue;
+        SkPlan sp = plan_streamk(c, M, N, K, num_cus, direct);
+        if (sp.args.workers > 0 && sp.cycles / kSkMargin < best) {
+            sp.use = true;
+            ch = {&c, sp};
+            best = sp.cycles / kSkMargin;
+        }
+    }
+    return ch;
+}
+
+// Stream-K workspaces, one per (device, stream): calls on one stream run in
+// order and share it; calls on different streams never do.  Allocated on
+// first need and grown, never freed.
+struct Workspace {
+    int device;
+    hipStream_t stream;
+    void *ptr;
+    size_t bytes;
+};
+std::mutex g_ws_mutex;
+std::vector<Workspace> g_ws;
+
+hipError_t workspace(hipStream_t stream, size_t bytes, float **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    for (Workspace &w : g_ws) {
+        if (w.device != dev || w.stream != stream) continue;
+        if (w.bytes < bytes) {
+            // Work queued earlier on this stream may still read the old block;
+            // hipFree waits for the device to finish with it.
+            e = hipFree(w.ptr);
+            if (e != hipSuccess) return e;
+            w.ptr = nullptr;
+            w.bytes = 0;
+            e = hipMalloc(&w.ptr, bytes);
+            if (e != hipSuccess) return e;
+            w.bytes = bytes;
+        }
+        *out = static_cast<float *>(w.ptr);
+        return hipSuccess;
+    }
+    void *ptr = nullptr;
+    e = hipMalloc(&ptr, bytes);
+    if (e != hipSuccess) return e;
+    g_ws.push_back({dev, stream, ptr, bytes});
+    *out = static_cast<float *>(ptr);
+    return hipSuccess;
 }
 
 // Argument checks of the C ABI (no HIP call).  Returns 0 or -p.
@@ -160,6 +370,7 @@ bool valid_variant(int v)
     return v == SGEMM_VARIANT_AUTO || v == SGEMM_VARIANT_MFMA || v == SGEMM_VARIANT_VALU ||
            v == SGEMM_VARIANT_SKINNY ||
            (v >= SGEMM_VARIANT_MFMA_TILE && v < SGEMM_VARIANT_MFMA_TILE + kNumMfmaTiles) ||
+           (v >= SGEMM_VARIANT_STREAMK_TILE && v < SGEMM_VARIANT_STREAMK_TILE + kNumMfmaTiles) ||
            is_ladder(v);
 }
 
@@ -412,13 +623,38 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
         variant = SGEMM_VARIANT_VALU;
     }
     const bool direct = avec && bvec && K % 16 == 0;
-    const TileConfig *c = select_tile(variant, M, N, K, cus, direct);
+    const Choice ch = choose(variant, M, N, K, cus, direct);
+    const TileConfig *c = ch.c;
     g.tiles_m = (int)ceil_div(M, c->bm);
     g.tiles_n = (int)ceil_div(N, c->bn);
     g.group_m = group_rows(*c, g.tiles_m, g.tiles_n, cus);
     const int64_t blocks = (int64_t)g.tiles_m * g.tiles_n;
     if (blocks > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
     const int threads = c->threads;
+
+    const bool force_sk = variant >= SGEMM_VARIANT_STREAMK_TILE;
+    const SkPlan &sp = ch.sk;
+    if (sp.use) {
+        float *ws = nullptr;
+        const hipError_t we = workspace(stream, sp.ws_bytes, &ws);
+        if (we != hipSuccess) {
+            if (force_sk) return (int)we;
+            (void)hipGetLastError();  // fall back to one tile per workgroup
+        } else {
+            SkArgs sa = sp.args;
+            sa.ws = ws;
+            const SkKernelFn fn = c->sk_dl && direct ? c->sk_dl : c->sk_fn[avec][bvec];
+            hipLaunchKernelGGL(fn, dim3((unsigned)sa.workers), dim3(threads), 0, stream, g, sa);
+            const hipError_t le = hipGetLastError();
+            if (le != hipSuccess) return (int)le;
+            if (sp.split_tiles > 0)
+                hipLaunchKernelGGL(sk_fixup_kernel,
+                                   dim3((unsigned)blocks,
+                                        (unsigned)ceil_div(c->bm * c->bn, kSkFixupElems)),
+                                   dim3(256), 0, stream, g, sa, c->bm, c->bn);
+            return (int)hipGetLastError();
+        }
+    }
     const KernelFn fn = c->dl && direct ? c->dl : c->fn[avec][bvec];
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), 0, stream, g);
     return (int)hipGetLastError();
@@ -481,16 +717,19 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
                       (long long)ceil_div(M, r.tile_m) * ceil_div(N, r.tile_n));
     } else {
         const bool direct = (lda & 3) == 0 && (ldb & 3) == 0 && K % 16 == 0;
-        const TileConfig *c = select_tile(variant, M, N, K, num_cus, direct);
+        const Choice ch = choose(variant, M, N, K, num_cus, direct);
+        const TileConfig *c = ch.c;
         const int tiles_m = (int)ceil_div(M, c->bm);
         const int tiles_n = (int)ceil_div(N, c->bn);
         const bool dl = c->dl && direct;
+        const SkPlan &sp = ch.sk;
         std::snprintf(text, sizeof text,
                       "%s bm=%d bn=%d bk=%d waves=%dx%d vecA=%d vecB=%d grid=%lld group=%d "
-                      "load=%s",
+                      "load=%s streamk=%d split=%d",
                       c->family, c->bm, c->bn, dl ? 16 : c->bk, c->wm, c->wn, (lda & 3) == 0,
                       (ldb & 3) == 0, (long long)tiles_m * tiles_n,
-                      group_rows(*c, tiles_m, tiles_n, num_cus), dl ? "direct" : "regs");
+                      group_rows(*c, tiles_m, tiles_n, num_cus), dl ? "direct" : "regs",
+                      sp.use ? sp.args.workers : 0, sp.use ? sp.split_tiles : 0);
     }
     if (buflen > 0) {
         std::strncpy(buf, text, (size_t)buflen - 1);

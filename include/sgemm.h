@@ -46,7 +46,12 @@ enum sgemm_variant {
      *   7 dbuf: as 6, double-buffered slabs (= SGEMM_VARIANT_VALU).
      * Any shape runs.  For measurement beside the pages' tables; the
      * selector never picks them. */
-    SGEMM_VARIANT_LADDER = 32
+    SGEMM_VARIANT_LADDER = 32,
+    /* SGEMM_VARIANT_STREAMK_TILE + i forces entry i of the MFMA tile table
+     * run stream-K: resident workgroups take equal ranges of (tile,
+     * k-slab) units and a second kernel adds the partial tiles (the
+     * selector does this by itself when it pays).  For tests and tuning. */
+    SGEMM_VARIANT_STREAMK_TILE = 48
 };
 
 #define SGEMM_LADDER_RUNGS 8
@@ -70,9 +75,21 @@ enum sgemm_variant {
  *   stream    HIP stream the work is queued on (0 = the null stream).
  *
  * Ownership and synchronisation: all buffers belong to the caller and stay
- * on the current HIP device.  The call allocates, frees, copies and
- * synchronises nothing; it queues kernels on `stream` and returns.  Results
- * are visible once the stream has been synchronised.
+ * on the current HIP device.  The call copies and synchronises nothing; it
+ * queues kernels on `stream` and returns.  Results are visible once the
+ * stream has been synchronised.
+ *
+ * Workspace: shapes that the selector runs stream-K (when whole tiles would
+ * leave the last round of resident workgroups part-empty; see
+ * SGEMM_VARIANT_STREAMK_TILE) keep partial tiles in a workspace of up to
+ * 2 x (resident workgroups) x (tile floats), 64 MiB for 128 x 128 tiles on
+ * 256 CUs.  The library owns one per (device, stream): the first call that
+ * needs it allocates it with hipMalloc, a call that needs more frees and
+ * reallocates it (hipFree waits for the device), and it is kept until the
+ * process ends.  Calls on one stream share it, in stream order; calls on
+ * different streams never do.  If the allocation fails the call runs one
+ * tile per workgroup instead.  Make the first such call on a stream outside
+ * graph capture.  Other shapes allocate nothing.
  *
  * Pointers need only float (4-byte) alignment; 16-byte aligned operands
  * with leading dimensions divisible by 4 take 128-bit load paths.
@@ -93,13 +110,15 @@ enum sgemm_variant {
  * case nothing was queued.
  *
  * Accuracy: each element is a fp32 sum of fp32 products (matrix-core
- * accumulation) scaled by alpha plus beta times the old value.  It is
+ * accumulation) scaled by alpha plus beta times the old value; stream-K
+ * adds the partial sums of a tile in a fixed order, so results repeat bit
+ * for bit from call to call.  It is
  * within 1e-5 * (|alpha| * sum_k |A(i,k) B(k,j)| + |beta C(i,j)|) + 1e-6 of
  * the exact result for data like the benchmark's, and exact for integer
  * data whose partial sums stay below 2^24.
  *
- * Thread safety: re-entrant; the only shared state is a per-device cache of
- * the compute-unit count, filled once.
+ * Thread safety: re-entrant; the shared state is a per-device cache of the
+ * compute-unit count, filled once, and the workspace table, under a mutex.
  */
 int sgemm_f32(int M, int N, int K, float alpha, const float *A, int lda,
               const float *B, int ldb, float beta, float *C, int ldc,

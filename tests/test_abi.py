@@ -87,7 +87,8 @@ def test_bad_variant():
     names = ("M", "N", "K", "alpha", "A", "lda", "B", "ldb", "beta", "C", "ldc")
     args = dict(zip(names, GOOD))
     for v in (-1, 4, 15, sg.SGEMM_VARIANT_MFMA_TILE + sg.sgemm_num_mfma_tiles(),
-              sg.SGEMM_VARIANT_LADDER - 1, sg.SGEMM_VARIANT_LADDER + sg.SGEMM_LADDER_RUNGS):
+              sg.SGEMM_VARIANT_LADDER - 1, sg.SGEMM_VARIANT_LADDER + sg.SGEMM_LADDER_RUNGS,
+              sg.SGEMM_VARIANT_STREAMK_TILE + sg.sgemm_num_mfma_tiles()):
         assert sg.sgemm_f32_variant(v, *[args[n] for n in names], 0) == sg.SGEMM_ERR_BAD_VARIANT
         assert sg.sgemm_plan(v, 4, 5, 6, 6, 5, 5, 1.0, 256)[0] == sg.SGEMM_ERR_BAD_VARIANT
 
@@ -181,3 +182,19 @@ def test_ladder_constants_match_header():
     assert re.search(r"SGEMM_VARIANT_LADDER\s*=\s*%d\b" % sg.SGEMM_VARIANT_LADDER, text)
     assert re.search(r"#define SGEMM_LADDER_RUNGS %d\b" % sg.SGEMM_LADDER_RUNGS, text)
     assert len(sg.LADDER_RUNG_NAMES) == sg.SGEMM_LADDER_RUNGS
+
+
+def test_streamk_plans():
+    """Forced stream-K names its resident workers; the workers never exceed
+    the (tile, k-slab) units, and a shape whose tiles fill whole rounds runs
+    one tile per workgroup."""
+    n = sg.sgemm_num_mfma_tiles()
+    for i in range(n):
+        for M, N, K in [(300, 200, 1000), (1, 1, 1), (5120, 5120, 5120)]:
+            p = plan(M, N, K, variant=sg.SGEMM_VARIANT_STREAMK_TILE + i)
+            assert p["kind"] == "mfma" and int(p["streamk"]) > 0
+            bm, bn, bk = int(p["bm"]), int(p["bn"]), int(p["bk"])
+            units = -(-M // bm) * -(-N // bn) * -(-K // bk)
+            assert int(p["streamk"]) <= units
+            assert int(p["split"]) < int(p["streamk"])
+    assert plan(5120, 5120, 5120)["streamk"] == "0"

@@ -44,9 +44,11 @@ def _full_check(A, B, C, alpha, beta, variant=0, exact=False, **kw):
     return out
 
 
-# AUTO, VALU, SKINNY, the five forced MFMA tiles, and the eight rungs of the
-# pages' SIMT ladder (variant 32 + r).
-FAMILIES = [0, 2, 3] + [16 + i for i in range(5)] + [32 + r for r in range(8)]
+# AUTO, VALU, SKINNY, the five forced MFMA tiles, the same five run
+# stream-K (variant 48 + i), and the eight rungs of the pages' SIMT ladder
+# (variant 32 + r).
+STREAMK_FAMILIES = [48 + i for i in range(5)]
+FAMILIES = [0, 2, 3] + [16 + i for i in range(5)] + STREAMK_FAMILIES + [32 + r for r in range(8)]
 
 
 # ---------------------------------------------------------------- workloads
@@ -186,7 +188,7 @@ def test_padded_leading_dimensions(variant):
 # still gives aligned B rows.
 DIRECT_SHAPES = [(160, 160, 16), (320, 320, 32), (321, 319, 48), (333, 517, 64),
                  (256, 512, 80), (480, 160, 1024)]
-DIRECT_FAMILIES = [16, 17, 20]
+DIRECT_FAMILIES = [16, 17, 20, 48, 49, 52]
 
 
 def _plan_load(variant, M, N, K, lda, ldb, ldc):
@@ -337,3 +339,32 @@ def test_skinny_kernel_shapes(M, N, K):
     Au = workloads.uniform(M, K, M * 7 + K)
     Bu = workloads.uniform(K, N, N * 3 + K)
     _full_check(Au, Bu, None, 1.0, 0.0, 3)
+
+
+# Stream-K on shapes with many k-slabs per tile and ragged edges: worker
+# ranges then start and end inside tiles (partial tiles at both ends, tiles
+# split over three or more workers) and edge tiles take the masked body.
+STREAMK_SHAPES = [(300, 200, 1000), (513, 257, 333), (160, 320, 2048), (97, 1000, 640)]
+
+
+@pytest.mark.parametrize("variant", STREAMK_FAMILIES)
+def test_streamk_integer_exact(variant):
+    for M, N, K in STREAMK_SHAPES:
+        A = workloads.integers(M, K, 41 * M + K)
+        B = workloads.integers(K, N, 43 * N + K)
+        C = workloads.integers(M, N, 47 * M + N)
+        _full_check(A, B, C, 1.5, 0.5, variant, exact=True)
+        _full_check(A, B, None, 1.0, 0.0, variant, exact=True)
+
+
+@pytest.mark.parametrize("variant", STREAMK_FAMILIES)
+def test_streamk_uniform_repeatable(variant):
+    """Uniform data within tolerance, and the same bits on a second call
+    (the partial tiles are added in a fixed order)."""
+    M, N, K = 513, 257, 333
+    A = workloads.uniform(M, K, 53)
+    B = workloads.uniform(K, N, 59)
+    C = workloads.uniform(M, N, 61)
+    first = _full_check(A, B, C, -0.75, 1.25, variant)
+    second = _full_check(A, B, C, -0.75, 1.25, variant)
+    assert np.array_equal(first.view(np.uint32), second.view(np.uint32))
