@@ -15,7 +15,9 @@ HBM before timing starts.  The line printed also carries:
     HBM bandwidth the algorithmic bytes imply;
   * valu_comparison and ladder: the vector-FMA kernels on the headline
     workload, the register-tile comparison kernel and each rung of the
-    pages' SIMT optimisation ladder (naive ... double-buffered).
+    pages' SIMT optimisation ladder (naive ... double-buffered);
+    ladder_im2col: the rungs that match page 2's five kernels on its six
+    im2col shapes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-im2col]
                        [--no-valu] [--no-ladder]
@@ -190,6 +192,38 @@ def bench_ladder(sg, case, call_args, stream, mfma_tflops):
     return out
 
 
+def bench_ladder_im2col(sg, stream):
+    """The ladder rungs that match the five kernels page 2 times on the six
+    im2col shapes (naive, coalesced, LDS tiles, 1-D and 2-D thread tiles):
+    median of 3 launches each, in microseconds."""
+    import torch
+    out = []
+    for case in workloads.SKINNY + workloads.MID:
+        log("ladder im2col", case.name)
+        _, _, _, dA, dB, dC = device_operands(case)
+        args = (case.M, case.N, case.K, case.alpha, dA.data_ptr(), case.K, dB.data_ptr(),
+                case.N, case.beta, dC.data_ptr(), case.N, stream.cuda_stream)
+        row = {"shape": [case.M, case.N, case.K]}
+        for r in range(5):
+            v = sg.SGEMM_VARIANT_LADDER + r
+            rc = sg.sgemm_f32_variant(v, *args)
+            assert rc == 0, sg.sgemm_status_string(rc)
+            times = []
+            for _ in range(3):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                sg.sgemm_f32_variant(v, *args)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            row[sg.LADDER_RUNG_NAMES[r] + "_us"] = round(float(np.median(times)) * 1e3, 1)
+        out.append(row)
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+    return out
+
+
 def traffic_probe(sg, case, call_args, stream):
     """Launch sequence for the HBM-traffic counter passes (run under rocprofv3
     --pmc FETCH_SIZE, then WRITE_SIZE): three plain copies of 1 GiB, whose
@@ -294,6 +328,7 @@ def main():
             "mfma_over_valu": round(tflops / vtf, 3)}
     if not args.no_ladder:
         result["ladder"] = bench_ladder(sg, case, call_args, stream, tflops)
+        result["ladder_im2col"] = bench_ladder_im2col(sg, stream)
     if not args.no_im2col:
         result["im2col"] = bench_im2col(sg, stream, args.im2col_reps)
     if not args.no_cpu:
