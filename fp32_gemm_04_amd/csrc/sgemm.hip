@@ -89,6 +89,7 @@ struct TileConfig {
     double dl_efficiency;  // ... when the direct-load variant runs
     SkKernelFn sk_fn[2][2];  // stream-K forms of fn and dl
     SkKernelFn sk_dl;
+    double one_efficiency;   // measured with one workgroup per CU (0: 0.85 x efficiency)
 };
 
 // WPE (waves per SIMD) = OCC workgroups per CU x waves per workgroup / 4 SIMDs.
@@ -97,7 +98,7 @@ struct TileConfig {
     mfma_tile_kernel<BM, BN, BK, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), ST, AV, BV>
 #define SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, AV, BV) \
     mfma_tile_sk_kernel<BM, BN, BK, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), ST, AV, BV>
-#define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, ST, EFF, DL, DLEFF, SKDL)     \
+#define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, ST, EFF, DL, DLEFF, SKDL, ONE) \
     {"mfma", BM, BN, BK, WM, WN, WM * WN * 64, OCC, EFF,                         \
      {{SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, false),             \
        SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, true)},             \
@@ -108,7 +109,7 @@ struct TileConfig {
        SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, true)},          \
       {SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, false),           \
        SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, true)}},          \
-     SKDL}
+     SKDL, ONE}
 #define SGEMM_DL_KERNEL(BM, BN, WM, WN, OCC) \
     direct_kernel(BM, BN, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC))
 #define SGEMM_DL_SK_KERNEL(BM, BN, WM, WN, OCC) \
@@ -118,22 +119,30 @@ struct TileConfig {
 // register budget allow.  Efficiencies are the fractions of the CU's fp32
 // peak measured with every CU holding `occupancy` workgroups (5120^3,
 // 4096^3, 2048^3, the im2col mid shapes): register-staged path, then
-// direct-load path.
+// direct-load path.  The last column is the efficiency measured when each CU
+// holds a single tile (2560^3, 2048^3, 1024^3): small tiles lose most there,
+// with little work per tile to hide load latency behind.
+// The last entry is the 64 x 64 tile with a three-stage pipeline at two
+// workgroups per CU: faster than the four-per-CU entry when a CU has one
+// tile (1024^3: 27.6 against 31.1 us), slower when it has several, which
+// its lower efficiency encodes.
 const TileConfig kMfmaTiles[] = {
     SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 3, 0.77, SGEMM_DL_KERNEL(160, 160, 2, 2, 2), 0.88,
-                     SGEMM_DL_SK_KERNEL(160, 160, 2, 2, 2)),
+                     SGEMM_DL_SK_KERNEL(160, 160, 2, 2, 2), 0.82),
     SGEMM_MFMA_ENTRY(128, 128, 16, 2, 2, 2, 3, 0.82, SGEMM_DL_KERNEL(128, 128, 2, 2, 2), 0.90,
-                     SGEMM_DL_SK_KERNEL(128, 128, 2, 2, 2)),
-    SGEMM_MFMA_ENTRY(64, 64, 32, 2, 2, 4, 2, 0.70, nullptr, 0.0, nullptr),
-    SGEMM_MFMA_ENTRY(32, 256, 32, 1, 4, 2, 2, 0.50, nullptr, 0.0, nullptr),
+                     SGEMM_DL_SK_KERNEL(128, 128, 2, 2, 2), 0.79),
+    SGEMM_MFMA_ENTRY(64, 64, 32, 2, 2, 4, 2, 0.70, nullptr, 0.0, nullptr, 0.44),
+    SGEMM_MFMA_ENTRY(32, 256, 32, 1, 4, 2, 2, 0.50, nullptr, 0.0, nullptr, 0.0),
     SGEMM_MFMA_ENTRY(64, 256, 16, 1, 4, 2, 3, 0.60, SGEMM_DL_KERNEL(64, 256, 1, 4, 2), 0.90,
-                     SGEMM_DL_SK_KERNEL(64, 256, 1, 4, 2)),
+                     SGEMM_DL_SK_KERNEL(64, 256, 1, 4, 2), 0.0),
+    SGEMM_MFMA_ENTRY(64, 64, 32, 2, 2, 2, 3, 0.55, nullptr, 0.0, nullptr, 0.495),
 };
 
 const TileConfig kValuTile = {"valu", 128, 128, 8, 2, 2, 256, 2, 0.45,
                               {{valu_tile_kernel<false, false>, valu_tile_kernel<false, true>},
                                {valu_tile_kernel<true, false>, valu_tile_kernel<true, true>}},
-                              nullptr, 0.0, {{nullptr, nullptr}, {nullptr, nullptr}}, nullptr};
+                              nullptr, 0.0, {{nullptr, nullptr}, {nullptr, nullptr}}, nullptr,
+                              0.0};
 
 constexpr double kHbmBytesPerCuCycle = 8.0e12 / (256 * 2.4e9);  // MI355X HBM share
 constexpr double kFlopsPerCuCycle = 256.0;                      // fp32 MFMA per CU
@@ -158,7 +167,10 @@ double estimate_cycles(const TileConfig &c, int M, int N, int K, int num_cus, bo
     // body; a CU that holds one sets the pace (measured at 2304^3: the 160 tile
     // with a 64-wide edge reaches 52 TFLOPS, the 64 tile without edges 98).
     if ((M % c.bm != 0 || N % c.bn != 0) && c.efficiency < eff) eff = c.efficiency;
-    if (per_cu < c.occupancy) eff *= 0.85;
+    if (per_cu == 1 && c.one_efficiency > 0.0)
+        eff = c.one_efficiency;
+    else if (per_cu < c.occupancy)
+        eff *= 0.85;
     const double kpad = (double)ceil_div(K, bk) * bk;
     const double compute = (double)per_cu * 2.0 * c.bm * c.bn * kpad / (kFlopsPerCuCycle * eff);
     const double bytes = 4.0 * ((double)M * K + (double)K * N + (double)M * N);
@@ -724,9 +736,10 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
         const bool dl = c->dl && direct;
         const SkPlan &sp = ch.sk;
         std::snprintf(text, sizeof text,
-                      "%s bm=%d bn=%d bk=%d waves=%dx%d vecA=%d vecB=%d grid=%lld group=%d "
-                      "load=%s streamk=%d split=%d",
-                      c->family, c->bm, c->bn, dl ? 16 : c->bk, c->wm, c->wn, (lda & 3) == 0,
+                      "%s bm=%d bn=%d bk=%d waves=%dx%d occ=%d vecA=%d vecB=%d grid=%lld "
+                      "group=%d load=%s streamk=%d split=%d",
+                      c->family, c->bm, c->bn, dl ? 16 : c->bk, c->wm, c->wn, c->occupancy,
+                      (lda & 3) == 0,
                       (ldb & 3) == 0, (long long)tiles_m * tiles_n,
                       group_rows(*c, tiles_m, tiles_n, num_cus), dl ? "direct" : "regs",
                       sp.use ? sp.args.workers : 0, sp.use ? sp.split_tiles : 0);

@@ -162,8 +162,10 @@ def test_forced_tiles():
     for i in range(n):
         p = plan(300, 300, 300, variant=sg.SGEMM_VARIANT_MFMA_TILE + i)
         assert p["kind"] == "mfma"
-        seen.add((p["bm"], p["bn"]))
+        seen.add((p["bm"], p["bn"], p["bk"], p["waves"], p["occ"]))
     assert len(seen) == n
+    from tests.test_parity import NUM_TILES  # the GPU tests' forced families cover them all
+    assert NUM_TILES == n
 
 
 def test_ladder_rungs():

@@ -47,8 +47,10 @@ def _full_check(A, B, C, alpha, beta, variant=0, exact=False, **kw):
 # AUTO, VALU, SKINNY, the five forced MFMA tiles, the same five run
 # stream-K (variant 48 + i), and the eight rungs of the pages' SIMT ladder
 # (variant 32 + r).
-STREAMK_FAMILIES = [48 + i for i in range(5)]
-FAMILIES = [0, 2, 3] + [16 + i for i in range(5)] + STREAMK_FAMILIES + [32 + r for r in range(8)]
+NUM_TILES = 6  # entries of the MFMA tile table (checked against the library in test_abi)
+STREAMK_FAMILIES = [48 + i for i in range(NUM_TILES)]
+FAMILIES = ([0, 2, 3] + [16 + i for i in range(NUM_TILES)] + STREAMK_FAMILIES
+            + [32 + r for r in range(8)])
 
 
 # ---------------------------------------------------------------- workloads
