@@ -10,9 +10,13 @@ HBM before timing starts.  The line printed also carries:
     stored counter summary matches the current kernel sources;
   * cpu_baseline: the CPU reference timed on the host cores on a bounded
     sample of the same product (the first rows of C);
-  * im2col: the six convolution-as-GEMM shapes, each timed on its own with
-    the memory-side caches flushed between launches, with TFLOPS and the
-    HBM bandwidth the algorithmic bytes imply;
+  * squares: 256^3 (alpha 1, beta 0), 1024^3 (alpha 1, beta 0, C preloaded)
+    and every point of the square sweep 256 ... 5120 step 256 (alpha 1.5,
+    beta 0.5), each timed like the headline, launches back to back;
+  * im2col: the six convolution-as-GEMM shapes, each timed back to back over
+    rotating copies of its operands (and, for comparison, one launch at a
+    time after a cache flush), with TFLOPS and the HBM bandwidth the
+    algorithmic bytes imply;
   * valu_comparison and ladder: the vector-FMA kernels on the headline
     workload, the register-tile comparison kernel and each rung of the
     pages' SIMT optimisation ladder (naive ... double-buffered);
@@ -20,7 +24,7 @@ HBM before timing starts.  The line printed also carries:
     im2col shapes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-im2col]
-                       [--no-valu] [--no-ladder]
+                       [--no-valu] [--no-ladder] [--no-squares]
 """
 from __future__ import annotations
 
@@ -117,48 +121,127 @@ def cpu_baseline(case, A, B, C, budget_s):
                       % (rows, case.M, case.M, case.alpha, case.beta, dt)}
 
 
+def bench_squares(sg, stream):
+    """The square configurations: 256^3, 1024^3 and the sweep 256 ... 5120.
+    Each size runs back to back for about 50 ms (clocks up, the launch
+    pipeline full), then a timed run of about 20 ms of launches between two
+    HIP events, as for the headline."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = []
+    for case in [workloads.SMALL, workloads.SQUARE1024] + workloads.SWEEP:
+        log("square", case.name)
+        _, _, _, dA, dB, dC = device_operands(case)
+        args = (case.M, case.N, case.K, case.alpha, dA.data_ptr(), case.K, dB.data_ptr(),
+                case.N, case.beta, dC.data_ptr(), case.N, stream.cuda_stream)
+
+        def step():
+            rc = sg.sgemm_f32(*args)
+            if rc != 0:
+                raise RuntimeError(sg.sgemm_status_string(rc))
+
+        step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        once = max(time.perf_counter() - t0, 1e-6)
+        t_end = time.perf_counter() + 0.05
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
+        steps = int(min(2000, max(10, 0.02 / once)))
+        ms = time_steps(step, steps, 0, stream)
+        tflops = case.flops / (ms * 1e-3) / 1e12
+        out.append({"shape": [case.M, case.N, case.K], "alpha": case.alpha, "beta": case.beta,
+                    "steps": steps, "us": round(ms * 1e3, 2), "tflops": round(tflops, 2),
+                    "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4),
+                    "kernel": sg.sgemm_plan(0, case.M, case.N, case.K, case.K, case.N, case.N,
+                                            case.alpha, cus)[1]})
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_im2col(sg, stream, reps):
-    """Each im2col shape: median time of `reps` launches, caches flushed between."""
+    """Each im2col shape, timed two ways.
+
+    `us` (the figure the fractions use): the steady state of back-to-back
+    launches over enough copies of the operands (at least 1.6 GB in all) that
+    every launch reads its inputs from HBM, about 0.15 s of launches between
+    two HIP events, median of three such runs.  Each launch also pays for
+    writing back what the one before it left dirty in the caches.
+
+    `us_single_flushed`: one launch between two events after a 512 MB read that
+    evicts the caches, median of `reps`.  This reads low for kernels that
+    write C with plain stores: up to the memory-side cache's size of C can
+    still be dirty there when the launch ends, and the next flush writes it
+    back outside the timed region."""
     import torch
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = []
     for case in workloads.SKINNY + workloads.MID:
         log("im2col", case.name)
         _, _, _, dA, dB, dC = device_operands(case)
-        args = (case.M, case.N, case.K, case.alpha, dA.data_ptr(), case.K, dB.data_ptr(),
-                case.N, case.beta, dC.data_ptr(), case.N, stream.cuda_stream)
-        rc = sg.sgemm_f32(*args)
+        footprint = 4 * (case.M * case.K + case.K * case.N + case.M * case.N)
+        nset = max(2, -(-1600 * 1024 * 1024 // footprint))
+        sets = [(dA, dB, dC)] + [(dA.clone(), dB.clone(), dC.clone()) for _ in range(nset - 1)]
+        calls = [(case.M, case.N, case.K, case.alpha, a.data_ptr(), case.K, b.data_ptr(),
+                  case.N, case.beta, c.data_ptr(), case.N, stream.cuda_stream) for a, b, c in sets]
+        rc = sg.sgemm_f32(*calls[0])
         assert rc == 0, sg.sgemm_status_string(rc)
         # Warm-up: the inputs were just drawn on the host, the GPU sat idle
         # meanwhile and its clocks drop; a few launches are not enough for
         # them to come back up.  Run the product back to back for ~0.1 s.
         t_end = time.perf_counter() + 0.1
+        i = 0
         while time.perf_counter() < t_end:
             for _ in range(10):
-                sg.sgemm_f32(*args)
+                sg.sgemm_f32(*calls[i % nset])
+                i += 1
             torch.cuda.synchronize()
-        times = []
-        for _ in range(reps):
-            flush.sum()  # evict the caches without leaving dirty lines behind
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for c in calls:
+            sg.sgemm_f32(*c)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        n = max(nset, int(0.15 / max(e0.elapsed_time(e1) * 1e-3 / nset, 1e-6)))
+        runs = []
+        for _ in range(3):
             e0.record(stream)
-            sg.sgemm_f32(*args)
+            for k in range(n):
+                sg.sgemm_f32(*calls[k % nset])
             e1.record(stream)
             torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        ms = float(np.median(times))
+            runs.append(e0.elapsed_time(e1) / n)
+        ms = float(np.median(runs))
+        single = []
+        for _ in range(reps):
+            flush.sum()  # evict the caches without leaving dirty lines behind
+            e0.record(stream)
+            sg.sgemm_f32(*calls[0])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            single.append(e0.elapsed_time(e1))
+        ms_single = float(np.median(single))
         tflops = case.flops / (ms * 1e-3) / 1e12
         gbps = case.alg_bytes / (ms * 1e-3) / 1e9
         roof_us = max(case.alg_bytes / (PEAK_HBM_GBPS * 1e9), case.flops / (PEAK_FP32_TFLOPS * 1e12)) * 1e6
-        _, plan = sg.sgemm_plan(0, case.M, case.N, case.K, case.K, case.N, case.N, case.alpha,
-                                torch.cuda.get_device_properties(0).multi_processor_count)
+        _, plan = sg.sgemm_plan(0, case.M, case.N, case.K, case.K, case.N, case.N, case.alpha, cus)
         out.append({"shape": [case.M, case.N, case.K], "us": round(ms * 1e3, 2),
+                    "launches": n, "operand_sets": nset,
                     "tflops": round(tflops, 2), "hbm_gbps": round(gbps, 1),
                     "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
                     "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4),
-                    "frac_roofline": round(roof_us / (ms * 1e3), 4), "kernel": plan})
-        del dA, dB, dC
+                    "frac_roofline": round(roof_us / (ms * 1e3), 4),
+                    "us_single_flushed": round(ms_single * 1e3, 2),
+                    "frac_roofline_single_flushed": round(roof_us / (ms_single * 1e3), 4),
+                    "kernel": plan})
+        del dA, dB, dC, sets, calls
         torch.cuda.empty_cache()
     return out
 
@@ -257,6 +340,7 @@ def main():
     ap.add_argument("--variant", type=int, default=0, help="force a kernel family (tuning)")
     ap.add_argument("--no-valu", action="store_true", help="skip the VALU-kernel comparison")
     ap.add_argument("--no-ladder", action="store_true", help="skip the SIMT-ladder table")
+    ap.add_argument("--no-squares", action="store_true", help="skip the square sweep")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the launch sequence for the HBM-traffic counter passes")
     args = ap.parse_args()
@@ -329,6 +413,8 @@ def main():
     if not args.no_ladder:
         result["ladder"] = bench_ladder(sg, case, call_args, stream, tflops)
         result["ladder_im2col"] = bench_ladder_im2col(sg, stream)
+    if not args.no_squares:
+        result["squares"] = bench_squares(sg, stream)
     if not args.no_im2col:
         result["im2col"] = bench_im2col(sg, stream, args.im2col_reps)
     if not args.no_cpu:
