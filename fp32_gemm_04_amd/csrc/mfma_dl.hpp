@@ -13,7 +13,8 @@
 // and B rows are 16-byte aligned; other tiles of the same launch run the
 // masked register-staged path of mfma_tile.hpp.
 //
-// LDS: three buffers of (BM + BN) / 16 chunks of 1 KB (256 floats).  The
+// LDS: NBUF buffers (a ring; three unless the tile says otherwise) of
+// (BM + BN) / 16 chunks of 1 KB (256 floats).  The
 // position of every float inside a chunk is chosen so that each MFMA
 // operand read of a wave is one contiguous run of LDS:
 //   A chunk cm (rows 16 cm .. 16 cm + 15 of the tile), 16-byte slot j holds
@@ -25,14 +26,17 @@
 // Both patterns touch every bank once, so operand reads are conflict-free.
 //
 // Pipeline of slab t (its operands already in registers):
-//   k-steps 0, 1: MFMAs, with the loads of slab t+2 spread over them, into
-//     the buffer slab t-1 used (every wave took slab t-1's operands into
-//     registers before the previous barrier, so the buffer is free).
+//   k-steps 0, 1: MFMAs, with the loads of slab t+NBUF-1 spread over them,
+//     into the buffer slab t-1 used (every wave took slab t-1's operands
+//     into registers before the previous barrier, so the buffer is free).
 //   Wait until this wave's loads of slab t+1 have landed; barrier.
 //   k-steps 2, 3: MFMAs, with slab t+1's operand reads placed one per MFMA,
 //     in the order the next slab first uses them.
-// A slab's loads are issued about one and a half slabs before its operands
-// are read.  The spacing matters: issued back to back right after the
+// A slab's loads are issued about NBUF - 1.5 slabs before its operands are
+// read.  Three buffers suit tiles of 128 and 160, whose slabs take long
+// enough to cover the load latency; a 64 x 64 slab is 16 MFMAs per wave,
+// and with one tile per CU its kernel keeps twelve buffers (96 KB) so that
+// ten slabs are in flight.  The spacing matters: issued back to back right after the
 // barrier, reads and loads stall the wave's MFMA issue (measured at 5120^3:
 // 125 TFLOPS clustered, 140 with reads and loads spread over the second
 // half, 143 with the loads moved to the first half).
@@ -66,7 +70,24 @@ __device__ __forceinline__ void wait_vm_barrier()
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-template <int BM, int BN, int WM, int WN>
+// Wait until at most min(k, KMAX) slabs of L loads each are in flight (none
+// if k <= 0), then meet the workgroup at a barrier.  vmcnt takes an
+// immediate, so each count is a branch of its own; k is the same for the
+// whole workgroup.
+template <int L, int KMAX>
+__device__ __forceinline__ void wait_slabs_barrier(int k)
+{
+    if constexpr (KMAX > 0) {
+        if (k >= KMAX)
+            wait_vm_barrier<KMAX * L>();
+        else
+            wait_slabs_barrier<L, KMAX - 1>(k);
+    } else {
+        wait_vm_barrier<0>();
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int NBUF_ = 3>
 struct MfmaDl {
     static constexpr int NW = WM * WN;
     static constexpr int FM = BM / WM / 16;        // 16x16 blocks per wave along M
@@ -75,7 +96,7 @@ struct MfmaDl {
     static constexpr int CB = BN / 16;             // B chunks per slab
     static constexpr int L = (CA + CB) / NW;       // loads per wave per slab
     static constexpr int BUF = (CA + CB) * 256;    // floats per LDS buffer
-    static constexpr int NBUF = 3;
+    static constexpr int NBUF = NBUF_;
     static constexpr int LDS = NBUF * BUF;         // floats of LDS
     // The first half of a slab (2 FM FN MFMAs) carries L loads, one every
     // STRIDE MFMAs; the second half R operand reads, one per MFMA.
@@ -84,13 +105,14 @@ struct MfmaDl {
     static_assert((CA + CB) % NW == 0, "slab chunks must split evenly over the waves");
     static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile must be 16-aligned");
     static_assert(STRIDE >= 1 && R <= 2 * FM * FN, "too few MFMAs per slab for the reads and loads");
+    static_assert(NBUF >= 3, "the ring needs a buffer being read, one landing, one free");
     static_assert(L * (NBUF - 1) <= 63, "loads in flight must fit the vmcnt field");
 };
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NBUF_>
 __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, float *lds)
 {
-    using D = MfmaDl<BM, BN, WM, WN>;
+    using D = MfmaDl<BM, BN, WM, WN, NBUF_>;
     constexpr int NW = D::NW, FM = D::FM, FN = D::FN, CA = D::CA, L = D::L, BUF = D::BUF;
     constexpr int NBUF = D::NBUF, R = D::R, S1 = D::STRIDE;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -173,9 +195,9 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
     // from the waits the compiler places for them.
     auto slab = [&](auto P, int t, int buf) {
         constexpr int p = decltype(P)::value;
-        // First half: the loads of slab t+2 into the buffer slab t-1 used
-        // (every wave passed barrier t-1 with its operands in registers).
-        const bool more = t >= 1 && t + 2 < nslab;
+        // First half: the loads of slab t+NBUF-1 into the buffer slab t-1
+        // used (every wave passed barrier t-1 with its operands in registers).
+        const bool more = t >= 1 && t + NBUF - 1 < nslab;
         const uint32_t bb = buffer_bytes(buf == 0 ? NBUF - 1 : buf - 1);
         ksteps(0, 2, afs[p], bfs[p], [&](int n) {
             if (n > 0 && n % S1 == 0 && n / S1 <= L) {
@@ -183,11 +205,9 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
             }
         });
         __builtin_amdgcn_sched_barrier(0);
-        // In flight: slab t+1's loads, then slab t+2's (if any).
-        if (t + 2 < nslab)
-            wait_vm_barrier<L>();
-        else
-            wait_vm_barrier<0>();
+        // In flight: slab t+1's loads, then those of the slabs after it up to
+        // t+NBUF-1 (as far as they exist): wait for slab t+1's.
+        wait_slabs_barrier<L, NBUF - 2>(nslab - 2 - t);
         const int nb = buf + 1 == NBUF ? 0 : buf + 1;
         ksteps(2, 4, afs[p], bfs[p], [&](int n) {
             if (n < R) {
@@ -205,13 +225,8 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
 #pragma unroll
             for (int i = 0; i < L; ++i) load(i, buffer_bytes(b));
         }
-    if (nslab > 2)
-        wait_vm_barrier<2 * L>();
-    else if (nslab > 1)
-        wait_vm_barrier<L>();
-    else
-        wait_vm_barrier<0>();
-    // (slab 0 issues no loads: slabs 1 and 2 are already in flight)
+    wait_slabs_barrier<L, NBUF - 1>(nslab - 1);
+    // (slab 0 issues no loads: slabs 1 .. NBUF-1 are already in flight)
 #pragma unroll
     for (int r = 0; r < R; ++r) read_op(r, 0, afs[0], bfs[0]);
 
@@ -248,12 +263,12 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
 
 // Interior tiles take the direct-load body, border tiles the masked
 // register-staged one; both share the LDS array.
-template <int BM, int BN, int WM, int WN, int WPE>
+template <int BM, int BN, int WM, int WN, int WPE, int NBUF = 3>
 __global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 mfma_dl_kernel(GemmArgs g)
 {
     using T = MfmaTile<BM, BN, 16, WM, WN>;
-    constexpr int DL = MfmaDl<BM, BN, WM, WN>::LDS;
+    constexpr int DL = MfmaDl<BM, BN, WM, WN, NBUF>::LDS;
     constexpr int RG = 2 * (T::LDS_A + T::LDS_B);
     __shared__ __attribute__((aligned(16))) float lds[DL > RG ? DL : RG];
 
@@ -262,25 +277,25 @@ mfma_dl_kernel(GemmArgs g)
     const int m0 = tm * BM;
     const int n0 = tn * BN;
     if (m0 + BM <= g.M && n0 + BN <= g.N)
-        mfma_dl_body<BM, BN, WM, WN>(g, m0, n0, lds);
+        mfma_dl_body<BM, BN, WM, WN, NBUF>(g, m0, n0, lds);
     else
         mfma_tile_body<BM, BN, 16, WM, WN, 2, true, true, true>(g, m0, n0, lds, lds + 2 * T::LDS_A);
 }
 
 // Stream-K form: this workgroup's range of tile segments (sk_run), each
 // through the same two bodies.
-template <int BM, int BN, int WM, int WN, int WPE>
+template <int BM, int BN, int WM, int WN, int WPE, int NBUF = 3>
 __global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 mfma_dl_sk_kernel(GemmArgs g, SkArgs s)
 {
     using T = MfmaTile<BM, BN, 16, WM, WN>;
-    constexpr int DL = MfmaDl<BM, BN, WM, WN>::LDS;
+    constexpr int DL = MfmaDl<BM, BN, WM, WN, NBUF>::LDS;
     constexpr int RG = 2 * (T::LDS_A + T::LDS_B);
     __shared__ __attribute__((aligned(16))) float lds[DL > RG ? DL : RG];
 
     sk_run<BM, BN>(g, s, [&](const GemmArgs &a, int m0, int n0) __attribute__((always_inline)) {
         if (m0 + BM <= a.M && n0 + BN <= a.N)
-            mfma_dl_body<BM, BN, WM, WN>(a, m0, n0, lds);
+            mfma_dl_body<BM, BN, WM, WN, NBUF>(a, m0, n0, lds);
         else
             mfma_tile_body<BM, BN, 16, WM, WN, 2, true, true, true>(a, m0, n0, lds,
                                                                       lds + 2 * T::LDS_A);

@@ -98,18 +98,22 @@ struct TileConfig {
     mfma_tile_kernel<BM, BN, BK, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), ST, AV, BV>
 #define SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, AV, BV) \
     mfma_tile_sk_kernel<BM, BN, BK, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), ST, AV, BV>
-#define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, ST, EFF, DL, DLEFF, SKDL, ONE) \
-    {"mfma", BM, BN, BK, WM, WN, WM * WN * 64, OCC, EFF,                         \
-     {{SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, false),             \
-       SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, true)},             \
-      {SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, false),              \
-       SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, true)}},             \
-     DL, DLEFF,                                                                  \
-     {{SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, false),          \
-       SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, false, true)},          \
-      {SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, false),           \
-       SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, OCC, ST, true, true)}},          \
+// ROCC: the occupancy the register-staged kernels are compiled for (the
+// entry's own OCC unless its direct-load kernel holds more LDS).
+#define SGEMM_MFMA_ENTRY_R(BM, BN, BK, WM, WN, OCC, ROCC, ST, EFF, DL, DLEFF, SKDL, ONE) \
+    {"mfma", BM, BN, BK, WM, WN, WM * WN * 64, OCC, EFF,                                 \
+     {{SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, ROCC, ST, false, false),                    \
+       SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, ROCC, ST, false, true)},                    \
+      {SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, ROCC, ST, true, false),                     \
+       SGEMM_MFMA_KERNEL(BM, BN, BK, WM, WN, ROCC, ST, true, true)}},                    \
+     DL, DLEFF,                                                                          \
+     {{SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, ROCC, ST, false, false),                 \
+       SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, ROCC, ST, false, true)},                 \
+      {SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, ROCC, ST, true, false),                  \
+       SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, ROCC, ST, true, true)}},                 \
      SKDL, ONE}
+#define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, ST, EFF, DL, DLEFF, SKDL, ONE) \
+    SGEMM_MFMA_ENTRY_R(BM, BN, BK, WM, WN, OCC, OCC, ST, EFF, DL, DLEFF, SKDL, ONE)
 #define SGEMM_DL_KERNEL(BM, BN, WM, WN, OCC) \
     direct_kernel(BM, BN, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC))
 #define SGEMM_DL_SK_KERNEL(BM, BN, WM, WN, OCC) \
@@ -122,10 +126,14 @@ struct TileConfig {
 // direct-load path.  The last column is the efficiency measured when each CU
 // holds a single tile (2560^3, 2048^3, 1024^3): small tiles lose most there,
 // with little work per tile to hide load latency behind.
-// The last entry is the 64 x 64 tile with a three-stage pipeline at two
-// workgroups per CU: faster than the four-per-CU entry when a CU has one
-// tile (1024^3: 27.6 against 31.1 us), slower when it has several, which
-// its lower efficiency encodes.
+// The 64 x 64 tile with a three-stage pipeline at two workgroups per CU is
+// faster than the four-per-CU entry when a CU has one tile (1024^3: 27.6
+// against 31.1 us), slower when it has several, which its lower efficiency
+// encodes.  The last entry is the 64 x 64 direct-load tile with a twelve-slab
+// ring (96 KB of LDS, one workgroup per CU): with one tile per CU it keeps
+// ten slabs of loads in flight (1024^3: 24.3 against 27.6 us; 768^3: 19.6
+// against 22.5).  Its register-staged kernels (the two-per-CU build) are
+// only run when forced: its efficiency of 0 keeps the selector off them.
 const TileConfig kMfmaTiles[] = {
     SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 3, 0.77, SGEMM_DL_KERNEL(160, 160, 2, 2, 2), 0.88,
                      SGEMM_DL_SK_KERNEL(160, 160, 2, 2, 2), 0.82),
@@ -136,6 +144,8 @@ const TileConfig kMfmaTiles[] = {
     SGEMM_MFMA_ENTRY(64, 256, 16, 1, 4, 2, 3, 0.60, SGEMM_DL_KERNEL(64, 256, 1, 4, 2), 0.90,
                      SGEMM_DL_SK_KERNEL(64, 256, 1, 4, 2), 0.0),
     SGEMM_MFMA_ENTRY(64, 64, 32, 2, 2, 2, 3, 0.55, nullptr, 0.0, nullptr, 0.495),
+    SGEMM_MFMA_ENTRY_R(64, 64, 32, 2, 2, 1, 2, 3, 0.0, SGEMM_DL_KERNEL(64, 64, 2, 2, 1), 0.60,
+                       SGEMM_DL_SK_KERNEL(64, 64, 2, 2, 1), 0.56),
 };
 
 const TileConfig kValuTile = {"valu", 128, 128, 8, 2, 2, 256, 2, 0.45,
@@ -163,6 +173,7 @@ double estimate_cycles(const TileConfig &c, int M, int N, int K, int num_cus, bo
     const bool dl = direct && c.dl != nullptr;
     const int bk = dl ? 16 : c.bk;
     double eff = dl ? c.dl_efficiency : c.efficiency;
+    if (eff <= 0.0) return HUGE_VAL;  // only run when forced
     // Partial tiles at the right or bottom edge run the masked register-staged
     // body; a CU that holds one sets the pace (measured at 2304^3: the 160 tile
     // with a 64-wide edge reaches 52 TFLOPS, the 64 tile without edges 98).
@@ -252,6 +263,10 @@ SkPlan plan_streamk(const TileConfig &c, int M, int N, int K, int num_cus, bool 
 
     double eff = dl ? c.dl_efficiency : c.efficiency;
     if ((M % c.bm != 0 || N % c.bn != 0) && c.efficiency < eff) eff = c.efficiency;
+    if (eff <= 0.0) {  // only run when forced
+        p.cycles = HUGE_VAL;
+        return p;
+    }
     const double unit_cycles = 2.0 * c.bm * c.bn * bk / (kFlopsPerCuCycle * eff);
     const double compute = (double)units / num_cus * unit_cycles * kSkUnitOverhead;
     const double bytes = 4.0 * ((double)M * K + (double)K * N + (double)M * N);
