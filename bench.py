@@ -13,6 +13,8 @@ HBM before timing starts.  The line printed also carries:
   * squares: 256^3 (alpha 1, beta 0), 1024^3 (alpha 1, beta 0, C preloaded)
     and every point of the square sweep 256 ... 5120 step 256 (alpha 1.5,
     beta 0.5), each timed like the headline, launches back to back;
+  * device_copy: a plain device-to-device copy's bandwidth, the measured
+    ceiling for mixed read and write traffic;
   * im2col: the six convolution-as-GEMM shapes, each timed back to back over
     rotating copies of its operands (and, for comparison, one launch at a
     time after a cache flush), with TFLOPS and the HBM bandwidth the
@@ -101,6 +103,44 @@ def device_operands(case):
     return A, B, C, dA, dB, dC
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def device_copy(stream):
+    """Measured device-to-device copy bandwidth (a plain stream of reads and
+    writes, the ceiling to set the skinny shapes beside): 512 MiB copies back
+    to back between two buffer pairs for about 0.1 s, bytes read + written."""
+    import torch
+    n = 512 * 1024 * 1024 // 4
+    xs = [torch.ones(n, dtype=torch.float32, device="cuda") for _ in range(2)]
+    ys = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(2)]
+    for i in range(20):
+        ys[i % 2].copy_(xs[i % 2])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 100
+    e0.record(stream)
+    for i in range(reps):
+        ys[i % 2].copy_(xs[i % 2])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del xs, ys
+    torch.cuda.empty_cache()
+    return {"bytes_each_way": n * 4, "us": round(sec * 1e6, 1),
+            "gbps": round(2 * n * 4 / sec / 1e9, 1),
+            "frac_hbm_peak": round(2 * n * 4 / sec / 1e9 / PEAK_HBM_GBPS, 4)}
+
+
 def cpu_baseline(case, A, B, C, budget_s):
     """Time the CPU reference on the first R rows of the product."""
     import oracle
@@ -117,6 +157,7 @@ def cpu_baseline(case, A, B, C, budget_s):
         rows = min(case.M, max(rows * 2, int(rows * budget_s * 0.8 / max(dt, 1e-3))))
     flops = 2.0 * rows * case.N * case.K
     return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "first %d of %d rows of C for M=N=K=%d, alpha=%g, beta=%g (%.1f s)"
                       % (rows, case.M, case.M, case.alpha, case.beta, dt)}
 
@@ -416,6 +457,7 @@ def main():
     if not args.no_squares:
         result["squares"] = bench_squares(sg, stream)
     if not args.no_im2col:
+        result["device_copy"] = device_copy(stream)
         result["im2col"] = bench_im2col(sg, stream, args.im2col_reps)
     if not args.no_cpu:
         log("cpu baseline")

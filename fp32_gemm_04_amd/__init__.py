@@ -28,8 +28,8 @@ LADDER_RUNG_NAMES = ("naive", "coalesced", "lds", "tile1d", "tile2d", "regcache"
 SGEMM_ERR_BAD_VARIANT = -100
 SGEMM_ERR_VARIANT_SHAPE = -101
 
-EXPORTS = ("sgemm_f32", "sgemm_f32_variant", "sgemm_plan", "sgemm_num_mfma_tiles",
-           "sgemm_status_string")
+EXPORTS = ("sgemm_f32", "sgemm_f32_variant", "sgemm_plan", "sgemm_tune", "sgemm_tune_reset",
+           "sgemm_num_mfma_tiles", "sgemm_status_string")
 
 if not os.path.exists(LIBRARY):
     raise ImportError("libsgemm.so is not built; run __graft_entry__.build() "
@@ -55,6 +55,11 @@ _lib.sgemm_f32_variant.argtypes = [ctypes.c_int] + _gemm_args
 _lib.sgemm_plan.restype = ctypes.c_int
 _lib.sgemm_plan.argtypes = [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_int,
                                                  ctypes.c_char_p, ctypes.c_int]
+_lib.sgemm_tune.restype = ctypes.c_int
+_lib.sgemm_tune.argtypes = _gemm_args + [ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                         ctypes.POINTER(ctypes.c_float)]
+_lib.sgemm_tune_reset.restype = None
+_lib.sgemm_tune_reset.argtypes = []
 _lib.sgemm_num_mfma_tiles.restype = ctypes.c_int
 _lib.sgemm_num_mfma_tiles.argtypes = []
 _lib.sgemm_status_string.restype = ctypes.c_char_p
@@ -84,6 +89,20 @@ def sgemm_plan(variant, M, N, K, lda, ldb, ldc, alpha, num_cus):
     return rc, buf.value.decode()
 
 
+def sgemm_tune(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0, reps=5):
+    """C ABI ``sgemm_tune``.  Returns (status, chosen variant, microseconds per launch)."""
+    chosen = ctypes.c_int(0)
+    us = ctypes.c_float(0.0)
+    rc = _lib.sgemm_tune(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, reps,
+                         ctypes.byref(chosen), ctypes.byref(us))
+    return rc, chosen.value, us.value
+
+
+def sgemm_tune_reset() -> None:
+    """C ABI ``sgemm_tune_reset``."""
+    _lib.sgemm_tune_reset()
+
+
 def sgemm_num_mfma_tiles() -> int:
     """C ABI ``sgemm_num_mfma_tiles``."""
     return _lib.sgemm_num_mfma_tiles()
@@ -91,6 +110,23 @@ def sgemm_num_mfma_tiles() -> int:
 
 def sgemm_status_string(status: int) -> str:
     return _lib.sgemm_status_string(status).decode()
+
+
+def tune(A, B, C, alpha: float = 1.0, beta: float = 0.0, reps: int = 5, stream=None):
+    """Tune the kernel choice for this problem (``sgemm_tune``) and compute
+    C <- alpha*A@B + beta*C in place with the winner.  Returns (variant,
+    microseconds per launch); raises SgemmError on a non-zero status."""
+    import torch
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape), tuple(C.shape)))
+    s = stream if stream is not None else torch.cuda.current_stream(C.device)
+    rc, chosen, us = sgemm_tune(M, N, K, alpha, A.data_ptr(), _ld(A, "A"), B.data_ptr(),
+                                _ld(B, "B"), beta, C.data_ptr(), _ld(C, "C"), s.cuda_stream, reps)
+    if rc != 0:
+        raise SgemmError(rc)
+    return chosen, us
 
 
 def _ld(t, name):

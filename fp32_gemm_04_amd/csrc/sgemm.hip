@@ -211,12 +211,13 @@ struct SkPlan {
     double cycles;      // estimate, CU cycles
 };
 
-// Measured on MI355X (mid im2col shapes, 1024^3 to 4608^3): the stream-K
-// kernel's per-unit time is about 6% above one tile per workgroup (a pipeline
-// fill per segment), and the fixup pass moves its bytes at about 5.3 TB/s,
-// plus a launch.  Stream-K is taken only when its estimate is 5% below the
-// best one-tile-per-workgroup estimate.
-constexpr double kSkUnitOverhead = 1.06;
+// Measured on MI355X (mid im2col shapes, 1024^3 to 4608^3): each worker
+// pays about 4.5 units' time on top of its units (the pipeline fill and the
+// partial-tile store of its segments: 6% at (256,43264,1152), 95 units per
+// worker; 1% at 3840^3, 422), and the fixup pass moves its bytes at about
+// 5.3 TB/s, plus a launch.  Stream-K is taken only when its estimate is 5%
+// below the best one-tile-per-workgroup estimate.
+constexpr double kSkWorkerOverheadUnits = 4.5;
 constexpr double kSkFixupBytesPerCycle = 5.3e12 / 2.4e9;
 constexpr double kSkFixupLaunchCycles = 7200.0;
 constexpr double kSkMargin = 0.95;
@@ -268,7 +269,9 @@ SkPlan plan_streamk(const TileConfig &c, int M, int N, int K, int num_cus, bool 
         return p;
     }
     const double unit_cycles = 2.0 * c.bm * c.bn * bk / (kFlopsPerCuCycle * eff);
-    const double compute = (double)units / num_cus * unit_cycles * kSkUnitOverhead;
+    const double per_worker = (double)units / workers;
+    const double compute =
+        (double)units / num_cus * unit_cycles * (1.0 + kSkWorkerOverheadUnits / per_worker);
     const double bytes = 4.0 * ((double)M * K + (double)K * N + (double)M * N);
     const double memory = bytes / (kHbmBytesPerCuCycle * num_cus);
     // The fixup reads every partial and reads and writes C of the split tiles.
@@ -594,13 +597,70 @@ int launch_skinny(const GemmArgs &g, const SkinnyPlan &p, hipStream_t stream)
 
 
 
+// Tuned choices (sgemm_tune): the variant measured fastest for a problem
+// key.  Looked up by AUTO calls while the table is not empty.
+struct TuneKey {
+    int device, M, N, K, lda, ldb, ldc, vec;  // vec: bit 0 A, bit 1 B, bit 2 C 128-bit paths
+    bool operator==(const TuneKey &o) const
+    {
+        return device == o.device && M == o.M && N == o.N && K == o.K && lda == o.lda &&
+               ldb == o.ldb && ldc == o.ldc && vec == o.vec;
+    }
+};
+struct TuneEntry {
+    TuneKey key;
+    int variant;
+};
+std::mutex g_tune_mutex;
+std::vector<TuneEntry> g_tuned;
+std::atomic<int> g_tuned_count{0};
+
+TuneKey tune_key(int device, int M, int N, int K, int lda, int ldb, int ldc, bool avec,
+                 bool bvec, bool cvec)
+{
+    return {device, M, N, K, lda, ldb, ldc, (avec ? 1 : 0) | (bvec ? 2 : 0) | (cvec ? 4 : 0)};
+}
+
+// The tuned variant for key, or SGEMM_VARIANT_AUTO.
+int tuned_variant(const TuneKey &key)
+{
+    if (g_tuned_count.load(std::memory_order_acquire) == 0) return SGEMM_VARIANT_AUTO;
+    std::lock_guard<std::mutex> lock(g_tune_mutex);
+    for (const TuneEntry &e : g_tuned)
+        if (e.key == key) return e.variant;
+    return SGEMM_VARIANT_AUTO;
+}
+
+void record_tuned(const TuneKey &key, int variant)
+{
+    std::lock_guard<std::mutex> lock(g_tune_mutex);
+    for (TuneEntry &e : g_tuned)
+        if (e.key == key) {
+            e.variant = variant;
+            return;
+        }
+    g_tuned.push_back({key, variant});
+    g_tuned_count.store((int)g_tuned.size(), std::memory_order_release);
+}
+
+// use_tuned: an AUTO call takes the tuned variant of its key if there is one.
 int launch(int variant, int M, int N, int K, float alpha, const float *A, int lda,
-           const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream)
+           const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream,
+           bool use_tuned = true)
 {
     if (!valid_variant(variant)) return SGEMM_ERR_BAD_VARIANT;
     const int bad = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
     if (bad != 0) return bad;
     if (M == 0 || N == 0) return 0;
+    bool from_tuned = false;
+    if (use_tuned && variant == SGEMM_VARIANT_AUTO &&
+        g_tuned_count.load(std::memory_order_acquire) > 0 && K > 0 && alpha != 0.0f) {
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess)
+            variant = tuned_variant(tune_key(dev, M, N, K, lda, ldb, ldc, is_vec_ok(A, lda),
+                                             is_vec_ok(B, ldb), is_vec_ok(C, ldc)));
+        from_tuned = variant != SGEMM_VARIANT_AUTO;
+    }
 
     if (K == 0 || alpha == 0.0f) {
         const int64_t total = (int64_t)M * N;
@@ -659,7 +719,9 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
     if (blocks > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
     const int threads = c->threads;
 
-    const bool force_sk = variant >= SGEMM_VARIANT_STREAMK_TILE;
+    // A forced stream-K variant reports a workspace failure; the selector's
+    // choice (or a tuned one) falls back to one tile per workgroup.
+    const bool force_sk = variant >= SGEMM_VARIANT_STREAMK_TILE && !from_tuned;
     const SkPlan &sp = ch.sk;
     if (sp.use) {
         float *ws = nullptr;
@@ -685,6 +747,94 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
     const KernelFn fn = c->dl && direct ? c->dl : c->fn[avec][bvec];
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), 0, stream, g);
     return (int)hipGetLastError();
+}
+
+// Mean time per launch (us) of `reps` launches of variant, after one
+// untimed launch; the launches write C (a scratch copy).  A variant that
+// cannot run the problem returns its status and no time.
+int time_variant(int variant, int M, int N, int K, float alpha, const float *A, int lda,
+                 const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream,
+                 int reps, hipEvent_t e0, hipEvent_t e1, float *us)
+{
+    int rc = launch(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, false);
+    if (rc != 0) return rc;
+    hipError_t e = hipEventRecord(e0, stream);
+    for (int r = 0; r < reps && e == hipSuccess && rc == 0; ++r)
+        rc = launch(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, false);
+    if (rc != 0) return rc;
+    if (e == hipSuccess) e = hipEventRecord(e1, stream);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    if (e != hipSuccess) return (int)e;
+    *us = ms * 1000.f / (float)reps;
+    return 0;
+}
+
+int tune(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+         float beta, float *C, int ldc, hipStream_t stream, int reps, int *chosen, float *us)
+{
+    const int bad = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc, true);
+    if (bad != 0) return bad;
+    if (reps < 1) return -13;
+    if (chosen) *chosen = SGEMM_VARIANT_AUTO;
+    if (us) *us = 0.f;
+    if (M == 0 || N == 0 || K == 0 || alpha == 0.0f)  // nothing to choose
+        return launch(SGEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    // Scratch C with the same offset from a 16-byte boundary as C, so each
+    // candidate takes the load and store paths it takes on C.
+    const size_t c_floats = (size_t)(M - 1) * ldc + N;
+    const size_t shift = ((uintptr_t)C & 15u);
+    char *raw = nullptr;
+    e = hipMalloc((void **)&raw, c_floats * sizeof(float) + 16);
+    if (e != hipSuccess) return (int)e;
+    float *scratch = reinterpret_cast<float *>(raw + shift);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    e = hipMemsetAsync(raw, 0, c_floats * sizeof(float) + 16, stream);
+    if (e == hipSuccess) e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+
+    int best = SGEMM_VARIANT_AUTO, first_error = 0;
+    float best_us = 0.f;
+    bool have = false;
+    std::vector<int> candidates = {SGEMM_VARIANT_AUTO};
+    if (skinny_fits(M, K)) candidates.push_back(SGEMM_VARIANT_SKINNY);
+    for (int i = 0; i < kNumMfmaTiles; ++i) candidates.push_back(SGEMM_VARIANT_MFMA_TILE + i);
+    for (int i = 0; i < kNumMfmaTiles; ++i) candidates.push_back(SGEMM_VARIANT_STREAMK_TILE + i);
+    for (size_t i = 0; i < candidates.size() && e == hipSuccess; ++i) {
+        float t = 0.f;
+        const int rc = time_variant(candidates[i], M, N, K, alpha, A, lda, B, ldb, beta, scratch,
+                                    ldc, stream, reps, e0, e1, &t);
+        if (rc > 0) (void)hipGetLastError();  // a launch the device refused
+        if (rc != 0) {
+            if (first_error == 0) first_error = rc;
+            continue;
+        }
+        if (!have || t < best_us) {
+            best = candidates[i];
+            best_us = t;
+            have = true;
+        }
+    }
+    const hipError_t se = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = se;
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    const hipError_t fe = hipFree(raw);
+    if (e == hipSuccess) e = fe;
+    if (e != hipSuccess) return (int)e;
+    if (!have) return first_error;
+
+    record_tuned(tune_key(dev, M, N, K, lda, ldb, ldc, is_vec_ok(A, lda), is_vec_ok(B, ldb),
+                          is_vec_ok(C, ldc)),
+                 best);
+    if (chosen) *chosen = best;
+    if (us) *us = best_us;
+    return launch(best, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, false);
 }
 
 }  // namespace
@@ -713,6 +863,18 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
     const int bad = check_args(M, N, K, alpha, nullptr, lda, nullptr, ldb, nullptr, ldc, false);
     if (bad != 0) return bad;
     if (num_cus < 1 || (buf == nullptr && buflen > 0) || buflen < 0) return -12;
+    // A tuned choice for this problem on the current device (bases assumed
+    // 16-byte aligned); the table is empty unless sgemm_tune ran, and only
+    // then is the HIP runtime asked for the device.
+    int tuned = SGEMM_VARIANT_AUTO;
+    if (variant == SGEMM_VARIANT_AUTO && g_tuned_count.load(std::memory_order_acquire) > 0 &&
+        M > 0 && N > 0 && K > 0 && alpha != 0.0f) {
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess)
+            tuned = tuned_variant(tune_key(dev, M, N, K, lda, ldb, ldc, (lda & 3) == 0,
+                                           (ldb & 3) == 0, (ldc & 3) == 0));
+        variant = tuned;
+    }
     char text[160];
     if (M == 0 || N == 0) {
         std::snprintf(text, sizeof text, "none");
@@ -759,11 +921,29 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
                       group_rows(*c, tiles_m, tiles_n, num_cus), dl ? "direct" : "regs",
                       sp.use ? sp.args.workers : 0, sp.use ? sp.split_tiles : 0);
     }
+    if (tuned != SGEMM_VARIANT_AUTO) {
+        const size_t n = std::strlen(text);
+        std::snprintf(text + n, sizeof text - n, " tuned=%d", tuned);
+    }
     if (buflen > 0) {
         std::strncpy(buf, text, (size_t)buflen - 1);
         buf[buflen - 1] = '\0';
     }
     return 0;
+}
+
+extern "C" int sgemm_tune(int M, int N, int K, float alpha, const float *A, int lda,
+                          const float *B, int ldb, float beta, float *C, int ldc,
+                          hipStream_t stream, int reps, int *chosen, float *us)
+{
+    return sgemm::tune(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, reps, chosen, us);
+}
+
+extern "C" void sgemm_tune_reset(void)
+{
+    std::lock_guard<std::mutex> lock(sgemm::g_tune_mutex);
+    sgemm::g_tuned.clear();
+    sgemm::g_tuned_count.store(0, std::memory_order_release);
 }
 
 extern "C" int sgemm_num_mfma_tiles(void) { return sgemm::kNumMfmaTiles; }
@@ -782,6 +962,7 @@ extern "C" const char *sgemm_status_string(int status)
     case -10: return "invalid C (NULL or not 4-byte aligned)";
     case -11: return "invalid ldc (< max(1, N))";
     case -12: return "invalid plan arguments (num_cus < 1 or no buffer)";
+    case -13: return "invalid reps (< 1)";
     case SGEMM_ERR_BAD_VARIANT: return "unknown kernel variant";
     case SGEMM_ERR_VARIANT_SHAPE: return "the forced kernel variant cannot run this shape";
     default: break;

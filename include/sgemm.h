@@ -118,7 +118,8 @@ enum sgemm_variant {
  * data whose partial sums stay below 2^24.
  *
  * Thread safety: re-entrant; the shared state is a per-device cache of the
- * compute-unit count, filled once, and the workspace table, under a mutex.
+ * compute-unit count, filled once, the workspace table, under a mutex, and
+ * the table of tuned choices (sgemm_tune), under another.
  */
 int sgemm_f32(int M, int N, int K, float alpha, const float *A, int lda,
               const float *B, int ldb, float beta, float *C, int ldc,
@@ -153,6 +154,59 @@ int sgemm_f32_variant(int variant, int M, int N, int K, float alpha,
  */
 int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, int ldc,
                float alpha, int num_cus, char *buf, int buflen);
+
+/*
+ * sgemm_tune -- measure which kernel runs this problem fastest on the
+ * caller's operands, make it the one sgemm_f32 launches from then on for
+ * problems with the same key, and compute C <- alpha * A * B + beta * C
+ * with it.  This automates, by measurement, the block-size trade-off the
+ * NVIDIA_SGEMM_PRACTICE README reasons through by hand (kernel 3 section:
+ * larger blocks cut global traffic but leave compute units idle and need
+ * more shared memory) and the tile-parameter choice matmul_opt.cu's design
+ * notes justify (item 6).
+ *
+ *   M ... stream   as sgemm_f32; on return C holds exactly what sgemm_f32
+ *                  computes with the chosen kernel.
+ *   reps           timed launches per candidate (>= 1), after one untimed.
+ *   chosen         if not NULL, receives the chosen variant (an
+ *                  enum sgemm_variant value; SGEMM_VARIANT_AUTO when the
+ *                  selector's own choice was fastest).
+ *   us             if not NULL, receives its mean time per launch, in
+ *                  microseconds.
+ *
+ * Candidates: the selector's choice, the skinny kernel when it can run the
+ * shape, and every entry of the MFMA tile table run one tile per workgroup
+ * and run stream-K.  The timed launches write into a temporary buffer the
+ * size of C's window, at the same offset from a 16-byte boundary as C,
+ * allocated with hipMalloc and freed before returning; candidates see the
+ * same A and B.  The call synchronises `stream` and waits for the device;
+ * do not call it under graph capture.
+ *
+ * Key: device, M, N, K, lda, ldb, ldc, and whether each of A, B and C takes
+ * the 128-bit paths (16-byte aligned base, leading dimension divisible by
+ * 4).  sgemm_f32 and SGEMM_VARIANT_AUTO look the key up while any choice is
+ * recorded; sgemm_plan(SGEMM_VARIANT_AUTO, ...) describes the tuned kernel
+ * and appends " tuned=<variant>".  Forced variants are never redirected.
+ * A tuned stream-K choice whose workspace cannot be allocated falls back
+ * to one tile per workgroup, as the selector's choice does.
+ *
+ * Quick-return problems (M, N or K zero, or alpha zero) are computed as by
+ * sgemm_f32 and record nothing.  Returns the argument checks of sgemm_f32,
+ * then -13 if reps < 1, all before any HIP call; a positive hipError_t if
+ * an allocation, event or synchronisation fails; otherwise the status of
+ * the final launch.  Candidates that cannot run the problem are skipped;
+ * if none can, the first one's status is returned.
+ *
+ * Thread safety: the table of choices is under a mutex.  Tuning one key
+ * from two threads at once records one of the two results.
+ */
+int sgemm_tune(int M, int N, int K, float alpha, const float *A, int lda,
+               const float *B, int ldb, float beta, float *C, int ldc,
+               hipStream_t stream, int reps, int *chosen, float *us);
+
+/* Forget every tuned choice: sgemm_f32 returns to the shape-driven
+ * selector for all problems.  Thread-safe; no HIP call. */
+void sgemm_tune_reset(void);
 
 /* Number of entries in the MFMA tile table (see SGEMM_VARIANT_MFMA_TILE). */
 int sgemm_num_mfma_tiles(void);

@@ -200,3 +200,32 @@ def test_streamk_plans():
             assert int(p["streamk"]) <= units
             assert int(p["split"]) < int(p["streamk"])
     assert plan(5120, 5120, 5120)["streamk"] == "0"
+
+
+def _tune(**kw):
+    names = ["M", "N", "K", "alpha", "A", "lda", "B", "ldb", "beta", "C", "ldc"]
+    args = dict(M=8, N=8, K=8, alpha=1.0, A=4096, lda=8, B=8192, ldb=8, beta=0.0, C=12288, ldc=8)
+    reps = kw.pop("reps", 3)
+    args.update(kw)
+    return sg.sgemm_tune(*[args[n] for n in names], 0, reps)
+
+
+def test_tune_checks_arguments_first():
+    # Fake pointers: every one of these is rejected before any HIP call.
+    assert _tune(M=-1)[0] == -1
+    assert _tune(lda=4)[0] == -6
+    assert _tune(C=12290)[0] == -10
+    assert _tune(reps=0) == (-13, 0, 0.0)
+    assert sg.sgemm_status_string(-13).startswith("invalid reps")
+
+
+def test_tune_quick_return_makes_no_hip_call():
+    assert _tune(M=0) == (0, sg.SGEMM_VARIANT_AUTO, 0.0)
+
+
+def test_tune_reset_and_untuned_plans():
+    sg.sgemm_tune_reset()
+    for shape in [(5120, 5120, 5120), (64, 1605632, 147), (384, 14161, 1152)]:
+        M, N, K = shape
+        rc, text = sg.sgemm_plan(0, M, N, K, K, N, N, 1.0, 256)
+        assert rc == 0 and "tuned=" not in text
