@@ -10,6 +10,8 @@ KernelFn direct_kernel(int bm, int bn, int wm, int wn, int wpe)
 {
     if (bm == 64 && bn == 64 && wm == 2 && wn == 2 && wpe == 1)
         return mfma_dl_kernel<64, 64, 2, 2, 1, 12>;
+    if (bm == 128 && bn == 128 && wm == 2 && wn == 4 && wpe == 2)
+        return mfma_dl_kernel<128, 128, 2, 4, 2, 3>;
     if (wpe != 2) return nullptr;
     if (bm == 160 && bn == 160 && wm == 2 && wn == 2) return mfma_dl_kernel<160, 160, 2, 2, 2>;
     if (bm == 128 && bn == 128 && wm == 2 && wn == 2) return mfma_dl_kernel<128, 128, 2, 2, 2>;
@@ -21,6 +23,8 @@ SkKernelFn direct_sk_kernel(int bm, int bn, int wm, int wn, int wpe)
 {
     if (bm == 64 && bn == 64 && wm == 2 && wn == 2 && wpe == 1)
         return mfma_dl_sk_kernel<64, 64, 2, 2, 1, 12>;
+    if (bm == 128 && bn == 128 && wm == 2 && wn == 4 && wpe == 2)
+        return mfma_dl_sk_kernel<128, 128, 2, 4, 2, 3>;
     if (wpe != 2) return nullptr;
     if (bm == 160 && bn == 160 && wm == 2 && wn == 2) return mfma_dl_sk_kernel<160, 160, 2, 2, 2>;
     if (bm == 128 && bn == 128 && wm == 2 && wn == 2) return mfma_dl_sk_kernel<128, 128, 2, 2, 2>;

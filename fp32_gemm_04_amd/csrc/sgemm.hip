@@ -134,6 +134,12 @@ struct TileConfig {
 // ten slabs of loads in flight (1024^3: 24.3 against 27.6 us; 768^3: 19.6
 // against 22.5).  Its register-staged kernels (the two-per-CU build) are
 // only run when forced: its efficiency of 0 keeps the selector off them.
+// The 128 x 128 direct-load tile with eight waves (two per SIMD, 64 x 32
+// each) at one workgroup per CU serves a CU that holds a single tile or a
+// stream-K share (2048^3: 133.5 against 138.7 us for the four-wave tile;
+// stream-K at 1280^3: 49.4 against 52.1); with several tiles per CU it is
+// slower (2304^3: 293 against 202 us), since no second workgroup overlaps a
+// tile's fill and epilogue.  Its register-staged kernels are forced-only.
 const TileConfig kMfmaTiles[] = {
     SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 3, 0.77, SGEMM_DL_KERNEL(160, 160, 2, 2, 2), 0.88,
                      SGEMM_DL_SK_KERNEL(160, 160, 2, 2, 2), 0.82),
@@ -146,6 +152,8 @@ const TileConfig kMfmaTiles[] = {
     SGEMM_MFMA_ENTRY(64, 64, 32, 2, 2, 2, 3, 0.55, nullptr, 0.0, nullptr, 0.495),
     SGEMM_MFMA_ENTRY_R(64, 64, 32, 2, 2, 1, 2, 3, 0.0, SGEMM_DL_KERNEL(64, 64, 2, 2, 1), 0.60,
                        SGEMM_DL_SK_KERNEL(64, 64, 2, 2, 1), 0.56),
+    SGEMM_MFMA_ENTRY_R(128, 128, 16, 2, 4, 1, 1, 3, 0.0, SGEMM_DL_KERNEL(128, 128, 2, 4, 1), 0.80,
+                       SGEMM_DL_SK_KERNEL(128, 128, 2, 4, 1), 0.82),
 };
 
 const TileConfig kValuTile = {"valu", 128, 128, 8, 2, 2, 256, 2, 0.45,

@@ -47,7 +47,7 @@ def _full_check(A, B, C, alpha, beta, variant=0, exact=False, **kw):
 # AUTO, VALU, SKINNY, the five forced MFMA tiles, the same five run
 # stream-K (variant 48 + i), and the eight rungs of the pages' SIMT ladder
 # (variant 32 + r).
-NUM_TILES = 7  # entries of the MFMA tile table (checked against the library in test_abi)
+NUM_TILES = 8  # entries of the MFMA tile table (checked against the library in test_abi)
 STREAMK_FAMILIES = [48 + i for i in range(NUM_TILES)]
 FAMILIES = ([0, 2, 3] + [16 + i for i in range(NUM_TILES)] + STREAMK_FAMILIES
             + [32 + r for r in range(8)])
@@ -190,7 +190,7 @@ def test_padded_leading_dimensions(variant):
 # still gives aligned B rows.
 DIRECT_SHAPES = [(160, 160, 16), (320, 320, 32), (321, 319, 48), (333, 517, 64),
                  (256, 512, 80), (480, 160, 1024)]
-DIRECT_FAMILIES = [16, 17, 20, 22, 48, 49, 52, 54]
+DIRECT_FAMILIES = [16, 17, 20, 22, 23, 48, 49, 52, 54, 55]
 
 
 def _plan_load(variant, M, N, K, lda, ldb, ldc):
