@@ -68,12 +68,19 @@ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
 // kernel (the fixup) then adds a split tile's partials in worker order and
 // applies alpha and beta.  The result does not depend on timing, and no
 // workgroup waits for another.
+// Stream-K with whole rounds first: the tiles that fill whole rounds of the
+// resident workgroups (dp_tiles, a multiple of workers) run one tile per
+// workgroup, round-robin; only the tiles of the last, part-full round are
+// cut into (tile, k-iteration) units and shared out, so only they leave
+// partial sums for the fixup.
 struct SkArgs {
-    float *ws;       // 2 * workers slots of BM * BN floats
-    int64_t units;   // tiles * iters
+    float *ws;       // 2 * sk_workers slots of BM * BN floats
+    int64_t units;   // (tiles - dp_tiles) * iters: the shared units
     int iters;       // k-iterations per tile
     int bk;          // k per iteration
-    int workers;     // resident workgroups (<= units)
+    int workers;     // resident workgroups (the grid)
+    int dp_tiles;    // tiles run whole: tile r * workers + w for each round r
+    int sk_workers;  // workers sharing the units (<= workers, <= units; 0 if none)
 };
 
 __host__ __device__ inline int64_t sk_begin(int64_t w, int64_t units, int workers)
@@ -109,19 +116,29 @@ __host__ __device__ inline void sk_tile(int t, int tiles_m, int tiles_n, int gro
     tn = in_group / rows;
 }
 
-// Runs this workgroup's stream-K range: body(args, m0, n0) once per tile
-// segment, with args narrowed to the segment's k-range and, for a partial
-// tile, pointed at the workspace slot (row pitch BN, alpha 1, beta 0).
+// Runs this workgroup's share: its whole tiles, then its stream-K range,
+// body(args, m0, n0) once per tile segment, with args narrowed to the
+// segment's k-range and, for a partial tile, pointed at the workspace slot
+// (row pitch BN, alpha 1, beta 0).
 template <int BM, int BN, typename Body>
 __device__ __forceinline__ void sk_run(const GemmArgs &g, const SkArgs &s, Body body)
 {
     const int w = sk_logical_worker(blockIdx.x, s.workers);
-    int64_t u = sk_begin(w, s.units, s.workers);
-    const int64_t u1 = sk_begin(w + 1, s.units, s.workers);
+    // Whole tiles: in round r the workgroups take tiles r W .. r W + W - 1,
+    // so those one XCD runs at once are adjacent.
+    for (int t = w; t < s.dp_tiles; t += s.workers) {
+        int tm, tn;
+        sk_tile(t, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+        body(g, tm * BM, tn * BN);
+        __syncthreads();  // the next tile reuses the LDS buffers
+    }
+    if (w >= s.sk_workers) return;
+    int64_t u = sk_begin(w, s.units, s.sk_workers);
+    const int64_t u1 = sk_begin(w + 1, s.units, s.sk_workers);
     bool first = true;
     while (u < u1) {
-        const int t = (int)(u / s.iters);
-        const int it0 = (int)(u - (int64_t)t * s.iters);
+        const int t = s.dp_tiles + (int)(u / s.iters);
+        const int it0 = (int)(u - (int64_t)(t - s.dp_tiles) * s.iters);
         const int64_t left = u1 - u;
         const int it1 = left < (int64_t)(s.iters - it0) ? it0 + (int)left : s.iters;
         int tm, tn;

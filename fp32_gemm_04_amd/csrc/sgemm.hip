@@ -27,9 +27,9 @@ namespace sgemm {
 __device__ float g_stream_zero16[4] = {0.f, 0.f, 0.f, 0.f};
 
 // Stream-K fixup.  Workgroup (x, y) handles elements [1024 y, 1024 (y+1))
-// of output tile x, four adjacent ones per thread (BN is a multiple of 4, so
-// they share a row).  A tile whose units all fall to one worker was written
-// in full and is skipped.  Otherwise its partial sums are added in worker
+// of output tile dp_tiles + x (the shared tiles only), four adjacent ones
+// per thread (BN is a multiple of 4, so they share a row).  A tile whose
+// units all fall to one worker was written in full and is skipped.  Otherwise its partial sums are added in worker
 // order, from the slot each worker used (2 w if the tile was its first
 // segment, 2 w + 1 if its last), and C is written as alpha * sum + beta * C
 // (C not read when beta == 0).  The slot list (one 64-bit division per
@@ -40,16 +40,16 @@ constexpr int kSkFixupElems = 1024;  // elements per fixup workgroup
 __global__ void __launch_bounds__(256) sk_fixup_kernel(GemmArgs g, SkArgs s, int bm, int bn)
 {
     __shared__ int slot_of[kSkMaxWorkers];
-    const int t = blockIdx.x;
+    const int t = s.dp_tiles + blockIdx.x;
     const int e = (blockIdx.y * 256 + threadIdx.x) * 4;
-    const int64_t ua = (int64_t)t * s.iters;
-    const int wa = sk_worker_of(ua, s.units, s.workers);
-    const int wb = sk_worker_of(ua + s.iters - 1, s.units, s.workers);
+    const int64_t ua = (int64_t)blockIdx.x * s.iters;
+    const int wa = sk_worker_of(ua, s.units, s.sk_workers);
+    const int wb = sk_worker_of(ua + s.iters - 1, s.units, s.sk_workers);
     if (wa == wb) return;
     const int nw = wb - wa + 1;
     for (int i = threadIdx.x; i < nw; i += blockDim.x) {
         const int w = wa + i;
-        const int64_t b = sk_begin(w, s.units, s.workers);
+        const int64_t b = sk_begin(w, s.units, s.sk_workers);
         slot_of[i] = 2 * w + (b >= ua ? 0 : 1);
     }
     __syncthreads();
@@ -241,18 +241,22 @@ SkPlan plan_streamk(const TileConfig &c, int M, int N, int K, int num_cus, bool 
     const int bk = dl ? 16 : c.bk;
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
     const int iters = (int)ceil_div(K, bk);
-    const int64_t units = tiles * iters;
-    if (tiles > 0x7fffffff || units <= 0) return p;
+    const int64_t all_units = tiles * iters;
+    if (tiles > 0x7fffffff || all_units <= 0) return p;
     const int64_t slots = (int64_t)num_cus * c.occupancy;
     const int64_t cap = slots < kSkMaxWorkers ? slots : kSkMaxWorkers;
-    const int workers = (int)(units < cap ? units : cap);
-    // Partial segments: a worker's first segment unless it starts a tile and
-    // covers all of it; its last (if another) unless it ends a tile.  Split
-    // tiles: tiles holding a worker boundary.
+    const int workers = (int)(all_units < cap ? all_units : cap);
+    // Whole rounds run one tile per workgroup; the rest is shared out.
+    const int64_t dp_tiles = tiles / workers * workers;
+    const int64_t units = (tiles - dp_tiles) * iters;
+    const int sk_workers = (int)(units < workers ? units : workers);
+    // Partial segments: a worker's first shared segment unless it starts a
+    // tile and covers all of it; its last (if another) unless it ends a tile.
+    // Split tiles: tiles holding a worker boundary.
     int partials = 0, split = 0;
     int64_t last_split = -1;
-    for (int w = 0; w < workers; ++w) {
-        const int64_t b = sk_begin(w, units, workers), e = sk_begin(w + 1, units, workers);
+    for (int w = 0; w < sk_workers; ++w) {
+        const int64_t b = sk_begin(w, units, sk_workers), e = sk_begin(w + 1, units, sk_workers);
         const int64_t first_end = (b / iters + 1) * iters;
         if (b % iters != 0 || e < first_end) ++partials;
         if (e > first_end && e % iters != 0) ++partials;
@@ -266,9 +270,11 @@ SkPlan plan_streamk(const TileConfig &c, int M, int N, int K, int num_cus, bool 
     p.args.iters = iters;
     p.args.bk = bk;
     p.args.workers = workers;
+    p.args.dp_tiles = (int)dp_tiles;
+    p.args.sk_workers = sk_workers;
     p.split_tiles = split;
     p.partials = partials;
-    p.ws_bytes = (size_t)2 * workers * c.bm * c.bn * sizeof(float);
+    p.ws_bytes = (size_t)2 * sk_workers * c.bm * c.bn * sizeof(float);
 
     double eff = dl ? c.dl_efficiency : c.efficiency;
     if ((M % c.bm != 0 || N % c.bn != 0) && c.efficiency < eff) eff = c.efficiency;
@@ -277,9 +283,9 @@ SkPlan plan_streamk(const TileConfig &c, int M, int N, int K, int num_cus, bool 
         return p;
     }
     const double unit_cycles = 2.0 * c.bm * c.bn * bk / (kFlopsPerCuCycle * eff);
-    const double per_worker = (double)units / workers;
+    const double per_worker = (double)all_units / workers;
     const double compute =
-        (double)units / num_cus * unit_cycles * (1.0 + kSkWorkerOverheadUnits / per_worker);
+        (double)all_units / num_cus * unit_cycles * (1.0 + kSkWorkerOverheadUnits / per_worker);
     const double bytes = 4.0 * ((double)M * K + (double)K * N + (double)M * N);
     const double memory = bytes / (kHbmBytesPerCuCycle * num_cus);
     // The fixup reads every partial and reads and writes C of the split tiles.
@@ -732,8 +738,8 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
     const bool force_sk = variant >= SGEMM_VARIANT_STREAMK_TILE && !from_tuned;
     const SkPlan &sp = ch.sk;
     if (sp.use) {
-        float *ws = nullptr;
-        const hipError_t we = workspace(stream, sp.ws_bytes, &ws);
+        float *ws = nullptr;  // no shared units (whole rounds only): no workspace
+        const hipError_t we = sp.ws_bytes > 0 ? workspace(stream, sp.ws_bytes, &ws) : hipSuccess;
         if (we != hipSuccess) {
             if (force_sk) return (int)we;
             (void)hipGetLastError();  // fall back to one tile per workgroup
@@ -746,7 +752,7 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
             if (le != hipSuccess) return (int)le;
             if (sp.split_tiles > 0)
                 hipLaunchKernelGGL(sk_fixup_kernel,
-                                   dim3((unsigned)blocks,
+                                   dim3((unsigned)(blocks - sa.dp_tiles),
                                         (unsigned)ceil_div(c->bm * c->bn, kSkFixupElems)),
                                    dim3(256), 0, stream, g, sa, c->bm, c->bn);
             return (int)hipGetLastError();
@@ -922,12 +928,13 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
         const SkPlan &sp = ch.sk;
         std::snprintf(text, sizeof text,
                       "%s bm=%d bn=%d bk=%d waves=%dx%d occ=%d vecA=%d vecB=%d grid=%lld "
-                      "group=%d load=%s streamk=%d split=%d",
+                      "group=%d load=%s streamk=%d dp=%d split=%d",
                       c->family, c->bm, c->bn, dl ? 16 : c->bk, c->wm, c->wn, c->occupancy,
                       (lda & 3) == 0,
                       (ldb & 3) == 0, (long long)tiles_m * tiles_n,
                       group_rows(*c, tiles_m, tiles_n, num_cus), dl ? "direct" : "regs",
-                      sp.use ? sp.args.workers : 0, sp.use ? sp.split_tiles : 0);
+                      sp.use ? sp.args.workers : 0, sp.use ? sp.args.dp_tiles : 0,
+                      sp.use ? sp.split_tiles : 0);
     }
     if (tuned != SGEMM_VARIANT_AUTO) {
         const size_t n = std::strlen(text);

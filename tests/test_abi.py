@@ -199,7 +199,15 @@ def test_streamk_plans():
             units = -(-M // bm) * -(-N // bn) * -(-K // bk)
             assert int(p["streamk"]) <= units
             assert int(p["split"]) < int(p["streamk"])
+            # Whole rounds run one tile per workgroup; only the rest is split.
+            tiles = -(-M // bm) * -(-N // bn)
+            dp, w = int(p["dp"]), int(p["streamk"])
+            assert dp % w == 0 and dp <= tiles and tiles - dp < w
+            assert int(p["split"]) <= tiles - dp
     assert plan(5120, 5120, 5120)["streamk"] == "0"
+    # 576 tiles of 128 over 512 workgroups: one whole round, 64 tiles shared.
+    p = plan(3072, 3072, 3072, variant=sg.SGEMM_VARIANT_STREAMK_TILE + 1)
+    assert (p["streamk"], p["dp"]) == ("512", "512") and 0 < int(p["split"]) <= 64
 
 
 def _tune(**kw):
