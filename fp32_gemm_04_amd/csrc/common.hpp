@@ -8,6 +8,7 @@
 namespace sgemm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Everything a tile kernel needs.  Leading dimensions are 64-bit so that
 // row*ld never overflows, whatever the matrix size.

@@ -156,11 +156,31 @@ const TileConfig kMfmaTiles[] = {
                        SGEMM_DL_SK_KERNEL(128, 128, 2, 4, 1), 0.82),
 };
 
-const TileConfig kValuTile = {"valu", 128, 128, 8, 2, 2, 256, 2, 0.45,
-                              {{valu_tile_kernel<false, false>, valu_tile_kernel<false, true>},
-                               {valu_tile_kernel<true, false>, valu_tile_kernel<true, true>}},
-                              nullptr, 0.0, {{nullptr, nullptr}, {nullptr, nullptr}}, nullptr,
-                              0.0};
+// The vector-FMA kernel's two tiles (both two workgroups per CU).
+#define SGEMM_VALU_ENTRY(BT)                                                        \
+    {"valu", BT, BT, 8, 2, 2, 256, 2, 0.45,                                         \
+     {{valu_tile_kernel<false, false, BT>, valu_tile_kernel<false, true, BT>},      \
+      {valu_tile_kernel<true, false, BT>, valu_tile_kernel<true, true, BT>}},       \
+     nullptr, 0.0, {{nullptr, nullptr}, {nullptr, nullptr}}, nullptr, 0.0}
+const TileConfig kValuTiles[] = {SGEMM_VALU_ENTRY(128), SGEMM_VALU_ENTRY(160)};
+
+// The VALU tile that leaves the least work per resident workgroup: the 160
+// tile where the 128 one would leave a part-empty last round (5120^3).
+const TileConfig *valu_tile(int M, int N, int num_cus)
+{
+    const TileConfig *best = nullptr;
+    double best_work = 0.0;
+    for (const TileConfig &c : kValuTiles) {
+        const int64_t tiles = ((int64_t)M + c.bm - 1) / c.bm * (((int64_t)N + c.bn - 1) / c.bn);
+        const int64_t slots = (int64_t)num_cus * c.occupancy;
+        const double work = (double)((tiles + slots - 1) / slots) * c.bm * c.bn;
+        if (best == nullptr || work < best_work) {
+            best = &c;
+            best_work = work;
+        }
+    }
+    return best;
+}
 
 constexpr double kHbmBytesPerCuCycle = 8.0e12 / (256 * 2.4e9);  // MI355X HBM share
 constexpr double kFlopsPerCuCycle = 256.0;                      // fp32 MFMA per CU
@@ -305,7 +325,7 @@ Choice choose(int variant, int M, int N, int K, int num_cus, bool direct)
 {
     Choice ch = {nullptr, {}};
     if (variant == SGEMM_VARIANT_VALU) {
-        ch.c = &kValuTile;
+        ch.c = valu_tile(M, N, num_cus);
         return ch;
     }
     if (variant >= SGEMM_VARIANT_STREAMK_TILE) {

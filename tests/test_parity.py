@@ -370,3 +370,29 @@ def test_streamk_uniform_repeatable(variant):
     first = _full_check(A, B, C, -0.75, 1.25, variant)
     second = _full_check(A, B, C, -0.75, 1.25, variant)
     assert np.array_equal(first.view(np.uint32), second.view(np.uint32))
+
+
+# The vector-FMA kernel's 160 x 160 tile: shapes where it leaves less work per
+# resident workgroup than the 128 tile (529 tiles of 128 over 512 slots
+# against 361 of 160), with ragged edges and K not a multiple of 8.
+VALU160_SHAPES = [(2900, 2900, 40), (3000, 2800, 37)]
+
+
+@pytest.mark.parametrize("M,N,K", VALU160_SHAPES)
+def test_valu_160_tile_integer_exact(M, N, K):
+    import fp32_gemm_04_amd as sg
+    _, text = sg.sgemm_plan(sg.SGEMM_VARIANT_VALU, M, N, K, K, N, N, 1.0, 256)
+    assert " bm=160 " in text, text
+    A = workloads.integers(M, K, 900 + K)
+    B = workloads.integers(K, N, 901 + K)
+    C = workloads.integers(M, N, 902 + K)
+    _full_check(A, B, C, 1.0, -2.0, variant=sg.SGEMM_VARIANT_VALU, exact=True)
+
+
+@pytest.mark.parametrize("M,N,K", VALU160_SHAPES)
+def test_valu_160_tile_uniform(M, N, K):
+    import fp32_gemm_04_amd as sg
+    A = workloads.uniform(M, K, 910 + K)
+    B = workloads.uniform(K, N, 911 + K)
+    C = workloads.uniform(M, N, 912 + K)
+    _full_check(A, B, C, 1.5, 0.5, variant=sg.SGEMM_VARIANT_VALU)
