@@ -214,6 +214,10 @@ def bench_im2col(sg, stream, reps):
     two HIP events, median of three such runs.  Each launch also pays for
     writing back what the one before it left dirty in the caches.
 
+    `us_tuned`: the same steady state after sgemm_tune (the library's
+    autotuner) chose the kernel for the shape; `tuned_variant` is its choice
+    (0: the selector's own).
+
     `us_single_flushed`: one launch between two events after a 512 MB read that
     evicts the caches, median of `reps`.  This reads low for kernels that
     write C with plain stores: up to the memory-side cache's size of C can
@@ -269,6 +273,20 @@ def bench_im2col(sg, stream, reps):
             torch.cuda.synchronize()
             single.append(e0.elapsed_time(e1))
         ms_single = float(np.median(single))
+        # The library's autotuner on the same operands (sgemm_tune), then the
+        # same steady-state timing with its choice; the table is reset after.
+        rc, tuned_variant, _ = sg.sgemm_tune(*calls[0], 5)
+        assert rc == 0, sg.sgemm_status_string(rc)
+        runs_tuned = []
+        for _ in range(3):
+            e0.record(stream)
+            for k in range(n):
+                sg.sgemm_f32(*calls[k % nset])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            runs_tuned.append(e0.elapsed_time(e1) / n)
+        sg.sgemm_tune_reset()
+        ms_tuned = float(np.median(runs_tuned))
         tflops = case.flops / (ms * 1e-3) / 1e12
         gbps = case.alg_bytes / (ms * 1e-3) / 1e9
         roof_us = max(case.alg_bytes / (PEAK_HBM_GBPS * 1e9), case.flops / (PEAK_FP32_TFLOPS * 1e12)) * 1e6
@@ -281,6 +299,8 @@ def bench_im2col(sg, stream, reps):
                     "frac_roofline": round(roof_us / (ms * 1e3), 4),
                     "us_single_flushed": round(ms_single * 1e3, 2),
                     "frac_roofline_single_flushed": round(roof_us / (ms_single * 1e3), 4),
+                    "us_tuned": round(ms_tuned * 1e3, 2), "tuned_variant": tuned_variant,
+                    "frac_roofline_tuned": round(roof_us / (ms_tuned * 1e3), 4),
                     "kernel": plan})
         del dA, dB, dC, sets, calls
         torch.cuda.empty_cache()
