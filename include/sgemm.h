@@ -91,6 +91,12 @@ enum sgemm_variant {
  * tile per workgroup instead.  Make the first such call on a stream outside
  * graph capture.  Other shapes allocate nothing.
  *
+ * Graph capture: the call only launches kernels on `stream` (no copies, no
+ * memsets, no synchronisation), so it may be captured into a HIP graph and
+ * replayed, once the stream's stream-K workspace exists (an earlier call of
+ * a stream-K shape on that stream, outside capture).  A replay computes what
+ * an eager call computes, bit for bit.  sgemm_tune may not be captured.
+ *
  * Pointers need only float (4-byte) alignment; 16-byte aligned operands
  * with leading dimensions divisible by 4 take 128-bit load paths.
  *
