@@ -364,15 +364,20 @@ Choice choose(int variant, int M, int N, int K, int num_cus, bool direct)
 
 // Stream-K workspaces, one per (device, stream): calls on one stream run in
 // order and share it; calls on different streams never do.  Allocated on
-// first need and grown, never freed.
+// first need and grown.  At most kMaxWorkspacesPerDevice are kept per
+// device: a new stream beyond that takes over the least recently used one
+// (hipFree waits until the device has finished every queued use of it).
+constexpr int kMaxWorkspacesPerDevice = 16;
 struct Workspace {
     int device;
     hipStream_t stream;
     void *ptr;
     size_t bytes;
+    uint64_t last_use;
 };
 std::mutex g_ws_mutex;
 std::vector<Workspace> g_ws;
+uint64_t g_ws_clock = 0;
 
 hipError_t workspace(hipStream_t stream, size_t bytes, float **out)
 {
@@ -380,26 +385,45 @@ hipError_t workspace(hipStream_t stream, size_t bytes, float **out)
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace *slot = nullptr, *lru = nullptr;
+    int on_device = 0;
     for (Workspace &w : g_ws) {
-        if (w.device != dev || w.stream != stream) continue;
-        if (w.bytes < bytes) {
-            // Work queued earlier on this stream may still read the old block;
-            // hipFree waits for the device to finish with it.
-            e = hipFree(w.ptr);
+        if (w.device != dev) continue;
+        ++on_device;
+        if (w.stream == stream) slot = &w;
+        if (lru == nullptr || w.last_use < lru->last_use) lru = &w;
+    }
+    bool taken_over = false;
+    if (slot == nullptr && on_device >= kMaxWorkspacesPerDevice) {
+        slot = lru;  // taken over by this stream
+        slot->stream = stream;
+        taken_over = true;
+    }
+    if (slot != nullptr) {
+        if (slot->bytes < bytes) {
+            // Work queued earlier may still read the old block; hipFree waits
+            // for the device to finish with it.
+            e = hipFree(slot->ptr);
             if (e != hipSuccess) return e;
-            w.ptr = nullptr;
-            w.bytes = 0;
-            e = hipMalloc(&w.ptr, bytes);
+            slot->ptr = nullptr;
+            slot->bytes = 0;
+            e = hipMalloc(&slot->ptr, bytes);
             if (e != hipSuccess) return e;
-            w.bytes = bytes;
+            slot->bytes = bytes;
+        } else if (taken_over) {
+            // Taken over without growing: the previous stream's queued work
+            // may still be using it, so wait for the device first.
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return e;
         }
-        *out = static_cast<float *>(w.ptr);
+        slot->last_use = ++g_ws_clock;
+        *out = static_cast<float *>(slot->ptr);
         return hipSuccess;
     }
     void *ptr = nullptr;
     e = hipMalloc(&ptr, bytes);
     if (e != hipSuccess) return e;
-    g_ws.push_back({dev, stream, ptr, bytes});
+    g_ws.push_back({dev, stream, ptr, bytes, ++g_ws_clock});
     *out = static_cast<float *>(ptr);
     return hipSuccess;
 }

@@ -87,7 +87,9 @@ enum sgemm_variant {
  * needs it allocates it with hipMalloc, a call that needs more frees and
  * reallocates it (hipFree waits for the device), and it is kept until the
  * process ends.  Calls on one stream share it, in stream order; calls on
- * different streams never do.  If the allocation fails the call runs one
+ * different streams never do.  At most 16 are kept per device: a call on a
+ * further stream takes over the least recently used one, after waiting for
+ * the device to finish the work queued on it.  If the allocation fails the call runs one
  * tile per workgroup instead.  Make the first such call on a stream outside
  * graph capture.  Other shapes allocate nothing.
  *

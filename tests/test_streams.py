@@ -121,3 +121,25 @@ def test_two_host_threads():
     torch.cuda.synchronize()
     for j, (_, _, _, C, ref) in enumerate(jobs):
         assert_bits_equal(C.cpu().numpy(), ref.cpu().numpy(), "thread %d" % j)
+
+
+def test_more_streams_than_kept_workspaces():
+    """Stream-K calls on 20 streams in turn (twice round), more than the 16
+    workspaces the library keeps per device: later streams take over the
+    least recently used ones, after the device has finished the work queued
+    on them.  Every result equals the one-stream run."""
+    import fp32_gemm_04_amd as sg
+    variant, M, N, K = 49, 384, 1000, 1152
+    A, B, C0 = _operands(M, N, K, 860)
+    ref = C0.clone()
+    _launch(sg, variant, A, B, ref, 1.0, 0.0, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(20)]
+    outs = [torch.empty_like(C0) for _ in streams]
+    say("stream-K on 20 streams, two rounds")
+    for _ in range(2):
+        for s, C in zip(streams, outs):
+            _launch(sg, variant, A, B, C, 1.0, 0.0, s)
+    torch.cuda.synchronize()
+    for i, C in enumerate(outs):
+        assert_bits_equal(C.cpu().numpy(), ref.cpu().numpy(), "stream %d" % i)
