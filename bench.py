@@ -371,8 +371,9 @@ def bench_ladder_im2col(sg, stream):
 def traffic_probe(sg, case, call_args, stream):
     """Launch sequence for the HBM-traffic counter passes (run under rocprofv3
     --pmc FETCH_SIZE, then WRITE_SIZE): three plain copies of 1 GiB, whose
-    true read and write bytes are known, then three headline SGEMM launches.
-    The copy's counter values give the scale from counter to bytes."""
+    true read and write bytes are known, then three launches of the workload
+    (the headline, or an im2col shape).  The copy's counter values give the
+    scale from counter to bytes."""
     import torch
     n = (1 << 30) // 4
     x = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -386,6 +387,7 @@ def traffic_probe(sg, case, call_args, stream):
             raise RuntimeError(sg.sgemm_status_string(rc))
     torch.cuda.synchronize()
     print(json.dumps({"traffic_probe": True, "copy_bytes_each_way": n * 4,
+                      "shape": [case.M, case.N, case.K], "algorithmic_bytes": case.alg_bytes,
                       "source_hash": source_hash()}), flush=True)
 
 
@@ -402,8 +404,10 @@ def main():
     ap.add_argument("--no-valu", action="store_true", help="skip the VALU-kernel comparison")
     ap.add_argument("--no-ladder", action="store_true", help="skip the SIMT-ladder table")
     ap.add_argument("--no-squares", action="store_true", help="skip the square sweep")
-    ap.add_argument("--traffic-probe", action="store_true",
-                    help="only run the launch sequence for the HBM-traffic counter passes")
+    ap.add_argument("--traffic-probe", nargs="?", const="headline", default=None,
+                    metavar="M,N,K",
+                    help="only run the launch sequence for the HBM-traffic counter passes "
+                         "(the headline, or the im2col shape M,N,K)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -418,13 +422,20 @@ def main():
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     case = workloads.HEADLINE
+    if args.traffic_probe not in (None, "headline"):
+        want = [int(v) for v in args.traffic_probe.split(",")]
+        found = [c for c in workloads.SKINNY + workloads.MID if [c.M, c.N, c.K] == want]
+        if not found:
+            print("no im2col shape %s" % args.traffic_probe, file=sys.stderr)
+            return 2
+        case = found[0]
     log("device", props.name, "CUs", props.multi_processor_count)
     A, B, C, dA, dB, dC = device_operands(case)
     stream = torch.cuda.current_stream()
     call_args = (case.M, case.N, case.K, case.alpha, dA.data_ptr(), case.K, dB.data_ptr(),
                  case.N, case.beta, dC.data_ptr(), case.N, stream.cuda_stream)
 
-    if args.traffic_probe:
+    if args.traffic_probe is not None:
         traffic_probe(sg, case, call_args, stream)
         return 0
 
