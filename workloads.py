@@ -120,3 +120,14 @@ def operands(case: Case, integer: bool = False) -> Tuple[np.ndarray, np.ndarray,
     B = gen(case.K, case.N, seed(case, 1, integer))
     C = gen(case.M, case.N, seed(case, 2, integer)) if case.c_preload else None
     return A, B, C
+
+
+def device_integers(rows: int, cols: int, seed_value: int):
+    """rows x cols float32 integers in [-4, 4] drawn on the GPU (torch's seeded
+    generator), for operands too large to draw on the host; the tests copy
+    the rows or columns they check back to the host for the reference."""
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed_value)
+    return torch.randint(-4, 5, (rows, cols), generator=gen, device="cuda",
+                         dtype=torch.float32)
