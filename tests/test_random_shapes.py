@@ -1,0 +1,69 @@
+"""Seeded random problems (960) through every kernel family: sizes, leading-dimension
+padding, base misalignment, alpha and beta drawn at random (one fixed seed,
+so every run draws the same cases).  Integer data, so every output must match
+the reference bit for bit, and nothing outside C's window may change."""
+import numpy as np
+import pytest
+
+import workloads
+from tests.gpu_helpers import assert_bits_equal, run, say
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp32_gemm_04_amd  # noqa: F401
+
+
+def _families():
+    import fp32_gemm_04_amd as sg
+    n = sg.sgemm_num_mfma_tiles()
+    return ([sg.SGEMM_VARIANT_AUTO, sg.SGEMM_VARIANT_VALU, sg.SGEMM_VARIANT_SKINNY]
+            + [sg.SGEMM_VARIANT_MFMA_TILE + i for i in range(n)]
+            + [sg.SGEMM_VARIANT_STREAMK_TILE + i for i in range(n)]
+            + [sg.SGEMM_VARIANT_LADDER + r for r in range(sg.SGEMM_LADDER_RUNGS)])
+
+
+def _cases(count=960, seed=2024):
+    rng = np.random.default_rng(seed)
+    fams = _families()
+    out = []
+    for i in range(count):
+        v = fams[i % len(fams)]
+        big = rng.random() < 0.3
+        M = int(rng.integers(1, 400 if big else 140))
+        N = int(rng.integers(1, 400 if big else 140))
+        K = int(rng.integers(1, 600 if big else 150))
+        if v == 3:  # the skinny kernel takes M <= 64, K <= 240
+            M, K = min(M, 64), min(K, 240)
+        pads = [int(p) if rng.random() < 0.4 else 0 for p in rng.integers(1, 9, 3)]
+        offs = [int(o) if rng.random() < 0.3 else 0 for o in rng.integers(1, 4, 3)]
+        alpha = float(rng.choice([1.0, -1.0, 0.5, 1.5, 2.0, 0.0]))
+        beta = float(rng.choice([0.0, 0.0, 1.0, -0.5, 0.25]))
+        out.append((i, v, M, N, K, pads, offs, alpha, beta))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("chunk", range(8))
+def test_random_problems_integer_exact(chunk):
+    for (i, v, M, N, K, pads, offs, alpha, beta) in CASES[chunk::8]:
+        A = workloads.integers(M, K, 5000 + 3 * i)
+        B = workloads.integers(K, N, 5001 + 3 * i)
+        C = workloads.integers(M, N, 5002 + 3 * i)
+        lds = (K + pads[0], N + pads[1], N + pads[2])
+        say("random case %d: variant %d M=%d N=%d K=%d pads=%s offsets=%s alpha=%g beta=%g"
+            % (i, v, M, N, K, pads, offs, alpha, beta))
+        out, dC = run(A, B, C, alpha, beta, variant=v, lds=lds, offsets=tuple(offs),
+                      name="random %d" % i)
+        ref, _ = oracle.sgemm(A, B, C, alpha, beta)
+        assert_bits_equal(out, ref, "random case %d (variant %d)" % (i, v))
+        assert dC.outside_is_nan(), "case %d: C written outside its window" % i
