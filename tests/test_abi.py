@@ -237,3 +237,34 @@ def test_tune_reset_and_untuned_plans():
         M, N, K = shape
         rc, text = sg.sgemm_plan(0, M, N, K, K, N, N, 1.0, 256)
         assert rc == 0 and "tuned=" not in text
+
+
+@pytest.mark.parametrize("M,N,K,expect", [
+    # one 64 x 64 tile per CU through the twelve-slab ring
+    (1024, 1024, 1024, dict(bm="64", bn="64", waves="2x2", occ="1", load="direct", streamk="0")),
+    # one 128 x 128 tile per CU with eight waves
+    (2048, 2048, 2048, dict(bm="128", waves="2x4", occ="1", load="direct", streamk="0")),
+    # stream-K shares with the eight-wave tile (100 tiles < 256 CUs)
+    (1280, 1280, 1280, dict(bm="128", waves="2x4", streamk="256", dp="0")),
+    # two whole rounds of 160 x 160
+    (5120, 5120, 5120, dict(bm="160", bn="160", occ="2", load="direct", streamk="0")),
+    # one whole round plus 64 shared tiles
+    (3072, 3072, 3072, dict(bm="128", waves="2x2", streamk="512", dp="512", split="64")),
+    # the mid im2col shapes
+    (256, 50176, 1024, dict(bm="128", streamk="512", dp="512")),
+    (256, 43264, 1152, dict(bm="128", load="direct", streamk="0")),
+    (384, 14161, 1152, dict(bm="64", occ="4", load="regs", vecB="0")),
+])
+def test_selector_choices(M, N, K, expect):
+    """The cost model's choices on the configurations, as measured best on
+    MI355X (256 CUs); a change to the model that moves them shows here."""
+    p = plan(M, N, K)
+    for k, v in expect.items():
+        assert p[k] == v, (k, p)
+
+
+def test_valu_tile_choice():
+    """The vector-FMA kernel takes the 160 tile where the 128 one leaves a
+    part-empty last round of resident workgroups."""
+    assert plan(5120, 5120, 5120, variant=sg.SGEMM_VARIANT_VALU)["bm"] == "160"
+    assert plan(4096, 4096, 4096, variant=sg.SGEMM_VARIANT_VALU)["bm"] == "128"
