@@ -174,8 +174,9 @@ typedef void (*SkKernelFn)(GemmArgs, SkArgs);
 
 // Direct-load MFMA kernel for a tile shape and waves-per-SIMD target, or
 // null if none is built for it (defined in mfma_dl.hip); the stream-K form.
-KernelFn direct_kernel(int bm, int bn, int wm, int wn, int wpe);
-SkKernelFn direct_sk_kernel(int bm, int bn, int wm, int wn, int wpe);
+// shifted: the form for B rows that need not be 16-byte aligned (or null).
+KernelFn direct_kernel(int bm, int bn, int wm, int wn, int wpe, bool shifted);
+SkKernelFn direct_sk_kernel(int bm, int bn, int wm, int wn, int wpe, bool shifted);
 
 // Balancing a kernel's work per SIMD, for kernels that run one workgroup
 // per CU whose 4 WPE waves fill it: each SIMD has its own matrix core, and

@@ -10,8 +10,14 @@
 // MFMAs run.
 //
 // Used for tiles that lie wholly inside C when K is a multiple of 16 and A
-// and B rows are 16-byte aligned; other tiles of the same launch run the
-// masked register-staged path of mfma_tile.hpp.
+// rows are 16-byte aligned; other tiles of the same launch run the masked
+// register-staged path of mfma_tile.hpp.  B rows are either 16-byte aligned
+// or, in the shifted form (BSH), start anywhere: then each B row of a slab
+// is fetched from the 16-byte boundary at or below its first column, d
+// floats early (d = 0..3, the row's own misalignment), into one more chunk
+// than the tile needs, and the operand reads add d back.  Every fetched
+// 16-byte piece holds at least one element of the row segment, so no fetch
+// leaves the pages B lies in.
 //
 // LDS: NBUF buffers (a ring; three unless the tile says otherwise) of
 // (BM + BN) / 16 chunks of 1 KB (256 floats).  The
@@ -24,6 +30,12 @@
 //     holds B[k0 + 4 g + s][16 cb + c]; at step s lane l reads float
 //     64 s + l, i.e. the wave reads 256 contiguous bytes.
 // Both patterns touch every bank once, so operand reads are conflict-free.
+// Shifted form: chunk cb holds columns 16 cb - d .. 16 cb - d + 15 of each
+// row (d of that row), and chunk CB the next four.  Rows 4 apart share d
+// (16-byte pieces hold four floats), so at step s one d serves the wave:
+// lane 16 g + c reads float 64 s + 16 g + (c + d) of its block's chunk,
+// spilling into the next chunk's first d floats when c + d >= 16; the
+// banks stay distinct.
 //
 // Pipeline of slab t (its operands already in registers):
 //   k-steps 0, 1: MFMAs, with the loads of slab t+NBUF-1 spread over them,
@@ -87,33 +99,39 @@ __device__ __forceinline__ void wait_slabs_barrier(int k)
     }
 }
 
-template <int BM, int BN, int WM, int WN, int NBUF_ = 3>
+template <int BM, int BN, int WM, int WN, int NBUF_ = 3, bool BSH = false>
 struct MfmaDl {
     static constexpr int NW = WM * WN;
     static constexpr int FM = BM / WM / 16;        // 16x16 blocks per wave along M
     static constexpr int FN = BN / WN / 16;        // ... along N
     static constexpr int CA = BM / 16;             // A chunks per slab
-    static constexpr int CB = BN / 16;             // B chunks per slab
-    static constexpr int L = (CA + CB) / NW;       // loads per wave per slab
-    static constexpr int BUF = (CA + CB) * 256;    // floats per LDS buffer
+    static constexpr int CB = BN / 16;             // B chunks per slab (+1 shifted)
+    static constexpr int CT = CA + CB + (BSH ? 1 : 0);
+    // Loads per wave per slab: L, and one more for waves 0 .. X-1.
+    static constexpr int L = CT / NW;
+    static constexpr int X = CT % NW;
+    static constexpr int LMAX = L + (X > 0 ? 1 : 0);
+    static constexpr int BUF = CT * 256;           // floats per LDS buffer
     static constexpr int NBUF = NBUF_;
     static constexpr int LDS = NBUF * BUF;         // floats of LDS
-    // The first half of a slab (2 FM FN MFMAs) carries L loads, one every
-    // STRIDE MFMAs; the second half R operand reads, one per MFMA.
+    // The first half of a slab (2 FM FN MFMAs) carries up to LMAX loads, one
+    // every STRIDE MFMAs; the second half R operand reads, one per MFMA.
     static constexpr int R = FM + 2 * FN;
-    static constexpr int STRIDE = 2 * FM * FN / (L + 1);
-    static_assert((CA + CB) % NW == 0, "slab chunks must split evenly over the waves");
+    static constexpr int STRIDE = 2 * FM * FN / (LMAX + 1);
+    static_assert(BSH || X == 0, "slab chunks must split evenly over the waves");
+    static_assert(L >= 1, "every wave loads");
     static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile must be 16-aligned");
     static_assert(STRIDE >= 1 && R <= 2 * FM * FN, "too few MFMAs per slab for the reads and loads");
     static_assert(NBUF >= 3, "the ring needs a buffer being read, one landing, one free");
-    static_assert(L * (NBUF - 1) <= 63, "loads in flight must fit the vmcnt field");
+    static_assert(LMAX * (NBUF - 1) <= 63, "loads in flight must fit the vmcnt field");
 };
 
-template <int BM, int BN, int WM, int WN, int NBUF_>
+template <int BM, int BN, int WM, int WN, int NBUF_, bool BSH>
 __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, float *lds)
 {
-    using D = MfmaDl<BM, BN, WM, WN, NBUF_>;
-    constexpr int NW = D::NW, FM = D::FM, FN = D::FN, CA = D::CA, L = D::L, BUF = D::BUF;
+    using D = MfmaDl<BM, BN, WM, WN, NBUF_, BSH>;
+    constexpr int NW = D::NW, FM = D::FM, FN = D::FN, CA = D::CA, CB = D::CB, L = D::L;
+    constexpr int X = D::X, LMAX = D::LMAX, BUF = D::BUF;
     constexpr int NBUF = D::NBUF, R = D::R, S1 = D::STRIDE;
     constexpr int TM = BM / WM, TN = BN / WN;
     const int nslab = g.K / 16;
@@ -123,14 +141,27 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
     const int wr = wave / WN;
     const int wc = wave % WN;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_float *)lds;
+    // Waves 0 .. X-1 issue one load more per slab than the others.
+    const bool extra = X > 0 && wave < X;
+
+    // Shifted form: shift[s] is the misalignment, in floats, of column n0 in
+    // B rows k with k % 4 == s (the same for every slab, 16 rows apart).
+    int shift[4] = {0, 0, 0, 0};
+    if constexpr (BSH) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            shift[s] = (int)((reinterpret_cast<uintptr_t>(g.B + (int64_t)s * g.ldb + n0) >> 2) & 3);
+    }
 
     // Load i of this wave fills chunk c = wave + i * NW of every slab: A
-    // block c if c < CA, else B block c - CA.
-    const float *src[L];
-    uint32_t dst[L];
-    bool is_a[L];
+    // block c if c < CA, else B chunk c - CA (the shifted form's chunk CB:
+    // the row's four floats after chunk CB - 1, or, where the row needs none,
+    // its last four floats again, unread).
+    const float *src[LMAX];
+    uint32_t dst[LMAX];
+    bool is_a[LMAX];
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
+    for (int i = 0; i < LMAX; ++i) {
         const int c = wave + i * NW;
         dst[i] = (uint32_t)c * 1024u;
         is_a[i] = c < CA;
@@ -138,7 +169,12 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
             src[i] = g.A + (int64_t)(m0 + 16 * c + (lane & 15)) * g.lda + 4 * (lane >> 4);
         } else {
             const int k = 4 * ((lane >> 2) & 3) + (lane >> 4);
-            src[i] = g.B + (int64_t)k * g.ldb + n0 + 16 * (c - CA) + 4 * (lane & 3);
+            const int d = shift[lane >> 4];
+            const float *row = g.B + (int64_t)k * g.ldb + n0 - d;
+            if (c < CA + CB)
+                src[i] = row + 16 * (c - CA) + 4 * (lane & 3);
+            else
+                src[i] = row + BN - (d > 0 ? 0 : 4);
         }
     }
     const int64_t a_step = 16, b_step = 16 * g.ldb;
@@ -162,15 +198,28 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
     float bfs[2][4][FN];
     // Operand read number r (0 .. R-1) of the slab in buffer buf, in order
     // of first use: A blocks, then B k-steps 0-1, then B k-steps 2-3.
+    // Shifted form: lane's float offset, inside its block's chunk, at step s.
+    int boff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int x = (lane & 15) + shift[s];
+        boff[s] = 64 * s + 16 * (lane >> 4) + (x & 15) + (x >= 16 ? 256 : 0);
+    }
     auto read_op = [&](int r, int buf, f32x4 (&af)[FM], float (&bf)[4][FN]) {
         const float *base = lds + buf * BUF;
         if (r < FM) {
             af[r] = *reinterpret_cast<const f32x4 *>(base + (wr * FM + r) * 256 + 4 * lane);
         } else {
             const int h = (r - FM) / FN, fn = (r - FM) % FN;
-            const float *bs = base + (CA + wc * FN + fn) * 256 + 128 * h + lane;
-            bf[2 * h][fn] = bs[0];
-            bf[2 * h + 1][fn] = bs[64];
+            if constexpr (BSH) {
+                const float *bs = base + (CA + wc * FN + fn) * 256;
+                bf[2 * h][fn] = bs[boff[2 * h]];
+                bf[2 * h + 1][fn] = bs[boff[2 * h + 1]];
+            } else {
+                const float *bs = base + (CA + wc * FN + fn) * 256 + 128 * h + lane;
+                bf[2 * h][fn] = bs[0];
+                bf[2 * h + 1][fn] = bs[64];
+            }
         }
     };
     // k-steps s0..s1-1; hook(n) runs before the n-th MFMA of the call.
@@ -200,14 +249,17 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
         const bool more = t >= 1 && t + NBUF - 1 < nslab;
         const uint32_t bb = buffer_bytes(buf == 0 ? NBUF - 1 : buf - 1);
         ksteps(0, 2, afs[p], bfs[p], [&](int n) {
-            if (n > 0 && n % S1 == 0 && n / S1 <= L) {
-                if (more) load(n / S1 - 1, bb);
+            if (n > 0 && n % S1 == 0 && n / S1 <= LMAX) {
+                if (more && (n / S1 <= L || extra)) load(n / S1 - 1, bb);
             }
         });
         __builtin_amdgcn_sched_barrier(0);
         // In flight: slab t+1's loads, then those of the slabs after it up to
         // t+NBUF-1 (as far as they exist): wait for slab t+1's.
-        wait_slabs_barrier<L, NBUF - 2>(nslab - 2 - t);
+        if (extra)
+            wait_slabs_barrier<LMAX, NBUF - 2>(nslab - 2 - t);
+        else
+            wait_slabs_barrier<L, NBUF - 2>(nslab - 2 - t);
         const int nb = buf + 1 == NBUF ? 0 : buf + 1;
         ksteps(2, 4, afs[p], bfs[p], [&](int n) {
             if (n < R) {
@@ -223,9 +275,13 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
     for (int b = 0; b < NBUF; ++b)
         if (b < nslab) {
 #pragma unroll
-            for (int i = 0; i < L; ++i) load(i, buffer_bytes(b));
+            for (int i = 0; i < LMAX; ++i)
+                if (i < L || extra) load(i, buffer_bytes(b));
         }
-    wait_slabs_barrier<L, NBUF - 1>(nslab - 1);
+    if (extra)
+        wait_slabs_barrier<LMAX, NBUF - 1>(nslab - 1);
+    else
+        wait_slabs_barrier<L, NBUF - 1>(nslab - 1);
     // (slab 0 issues no loads: slabs 1 .. NBUF-1 are already in flight)
 #pragma unroll
     for (int r = 0; r < R; ++r) read_op(r, 0, afs[0], bfs[0]);
@@ -262,13 +318,14 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
 }
 
 // Interior tiles take the direct-load body, border tiles the masked
-// register-staged one; both share the LDS array.
-template <int BM, int BN, int WM, int WN, int WPE, int NBUF = 3>
+// register-staged one (B through 32-bit loads in the shifted form); both
+// share the LDS array.
+template <int BM, int BN, int WM, int WN, int WPE, int NBUF = 3, bool BSH = false>
 __global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 mfma_dl_kernel(GemmArgs g)
 {
     using T = MfmaTile<BM, BN, 16, WM, WN>;
-    constexpr int DL = MfmaDl<BM, BN, WM, WN, NBUF>::LDS;
+    constexpr int DL = MfmaDl<BM, BN, WM, WN, NBUF, BSH>::LDS;
     constexpr int RG = 2 * (T::LDS_A + T::LDS_B);
     __shared__ __attribute__((aligned(16))) float lds[DL > RG ? DL : RG];
 
@@ -277,28 +334,29 @@ mfma_dl_kernel(GemmArgs g)
     const int m0 = tm * BM;
     const int n0 = tn * BN;
     if (m0 + BM <= g.M && n0 + BN <= g.N)
-        mfma_dl_body<BM, BN, WM, WN, NBUF>(g, m0, n0, lds);
+        mfma_dl_body<BM, BN, WM, WN, NBUF, BSH>(g, m0, n0, lds);
     else
-        mfma_tile_body<BM, BN, 16, WM, WN, 2, true, true, true>(g, m0, n0, lds, lds + 2 * T::LDS_A);
+        mfma_tile_body<BM, BN, 16, WM, WN, 2, true, !BSH, true>(g, m0, n0, lds,
+                                                                lds + 2 * T::LDS_A);
 }
 
 // Stream-K form: this workgroup's range of tile segments (sk_run), each
 // through the same two bodies.
-template <int BM, int BN, int WM, int WN, int WPE, int NBUF = 3>
+template <int BM, int BN, int WM, int WN, int WPE, int NBUF = 3, bool BSH = false>
 __global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 mfma_dl_sk_kernel(GemmArgs g, SkArgs s)
 {
     using T = MfmaTile<BM, BN, 16, WM, WN>;
-    constexpr int DL = MfmaDl<BM, BN, WM, WN, NBUF>::LDS;
+    constexpr int DL = MfmaDl<BM, BN, WM, WN, NBUF, BSH>::LDS;
     constexpr int RG = 2 * (T::LDS_A + T::LDS_B);
     __shared__ __attribute__((aligned(16))) float lds[DL > RG ? DL : RG];
 
     sk_run<BM, BN>(g, s, [&](const GemmArgs &a, int m0, int n0) __attribute__((always_inline)) {
         if (m0 + BM <= a.M && n0 + BN <= a.N)
-            mfma_dl_body<BM, BN, WM, WN, NBUF>(a, m0, n0, lds);
+            mfma_dl_body<BM, BN, WM, WN, NBUF, BSH>(a, m0, n0, lds);
         else
-            mfma_tile_body<BM, BN, 16, WM, WN, 2, true, true, true>(a, m0, n0, lds,
-                                                                      lds + 2 * T::LDS_A);
+            mfma_tile_body<BM, BN, 16, WM, WN, 2, true, !BSH, true>(a, m0, n0, lds,
+                                                                    lds + 2 * T::LDS_A);
     });
 }
 

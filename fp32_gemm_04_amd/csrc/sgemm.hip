@@ -90,7 +90,24 @@ struct TileConfig {
     SkKernelFn sk_fn[2][2];  // stream-K forms of fn and dl
     SkKernelFn sk_dl;
     double one_efficiency;   // measured with one workgroup per CU (0: 0.85 x efficiency)
+    KernelFn dls;            // direct-load forms for B rows of any alignment (or null)
+    SkKernelFn sk_dls;
 };
+
+// How the operands allow slabs to be loaded straight into LDS: not at all
+// (K % 16 != 0 or A rows not 16-byte aligned), with B rows 16-byte aligned,
+// or with B rows at any 4-byte alignment (the shifted form).
+enum DirectMode { kDirectNone = 0, kDirectAligned = 1, kDirectShifted = 2 };
+
+KernelFn dl_of(const TileConfig &c, int dmode)
+{
+    return dmode == kDirectAligned ? c.dl : dmode == kDirectShifted ? c.dls : nullptr;
+}
+
+SkKernelFn sk_dl_of(const TileConfig &c, int dmode)
+{
+    return dmode == kDirectAligned ? c.sk_dl : dmode == kDirectShifted ? c.sk_dls : nullptr;
+}
 
 // WPE (waves per SIMD) = OCC workgroups per CU x waves per workgroup / 4 SIMDs.
 #define SGEMM_MFMA_WPE(WM, WN, OCC) ((OCC) * (WM) * (WN) / 4)
@@ -111,13 +128,15 @@ struct TileConfig {
        SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, ROCC, ST, false, true)},                 \
       {SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, ROCC, ST, true, false),                  \
        SGEMM_MFMA_SK_KERNEL(BM, BN, BK, WM, WN, ROCC, ST, true, true)}},                 \
-     SKDL, ONE}
+     SKDL, ONE,                                                                          \
+     direct_kernel(BM, BN, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), true),                   \
+     direct_sk_kernel(BM, BN, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), true)}
 #define SGEMM_MFMA_ENTRY(BM, BN, BK, WM, WN, OCC, ST, EFF, DL, DLEFF, SKDL, ONE) \
     SGEMM_MFMA_ENTRY_R(BM, BN, BK, WM, WN, OCC, OCC, ST, EFF, DL, DLEFF, SKDL, ONE)
 #define SGEMM_DL_KERNEL(BM, BN, WM, WN, OCC) \
-    direct_kernel(BM, BN, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC))
+    direct_kernel(BM, BN, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), false)
 #define SGEMM_DL_SK_KERNEL(BM, BN, WM, WN, OCC) \
-    direct_sk_kernel(BM, BN, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC))
+    direct_sk_kernel(BM, BN, WM, WN, SGEMM_MFMA_WPE(WM, WN, OCC), false)
 
 // The MFMA tile table.  Occupancy (workgroups per CU) is what LDS and the
 // register budget allow.  Efficiencies are the fractions of the CU's fp32
@@ -161,7 +180,7 @@ const TileConfig kMfmaTiles[] = {
     {"valu", BT, BT, 8, 2, 2, 256, 2, 0.45,                                         \
      {{valu_tile_kernel<false, false, BT>, valu_tile_kernel<false, true, BT>},      \
       {valu_tile_kernel<true, false, BT>, valu_tile_kernel<true, true, BT>}},       \
-     nullptr, 0.0, {{nullptr, nullptr}, {nullptr, nullptr}}, nullptr, 0.0}
+     nullptr, 0.0, {{nullptr, nullptr}, {nullptr, nullptr}}, nullptr, 0.0, nullptr, nullptr}
 const TileConfig kValuTiles[] = {SGEMM_VALU_ENTRY(128), SGEMM_VALU_ENTRY(160)};
 
 // The VALU tile that leaves the least work per resident workgroup: the 160
@@ -184,6 +203,20 @@ const TileConfig *valu_tile(int M, int N, int num_cus)
 
 constexpr double kHbmBytesPerCuCycle = 8.0e12 / (256 * 2.4e9);  // MI355X HBM share
 constexpr double kFlopsPerCuCycle = 256.0;                      // fp32 MFMA per CU
+// The shifted direct-load form against the aligned one, both run stream-K
+// ((256,43265,1152) against (256,43264,1152): 221.4 against 203.7 us;
+// (384,14161,1152) with ldb 14161 against 14164: 125.3 against 116.8 us).
+constexpr double kShiftedEfficiency = 0.92;
+// Border tiles of a shifted direct-load kernel run the masked register-staged
+// body with 32-bit B loads: this fraction of the entry's register-staged
+// efficiency ((256,43265,1152) one tile per workgroup: 242.6 us, where the
+// aligned (256,43264,1152) takes 206.8).
+constexpr double kShiftedBorderEfficiency = 0.85;
+
+double dl_efficiency(const TileConfig &c, int dmode)
+{
+    return c.dl_efficiency * (dmode == kDirectShifted ? kShiftedEfficiency : 1.0);
+}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -192,20 +225,25 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // a whole one) at the entry's efficiency (that of the register-staged path
 // when partial tiles exist), lowered when a CU holds fewer
 // workgroups than its occupancy (fewer waves to hide latency); never less
-// than the time to move the operands through HBM once.  `direct`: the
-// operands allow the direct-load path.
-double estimate_cycles(const TileConfig &c, int M, int N, int K, int num_cus, bool direct)
+// than the time to move the operands through HBM once.  `dmode`: how the
+// operands allow the direct-load path (DirectMode).
+double estimate_cycles(const TileConfig &c, int M, int N, int K, int num_cus, int dmode)
 {
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
     const int64_t per_cu = ceil_div(tiles, num_cus);
-    const bool dl = direct && c.dl != nullptr;
+    const bool dl = dl_of(c, dmode) != nullptr;
     const int bk = dl ? 16 : c.bk;
-    double eff = dl ? c.dl_efficiency : c.efficiency;
+    double eff = dl ? dl_efficiency(c, dmode) : c.efficiency;
     if (eff <= 0.0) return HUGE_VAL;  // only run when forced
     // Partial tiles at the right or bottom edge run the masked register-staged
     // body; a CU that holds one sets the pace (measured at 2304^3: the 160 tile
     // with a 64-wide edge reaches 52 TFLOPS, the 64 tile without edges 98).
-    if ((M % c.bm != 0 || N % c.bn != 0) && c.efficiency < eff) eff = c.efficiency;
+    if ((M % c.bm != 0 || N % c.bn != 0) && dl && dmode == kDirectShifted &&
+        c.efficiency * kShiftedBorderEfficiency < eff)
+        eff = c.efficiency * kShiftedBorderEfficiency;
+    else if ((M % c.bm != 0 || N % c.bn != 0) && c.efficiency < eff)
+        eff = c.efficiency;
+    if (eff <= 0.0) return HUGE_VAL;
     if (per_cu == 1 && c.one_efficiency > 0.0)
         eff = c.one_efficiency;
     else if (per_cu < c.occupancy)
@@ -253,11 +291,11 @@ constexpr double kSkMargin = 0.95;
 // than stream-K saves (512^3 and 768^3 measured 9-25% slower with it).
 constexpr double kSkMinCycles = 60000.0;
 
-SkPlan plan_streamk(const TileConfig &c, int M, int N, int K, int num_cus, bool direct)
+SkPlan plan_streamk(const TileConfig &c, int M, int N, int K, int num_cus, int dmode)
 {
     SkPlan p = {};
     if (c.sk_fn[0][0] == nullptr || K <= 0 || M <= 0 || N <= 0) return p;
-    const bool dl = direct && c.sk_dl != nullptr;
+    const bool dl = sk_dl_of(c, dmode) != nullptr;
     const int bk = dl ? 16 : c.bk;
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
     const int iters = (int)ceil_div(K, bk);
@@ -296,8 +334,14 @@ SkPlan plan_streamk(const TileConfig &c, int M, int N, int K, int num_cus, bool 
     p.partials = partials;
     p.ws_bytes = (size_t)2 * sk_workers * c.bm * c.bn * sizeof(float);
 
-    double eff = dl ? c.dl_efficiency : c.efficiency;
-    if ((M % c.bm != 0 || N % c.bn != 0) && c.efficiency < eff) eff = c.efficiency;
+    double eff = dl ? dl_efficiency(c, dmode) : c.efficiency;
+    // Border tiles run the masked register-staged body; priced at the entry's
+    // register-staged efficiency, except in kernels whose register-staged
+    // build is forced-only (efficiency 0): their border segments, a small
+    // share of a worker's units, measured no slower ((384,14161,1152) on the
+    // eight-wave 128 x 128 tile: 125.3 us, the estimate without them 122).
+    if ((M % c.bm != 0 || N % c.bn != 0) && c.efficiency > 0.0 && c.efficiency < eff)
+        eff = c.efficiency;
     if (eff <= 0.0) {  // only run when forced
         p.cycles = HUGE_VAL;
         return p;
@@ -321,7 +365,7 @@ struct Choice {
     SkPlan sk;
 };
 
-Choice choose(int variant, int M, int N, int K, int num_cus, bool direct)
+Choice choose(int variant, int M, int N, int K, int num_cus, int dmode)
 {
     Choice ch = {nullptr, {}};
     if (variant == SGEMM_VARIANT_VALU) {
@@ -330,7 +374,7 @@ Choice choose(int variant, int M, int N, int K, int num_cus, bool direct)
     }
     if (variant >= SGEMM_VARIANT_STREAMK_TILE) {
         ch.c = &kMfmaTiles[variant - SGEMM_VARIANT_STREAMK_TILE];
-        ch.sk = plan_streamk(*ch.c, M, N, K, num_cus, direct);
+        ch.sk = plan_streamk(*ch.c, M, N, K, num_cus, dmode);
         ch.sk.use = ch.sk.args.workers > 0;
         return ch;
     }
@@ -340,7 +384,7 @@ Choice choose(int variant, int M, int N, int K, int num_cus, bool direct)
     }
     double best = 0.0;
     for (const TileConfig &c : kMfmaTiles) {
-        const double dp = estimate_cycles(c, M, N, K, num_cus, direct);
+        const double dp = estimate_cycles(c, M, N, K, num_cus, dmode);
         if (ch.c == nullptr || dp < best) {
             ch = {&c, {}};
             best = dp;
@@ -349,10 +393,10 @@ Choice choose(int variant, int M, int N, int K, int num_cus, bool direct)
     // Automatic stream-K only on the direct-load path: with unaligned
     // operands the register-staged segments run below the efficiency the
     // estimate assumes ((384, 14161, 1152) measured 4.5% slower with it).
-    if (!direct || best < kSkMinCycles) return ch;
+    if (dmode == kDirectNone || best < kSkMinCycles) return ch;
     for (const TileConfig &c : kMfmaTiles) {
-        if (c.sk_dl == nullptr) continue;
-        SkPlan sp = plan_streamk(c, M, N, K, num_cus, direct);
+        if (sk_dl_of(c, dmode) == nullptr) continue;
+        SkPlan sp = plan_streamk(c, M, N, K, num_cus, dmode);
         if (sp.args.workers > 0 && sp.cycles / kSkMargin < best) {
             sp.use = true;
             ch = {&c, sp};
@@ -767,8 +811,8 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
         if (rung < kLadderRungs - 1) return launch_ladder(rung, g, avec, bvec, stream);
         variant = SGEMM_VARIANT_VALU;
     }
-    const bool direct = avec && bvec && K % 16 == 0;
-    const Choice ch = choose(variant, M, N, K, cus, direct);
+    const int dmode = avec && K % 16 == 0 ? (bvec ? kDirectAligned : kDirectShifted) : kDirectNone;
+    const Choice ch = choose(variant, M, N, K, cus, dmode);
     const TileConfig *c = ch.c;
     g.tiles_m = (int)ceil_div(M, c->bm);
     g.tiles_n = (int)ceil_div(N, c->bn);
@@ -790,7 +834,8 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
         } else {
             SkArgs sa = sp.args;
             sa.ws = ws;
-            const SkKernelFn fn = c->sk_dl && direct ? c->sk_dl : c->sk_fn[avec][bvec];
+            const SkKernelFn dfn = sk_dl_of(*c, dmode);
+            const SkKernelFn fn = dfn ? dfn : c->sk_fn[avec][bvec];
             hipLaunchKernelGGL(fn, dim3((unsigned)sa.workers), dim3(threads), 0, stream, g, sa);
             const hipError_t le = hipGetLastError();
             if (le != hipSuccess) return (int)le;
@@ -802,7 +847,8 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
             return (int)hipGetLastError();
         }
     }
-    const KernelFn fn = c->dl && direct ? c->dl : c->fn[avec][bvec];
+    const KernelFn dfn = dl_of(*c, dmode);
+    const KernelFn fn = dfn ? dfn : c->fn[avec][bvec];
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), 0, stream, g);
     return (int)hipGetLastError();
 }
@@ -963,12 +1009,14 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
                       variant - SGEMM_VARIANT_LADDER, r.name, r.tile_m, r.tile_n, r.threads,
                       (long long)ceil_div(M, r.tile_m) * ceil_div(N, r.tile_n));
     } else {
-        const bool direct = (lda & 3) == 0 && (ldb & 3) == 0 && K % 16 == 0;
-        const Choice ch = choose(variant, M, N, K, num_cus, direct);
+        const int dmode = (lda & 3) == 0 && K % 16 == 0
+                              ? ((ldb & 3) == 0 ? kDirectAligned : kDirectShifted)
+                              : kDirectNone;
+        const Choice ch = choose(variant, M, N, K, num_cus, dmode);
         const TileConfig *c = ch.c;
         const int tiles_m = (int)ceil_div(M, c->bm);
         const int tiles_n = (int)ceil_div(N, c->bn);
-        const bool dl = c->dl && direct;
+        const bool dl = dl_of(*c, dmode) != nullptr;
         const SkPlan &sp = ch.sk;
         std::snprintf(text, sizeof text,
                       "%s bm=%d bn=%d bk=%d waves=%dx%d occ=%d vecA=%d vecB=%d grid=%lld "
@@ -976,7 +1024,8 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
                       c->family, c->bm, c->bn, dl ? 16 : c->bk, c->wm, c->wn, c->occupancy,
                       (lda & 3) == 0,
                       (ldb & 3) == 0, (long long)tiles_m * tiles_n,
-                      group_rows(*c, tiles_m, tiles_n, num_cus), dl ? "direct" : "regs",
+                      group_rows(*c, tiles_m, tiles_n, num_cus),
+                      !dl ? "regs" : dmode == kDirectShifted ? "shifted" : "direct",
                       sp.use ? sp.args.workers : 0, sp.use ? sp.args.dp_tiles : 0,
                       sp.use ? sp.split_tiles : 0);
     }

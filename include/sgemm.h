@@ -156,7 +156,9 @@ int sgemm_f32_variant(int variant, int M, int N, int K, float alpha,
  *   "mfma bm=160 bn=160 bk=16 waves=2x2 occ=2 vecA=1 vecB=1 grid=1024 group=8
  *    load=direct streamk=0 dp=0 split=0"
  * (on one line: tile, waves, workgroups per CU, 128-bit paths, tiles, raster
- * group, slab load path, stream-K workgroups, tiles run whole, tiles split)
+ * group, slab load path -- "direct" straight to LDS, "shifted" the same for
+ * B rows not 16-byte aligned, "regs" through registers -- stream-K
+ * workgroups, tiles run whole, tiles split)
  * into buf (at most buflen bytes, truncated if needed).  The leading word
  * names the kernel: "none" (nothing to do), "scale" (K == 0 or alpha == 0),
  * "mfma", "valu", "skinny", "stream16" or "ladder".  Returns 0, or the same negative codes as

@@ -222,6 +222,42 @@ def test_direct_load_path_uniform(variant):
         _full_check(A, B, C, -0.75, 1.25, variant)
 
 
+# B rows that are not 16-byte aligned (ldb % 4 != 0 or a B base off
+# 16-byte alignment) with A aligned and K % 16 == 0: the 128 x 128 tiles take
+# the shifted direct-load form, whose row misalignment d = 0..3 varies from
+# row to row (ldb % 4 = 1, 2, 3) and with the base offset.  Border tiles of
+# the same launch run the register-staged path with 32-bit B loads.
+SHIFTED_SHAPES = [(128, 128, 16), (256, 257, 32), (257, 389, 48), (384, 1001, 64),
+                  (130, 263, 80), (384, 1041, 320)]
+SHIFTED_FAMILIES = [17, 23, 49, 55]
+
+
+@pytest.mark.parametrize("variant", [0] + SHIFTED_FAMILIES)
+def test_shifted_direct_load_integer_exact(variant):
+    for M, N, K in SHIFTED_SHAPES:
+        A = workloads.integers(M, K, 41 * M + K)
+        B = workloads.integers(K, N, 43 * N + K)
+        C = workloads.integers(M, N, 47 * M + N)
+        for pad, boff in [(1, 0), (2, 1), (3, 3), (0, 2), (5, 0)]:
+            ldb = N + pad
+            lds = (K, ldb, N + 3)
+            if ldb % 4 == 0 and boff == 0:
+                continue
+            if variant in SHIFTED_FAMILIES and boff == 0:
+                assert _plan_load(variant, M, N, K, *lds) == "shifted"
+            _full_check(A, B, C, 1.5, 0.5, variant, exact=True, lds=lds,
+                        offsets=(0, boff, 0))
+
+
+@pytest.mark.parametrize("variant", SHIFTED_FAMILIES)
+def test_shifted_direct_load_uniform(variant):
+    for M, N, K in SHIFTED_SHAPES[1::2]:
+        A = workloads.uniform(M, K, 53 * M + K)
+        B = workloads.uniform(K, N, 59 * N + K)
+        C = workloads.uniform(M, N, 61 * M + N)
+        _full_check(A, B, C, -0.75, 1.25, variant, lds=(K, N + 1, N), offsets=(0, 1, 0))
+
+
 @pytest.mark.parametrize("variant", FAMILIES)
 def test_misaligned_bases(variant):
     """Base pointers off 16-byte alignment take the 32-bit load paths."""
