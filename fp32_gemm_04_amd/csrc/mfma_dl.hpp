@@ -9,9 +9,11 @@
 // MFMA operands, so a wave reads slab t+1's operands while slab t's last
 // MFMAs run.
 //
-// Used for tiles that lie wholly inside C when K is a multiple of 16 and A
-// rows are 16-byte aligned; other tiles of the same launch run the masked
-// register-staged path of mfma_tile.hpp.  B rows are either 16-byte aligned
+// Used when K is a multiple of 16 and A rows are 16-byte aligned, for every
+// tile of the launch: in a tile that sticks out of C, A rows past M fetch
+// row M - 1 and B pieces past column N - 1 fetch the piece that holds it.
+// Those values reach only outputs outside C, which are not stored, so no
+// zero fill is needed (K has no border).  B rows are either 16-byte aligned
 // or, in the shifted form (BSH), start anywhere: then each B row of a slab
 // is fetched from the 16-byte boundary at or below its first column, d
 // floats early (d = 0..3, the row's own misalignment), into one more chunk
@@ -126,7 +128,9 @@ struct MfmaDl {
     static_assert(LMAX * (NBUF - 1) <= 63, "loads in flight must fit the vmcnt field");
 };
 
-template <int BM, int BN, int WM, int WN, int NBUF_, bool BSH>
+// EDGE: the tile may stick out of C (clamped sources, masked stores); the
+// interior copy carries neither.
+template <int BM, int BN, int WM, int WN, int NBUF_, bool BSH, bool EDGE>
 __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, float *lds)
 {
     using D = MfmaDl<BM, BN, WM, WN, NBUF_, BSH>;
@@ -156,7 +160,8 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
     // Load i of this wave fills chunk c = wave + i * NW of every slab: A
     // block c if c < CA, else B chunk c - CA (the shifted form's chunk CB:
     // the row's four floats after chunk CB - 1, or, where the row needs none,
-    // its last four floats again, unread).
+    // its last four floats again, unread).  Sources past C's edge are
+    // clamped (rows to M - 1, B pieces to the one holding column N - 1).
     const float *src[LMAX];
     uint32_t dst[LMAX];
     bool is_a[LMAX];
@@ -166,15 +171,22 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
         dst[i] = (uint32_t)c * 1024u;
         is_a[i] = c < CA;
         if (c < CA) {
-            src[i] = g.A + (int64_t)(m0 + 16 * c + (lane & 15)) * g.lda + 4 * (lane >> 4);
+            int r = m0 + 16 * c + (lane & 15);
+            if constexpr (EDGE) r = r < g.M ? r : g.M - 1;
+            src[i] = g.A + (int64_t)r * g.lda + 4 * (lane >> 4);
         } else {
             const int k = 4 * ((lane >> 2) & 3) + (lane >> 4);
             const int d = shift[lane >> 4];
-            const float *row = g.B + (int64_t)k * g.ldb + n0 - d;
-            if (c < CA + CB)
-                src[i] = row + 16 * (c - CA) + 4 * (lane & 3);
-            else
-                src[i] = row + BN - (d > 0 ? 0 : 4);
+            const float *row = g.B + (int64_t)k * g.ldb;
+            int col = c < CA + CB ? n0 - d + 16 * (c - CA) + 4 * (lane & 3)
+                                  : n0 - d + BN - (d > 0 ? 0 : 4);
+            if constexpr (EDGE) {
+                // The 16-byte piece holding column N - 1 starts e floats before it.
+                const int e = (int)((reinterpret_cast<uintptr_t>(row + g.N - 1) >> 2) & 3);
+                const int last = g.N - 1 - e;
+                col = col < last ? col : last;
+            }
+            src[i] = row + col;
         }
     }
     const int64_t a_step = 16, b_step = 16 * g.ldb;
@@ -298,17 +310,20 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
         }
     }
 
-    // Epilogue: C = alpha*acc + beta*C (the tile is inside C).
+    // Epilogue: C = alpha*acc + beta*C inside C's M x N window.
     const float alpha = g.alpha, beta = g.beta;
     const int lm = lane & 15, lg = lane >> 4;
+    const int col0 = n0 + wc * TN + lm;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = m0 + wr * TM + fm * 16 + 4 * lg + i;
-            float *crow = g.C + (int64_t)row * g.ldc + n0 + wc * TN + lm;
+            if (EDGE && row >= g.M) continue;
+            float *crow = g.C + (int64_t)row * g.ldc + col0;
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
+                if (EDGE && col0 + fn * 16 >= g.N) continue;
                 float v = alpha * acc[fm][fn][i];
                 if (beta != 0.f) v = fmaf(beta, crow[fn * 16], v);
                 crow[fn * 16] = v;
@@ -317,46 +332,35 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
     }
 }
 
-// Interior tiles take the direct-load body, border tiles the masked
-// register-staged one (B through 32-bit loads in the shifted form); both
-// share the LDS array.
+// One BM x BN tile per workgroup; border tiles through the EDGE copy.
 template <int BM, int BN, int WM, int WN, int WPE, int NBUF = 3, bool BSH = false>
 __global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 mfma_dl_kernel(GemmArgs g)
 {
-    using T = MfmaTile<BM, BN, 16, WM, WN>;
-    constexpr int DL = MfmaDl<BM, BN, WM, WN, NBUF, BSH>::LDS;
-    constexpr int RG = 2 * (T::LDS_A + T::LDS_B);
-    __shared__ __attribute__((aligned(16))) float lds[DL > RG ? DL : RG];
+    __shared__ __attribute__((aligned(16))) float lds[MfmaDl<BM, BN, WM, WN, NBUF, BSH>::LDS];
 
     int tm, tn;
     tile_of_block(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
+    const int m0 = tm * BM, n0 = tn * BN;
     if (m0 + BM <= g.M && n0 + BN <= g.N)
-        mfma_dl_body<BM, BN, WM, WN, NBUF, BSH>(g, m0, n0, lds);
+        mfma_dl_body<BM, BN, WM, WN, NBUF, BSH, false>(g, m0, n0, lds);
     else
-        mfma_tile_body<BM, BN, 16, WM, WN, 2, true, !BSH, true>(g, m0, n0, lds,
-                                                                lds + 2 * T::LDS_A);
+        mfma_dl_body<BM, BN, WM, WN, NBUF, BSH, true>(g, m0, n0, lds);
 }
 
 // Stream-K form: this workgroup's range of tile segments (sk_run), each
-// through the same two bodies.
+// through the same bodies.
 template <int BM, int BN, int WM, int WN, int WPE, int NBUF = 3, bool BSH = false>
 __global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 mfma_dl_sk_kernel(GemmArgs g, SkArgs s)
 {
-    using T = MfmaTile<BM, BN, 16, WM, WN>;
-    constexpr int DL = MfmaDl<BM, BN, WM, WN, NBUF, BSH>::LDS;
-    constexpr int RG = 2 * (T::LDS_A + T::LDS_B);
-    __shared__ __attribute__((aligned(16))) float lds[DL > RG ? DL : RG];
+    __shared__ __attribute__((aligned(16))) float lds[MfmaDl<BM, BN, WM, WN, NBUF, BSH>::LDS];
 
     sk_run<BM, BN>(g, s, [&](const GemmArgs &a, int m0, int n0) __attribute__((always_inline)) {
         if (m0 + BM <= a.M && n0 + BN <= a.N)
-            mfma_dl_body<BM, BN, WM, WN, NBUF, BSH>(a, m0, n0, lds);
+            mfma_dl_body<BM, BN, WM, WN, NBUF, BSH, false>(a, m0, n0, lds);
         else
-            mfma_tile_body<BM, BN, 16, WM, WN, 2, true, !BSH, true>(a, m0, n0, lds,
-                                                                    lds + 2 * T::LDS_A);
+            mfma_dl_body<BM, BN, WM, WN, NBUF, BSH, true>(a, m0, n0, lds);
     });
 }
 

@@ -204,14 +204,9 @@ const TileConfig *valu_tile(int M, int N, int num_cus)
 constexpr double kHbmBytesPerCuCycle = 8.0e12 / (256 * 2.4e9);  // MI355X HBM share
 constexpr double kFlopsPerCuCycle = 256.0;                      // fp32 MFMA per CU
 // The shifted direct-load form against the aligned one, both run stream-K
-// ((256,43265,1152) against (256,43264,1152): 221.4 against 203.7 us;
-// (384,14161,1152) with ldb 14161 against 14164: 125.3 against 116.8 us).
-constexpr double kShiftedEfficiency = 0.92;
-// Border tiles of a shifted direct-load kernel run the masked register-staged
-// body with 32-bit B loads: this fraction of the entry's register-staged
-// efficiency ((256,43265,1152) one tile per workgroup: 242.6 us, where the
-// aligned (256,43264,1152) takes 206.8).
-constexpr double kShiftedBorderEfficiency = 0.85;
+// ((256,43265,1152) against (256,43264,1152): 212.5 against 201.2 us;
+// (384,14161,1152) with ldb 14161 against 14164: 115.0 against 109.8 us).
+constexpr double kShiftedEfficiency = 0.95;
 
 double dl_efficiency(const TileConfig &c, int dmode)
 {
@@ -233,17 +228,11 @@ double estimate_cycles(const TileConfig &c, int M, int N, int K, int num_cus, in
     const int64_t per_cu = ceil_div(tiles, num_cus);
     const bool dl = dl_of(c, dmode) != nullptr;
     const int bk = dl ? 16 : c.bk;
+    // Partial tiles at the right or bottom edge cost a whole tile: the
+    // direct-load kernels run them through the same body, the register-staged
+    // ones through a masked copy of theirs.
     double eff = dl ? dl_efficiency(c, dmode) : c.efficiency;
     if (eff <= 0.0) return HUGE_VAL;  // only run when forced
-    // Partial tiles at the right or bottom edge run the masked register-staged
-    // body; a CU that holds one sets the pace (measured at 2304^3: the 160 tile
-    // with a 64-wide edge reaches 52 TFLOPS, the 64 tile without edges 98).
-    if ((M % c.bm != 0 || N % c.bn != 0) && dl && dmode == kDirectShifted &&
-        c.efficiency * kShiftedBorderEfficiency < eff)
-        eff = c.efficiency * kShiftedBorderEfficiency;
-    else if ((M % c.bm != 0 || N % c.bn != 0) && c.efficiency < eff)
-        eff = c.efficiency;
-    if (eff <= 0.0) return HUGE_VAL;
     if (per_cu == 1 && c.one_efficiency > 0.0)
         eff = c.one_efficiency;
     else if (per_cu < c.occupancy)
@@ -334,14 +323,7 @@ SkPlan plan_streamk(const TileConfig &c, int M, int N, int K, int num_cus, int d
     p.partials = partials;
     p.ws_bytes = (size_t)2 * sk_workers * c.bm * c.bn * sizeof(float);
 
-    double eff = dl ? dl_efficiency(c, dmode) : c.efficiency;
-    // Border tiles run the masked register-staged body; priced at the entry's
-    // register-staged efficiency, except in kernels whose register-staged
-    // build is forced-only (efficiency 0): their border segments, a small
-    // share of a worker's units, measured no slower ((384,14161,1152) on the
-    // eight-wave 128 x 128 tile: 125.3 us, the estimate without them 122).
-    if ((M % c.bm != 0 || N % c.bn != 0) && c.efficiency > 0.0 && c.efficiency < eff)
-        eff = c.efficiency;
+    const double eff = dl ? dl_efficiency(c, dmode) : c.efficiency;
     if (eff <= 0.0) {  // only run when forced
         p.cycles = HUGE_VAL;
         return p;

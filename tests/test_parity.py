@@ -182,9 +182,9 @@ def test_padded_leading_dimensions(variant):
                     lds=(K + pads[0], N + pads[1], N + pads[2]))
 
 
-# K a multiple of 16 with 16-byte aligned rows: interior tiles of the 160,
-# 128 and 64x256 families take the direct global -> LDS path, border tiles
-# of the same launch the register-staged one.  K = 16 .. 64 covers one to
+# K a multiple of 16 with 16-byte aligned rows: the 160, 128, 64x256 and
+# 64x64 ring families take the direct global -> LDS path, border tiles
+# through its clamped and masked copy.  K = 16 .. 64 covers one to
 # four slabs (every prologue case of the three-buffer pipeline); K = 80 an
 # odd slab count; ldb is rounded up to a multiple of 4 so that ragged N
 # still gives aligned B rows.
@@ -225,8 +225,10 @@ def test_direct_load_path_uniform(variant):
 # B rows that are not 16-byte aligned (ldb % 4 != 0 or a B base off
 # 16-byte alignment) with A aligned and K % 16 == 0: the 128 x 128 tiles take
 # the shifted direct-load form, whose row misalignment d = 0..3 varies from
-# row to row (ldb % 4 = 1, 2, 3) and with the base offset.  Border tiles of
-# the same launch run the register-staged path with 32-bit B loads.
+# row to row (ldb % 4 = 1, 2, 3) and with the base offset.  Border tiles
+# (ragged M and N) run the same body with clamped sources and masked stores;
+# the NaN padding past each row and matrix shows any clamped value that
+# reaches C.
 SHIFTED_SHAPES = [(128, 128, 16), (256, 257, 32), (257, 389, 48), (384, 1001, 64),
                   (130, 263, 80), (384, 1041, 320)]
 SHIFTED_FAMILIES = [17, 23, 49, 55]
