@@ -234,7 +234,7 @@ double estimate_cycles(const TileConfig &c, int M, int N, int K, int num_cus, in
     double eff = dl ? dl_efficiency(c, dmode) : c.efficiency;
     if (eff <= 0.0) return HUGE_VAL;  // only run when forced
     if (per_cu == 1 && c.one_efficiency > 0.0)
-        eff = c.one_efficiency;
+        eff = c.one_efficiency * (dl && dmode == kDirectShifted ? kShiftedEfficiency : 1.0);
     else if (per_cu < c.occupancy)
         eff *= 0.85;
     const double kpad = (double)ceil_div(K, bk) * bk;

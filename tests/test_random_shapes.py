@@ -1,6 +1,7 @@
-"""Seeded random problems (960) through every kernel family: sizes, leading-dimension
-padding, base misalignment, alpha and beta drawn at random (one fixed seed,
-so every run draws the same cases).  Integer data, so every output must match
+"""Seeded random problems (960 through every kernel family, then 320 on the
+direct-load path): sizes, leading-dimension padding, base misalignment,
+alpha and beta drawn at random (one fixed seed, so every run draws the same
+cases).  Integer data, so every output must match
 the reference bit for bit, and nothing outside C's window may change."""
 import numpy as np
 import pytest
@@ -66,4 +67,45 @@ def test_random_problems_integer_exact(chunk):
                       name="random %d" % i)
         ref, _ = oracle.sgemm(A, B, C, alpha, beta)
         assert_bits_equal(out, ref, "random case %d (variant %d)" % (i, v))
+        assert dC.outside_is_nan(), "case %d: C written outside its window" % i
+
+
+def _direct_cases(count=320, seed=4096):
+    """K a multiple of 16 and A rows aligned, so the direct-load kernels run:
+    ragged M and N (border tiles through the clamped, masked body), B rows
+    at every alignment (the shifted form) and base offsets of B and C."""
+    # AUTO and the tile entries that have direct-load kernels (160, 128,
+    # 64x256, the 64x64 ring, the eight-wave 128), each one tile per
+    # workgroup and stream-K.
+    fams = [0, 16, 17, 20, 22, 23, 48, 49, 52, 54, 55]
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        v = fams[i % len(fams)]
+        M = int(rng.integers(1, 420))
+        N = int(rng.integers(1, 700))
+        K = 16 * int(rng.integers(1, 24))
+        lda = K + 4 * int(rng.integers(0, 3))
+        aligned = rng.random() < 0.4  # else the shifted form (on the 128 tiles)
+        ldb = (-(-N // 4) * 4 + 4 * int(rng.integers(0, 2))) if aligned else N + int(rng.integers(0, 8))
+        ldc = N + int(rng.integers(0, 5))
+        offs = [0, 0 if aligned else int(rng.integers(0, 4)), int(rng.integers(0, 4))]
+        alpha = float(rng.choice([1.0, -0.5, 2.0]))
+        beta = float(rng.choice([0.0, 1.0, -1.5]))
+        out.append((i, v, M, N, K, (lda, ldb, ldc), offs, alpha, beta))
+    return out
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_random_direct_load_problems_integer_exact(chunk):
+    for (i, v, M, N, K, lds, offs, alpha, beta) in _direct_cases()[chunk::4]:
+        A = workloads.integers(M, K, 9000 + 3 * i)
+        B = workloads.integers(K, N, 9001 + 3 * i)
+        C = workloads.integers(M, N, 9002 + 3 * i)
+        say("direct case %d: variant %d M=%d N=%d K=%d lds=%s offsets=%s alpha=%g beta=%g"
+            % (i, v, M, N, K, lds, offs, alpha, beta))
+        out, dC = run(A, B, C, alpha, beta, variant=v, lds=lds, offsets=tuple(offs),
+                      name="direct %d" % i)
+        ref, _ = oracle.sgemm(A, B, C, alpha, beta)
+        assert_bits_equal(out, ref, "direct case %d (variant %d)" % (i, v))
         assert dC.outside_is_nan(), "case %d: C written outside its window" % i
