@@ -1,8 +1,9 @@
 // fp32 MFMA tile kernel with direct global -> LDS slab loads (gfx950).
 //
-// Same mathematics as mfma_tile.hpp (one workgroup per BM x BN tile of C,
-// K in 16-wide slabs, v_mfma_f32_16x16x4_f32 with lane group g taking
-// k = 4g + s at step s), but the slabs travel from HBM to LDS with
+// The mathematics of the register-staged tile kernel in mfma_tile.hpp (one
+// workgroup per BM x BN tile of C, K in 16-wide slabs,
+// v_mfma_f32_16x16x4_f32 with lane group g taking k = 4g + s at step s),
+// but the slabs travel from HBM to LDS with
 // global_load_lds_dwordx4: lane l of the instruction writes its 16 bytes
 // to LDS at M0 + 16 l, so no registers hold slab data and no LDS store
 // instructions are issued.  The registers this frees hold a second set of
@@ -58,7 +59,7 @@
 
 #include <type_traits>
 
-#include "mfma_tile.hpp"
+#include "common.hpp"
 
 namespace sgemm {
 
