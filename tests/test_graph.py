@@ -21,13 +21,16 @@ def _need_gpu():
 
 
 # (variant, M, N, K, alpha, beta): one tile per workgroup, stream-K (which
-# also launches the fixup kernel), the skinny streaming kernel.
+# also launches the fixup kernel), the skinny streaming kernel, and odd N
+# (B rows unaligned: the shifted direct-load form, one tile per workgroup
+# and stream-K, with border tiles).
 CASES = [(0, 640, 768, 512, 1.5, 0.5), (49, 384, 1000, 1152, 1.0, -1.0),
-         (0, 64, 163840, 147, 1.0, 0.0)]
+         (0, 64, 163840, 147, 1.0, 0.0), (0, 384, 2001, 320, 1.0, 0.5),
+         (55, 384, 2001, 1152, -1.0, 1.0)]
 
 
 @pytest.mark.parametrize("variant,M,N,K,alpha,beta", CASES,
-                         ids=["tile", "streamk", "skinny"])
+                         ids=["tile", "streamk", "skinny", "shifted", "shifted_streamk"])
 def test_captured_call_replays_like_eager(variant, M, N, K, alpha, beta):
     import fp32_gemm_04_amd as sg
     A = torch.from_numpy(workloads.uniform(M, K, 950 + K)).cuda()
