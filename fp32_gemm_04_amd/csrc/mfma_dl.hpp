@@ -10,11 +10,12 @@
 // MFMA operands, so a wave reads slab t+1's operands while slab t's last
 // MFMAs run.
 //
-// Used when K is a multiple of 16 and A rows are 16-byte aligned, for every
-// tile of the launch: in a tile that sticks out of C, A rows past M fetch
-// row M - 1 and B pieces past column N - 1 fetch the piece that holds it.
-// Those values reach only outputs outside C, which are not stored, so no
-// zero fill is needed (K has no border).  B rows are either 16-byte aligned
+// Used when A rows are 16-byte aligned, for every tile of the launch: in a
+// tile that sticks out of C, A rows past M fetch row M - 1 and B pieces past
+// column N - 1 fetch the piece that holds it.  Those values reach only
+// outputs outside C, which are not stored, so they need no zero fill.  The
+// K % 16 columns after the last whole slab are a slab of their own, loaded
+// through registers with zeros past K.  B rows are either 16-byte aligned
 // or, in the shifted form (BSH), start anywhere: then each B row of a slab
 // is fetched from the 16-byte boundary at or below its first column, d
 // floats early (d = 0..3, the row's own misalignment), into one more chunk
@@ -130,8 +131,10 @@ struct MfmaDl {
 };
 
 // EDGE: the tile may stick out of C (clamped sources, masked stores); the
-// interior copy carries neither.
-template <int BM, int BN, int WM, int WN, int NBUF_, bool BSH, bool EDGE>
+// interior copy carries neither.  KT: K need not be a multiple of 16 (the
+// stream-K forms are only launched when it is, which keeps their scalar
+// registers within budget).
+template <int BM, int BN, int WM, int WN, int NBUF_, bool BSH, bool EDGE, bool KT>
 __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, float *lds)
 {
     using D = MfmaDl<BM, BN, WM, WN, NBUF_, BSH>;
@@ -311,6 +314,46 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
         }
     }
 
+    // K not a multiple of 16: the last K % 16 columns of A and rows of B go
+    // through registers into buffer 0, in the same chunk layout, with zeros
+    // for k >= K (and for B columns outside the row), then one more slab of
+    // MFMAs.  Every operand of the ring is in registers by now.
+    if (KT && g.K % 16 != 0) {
+        __syncthreads();
+        const int kt = nslab * 16;
+#pragma unroll
+        for (int i = 0; i < LMAX; ++i) {
+            const int c = wave + i * NW;
+            if (i >= L && !extra) continue;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (c < CA) {
+                int r = m0 + 16 * c + (lane & 15);
+                r = r < g.M ? r : g.M - 1;
+                const int k = kt + 4 * (lane >> 4);
+                const float *p = g.A + (int64_t)r * g.lda + k;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (k + j < g.K) v[j] = p[j];
+            } else {
+                const int k = kt + 4 * ((lane >> 2) & 3) + (lane >> 4);
+                const int col = n0 - shift[lane >> 4] + 16 * (c - CA) + 4 * (lane & 3);
+                if (k < g.K) {
+                    const float *p = g.B + (int64_t)k * g.ldb + col;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (col + j >= 0 && col + j < g.N) v[j] = p[j];
+                }
+            }
+            *reinterpret_cast<f32x4 *>(lds + c * 256 + 4 * lane) = v;
+        }
+        __syncthreads();
+        f32x4 af[FM];
+        float bf[4][FN];
+#pragma unroll
+        for (int r = 0; r < R; ++r) read_op(r, 0, af, bf);
+        ksteps(0, 4, af, bf, no_hook);
+    }
+
     // Epilogue: C = alpha*acc + beta*C inside C's M x N window.
     const float alpha = g.alpha, beta = g.beta;
     const int lm = lane & 15, lg = lane >> 4;
@@ -344,13 +387,13 @@ mfma_dl_kernel(GemmArgs g)
     tile_of_block(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     if (m0 + BM <= g.M && n0 + BN <= g.N)
-        mfma_dl_body<BM, BN, WM, WN, NBUF, BSH, false>(g, m0, n0, lds);
+        mfma_dl_body<BM, BN, WM, WN, NBUF, BSH, false, true>(g, m0, n0, lds);
     else
-        mfma_dl_body<BM, BN, WM, WN, NBUF, BSH, true>(g, m0, n0, lds);
+        mfma_dl_body<BM, BN, WM, WN, NBUF, BSH, true, true>(g, m0, n0, lds);
 }
 
 // Stream-K form: this workgroup's range of tile segments (sk_run), each
-// through the same bodies.
+// through the same bodies; K must be a multiple of 16.
 template <int BM, int BN, int WM, int WN, int WPE, int NBUF = 3, bool BSH = false>
 __global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 mfma_dl_sk_kernel(GemmArgs g, SkArgs s)
@@ -359,9 +402,9 @@ mfma_dl_sk_kernel(GemmArgs g, SkArgs s)
 
     sk_run<BM, BN>(g, s, [&](const GemmArgs &a, int m0, int n0) __attribute__((always_inline)) {
         if (m0 + BM <= a.M && n0 + BN <= a.N)
-            mfma_dl_body<BM, BN, WM, WN, NBUF, BSH, false>(a, m0, n0, lds);
+            mfma_dl_body<BM, BN, WM, WN, NBUF, BSH, false, false>(a, m0, n0, lds);
         else
-            mfma_dl_body<BM, BN, WM, WN, NBUF, BSH, true>(a, m0, n0, lds);
+            mfma_dl_body<BM, BN, WM, WN, NBUF, BSH, true, false>(a, m0, n0, lds);
     });
 }
 

@@ -85,7 +85,7 @@ struct TileConfig {
     int occupancy;       // workgroups that fit on one CU (LDS/registers)
     double efficiency;   // fraction of the CU's fp32 peak, register-staged path
     KernelFn fn[2][2];   // [A 128-bit loads][B 128-bit loads]
-    KernelFn dl;         // direct-to-LDS variant (K % 16 == 0, aligned rows) or null
+    KernelFn dl;         // direct-to-LDS variant (A rows 16-byte aligned, B rows too) or null
     double dl_efficiency;  // ... when the direct-load variant runs
     SkKernelFn sk_fn[2][2];  // stream-K forms of fn and dl
     SkKernelFn sk_dl;
@@ -95,8 +95,8 @@ struct TileConfig {
 };
 
 // How the operands allow slabs to be loaded straight into LDS: not at all
-// (K % 16 != 0 or A rows not 16-byte aligned), with B rows 16-byte aligned,
-// or with B rows at any 4-byte alignment (the shifted form).
+// (A rows not 16-byte aligned), with B rows 16-byte aligned, or with B rows
+// at any 4-byte alignment (the shifted form).
 enum DirectMode { kDirectNone = 0, kDirectAligned = 1, kDirectShifted = 2 };
 
 KernelFn dl_of(const TileConfig &c, int dmode)
@@ -108,6 +108,9 @@ SkKernelFn sk_dl_of(const TileConfig &c, int dmode)
 {
     return dmode == kDirectAligned ? c.sk_dl : dmode == kDirectShifted ? c.sk_dls : nullptr;
 }
+
+// The direct-load stream-K kernels take K a multiple of 16 only.
+int sk_dmode(int dmode, int K) { return K % 16 == 0 ? dmode : kDirectNone; }
 
 // WPE (waves per SIMD) = OCC workgroups per CU x waves per workgroup / 4 SIMDs.
 #define SGEMM_MFMA_WPE(WM, WN, OCC) ((OCC) * (WM) * (WN) / 4)
@@ -284,6 +287,7 @@ SkPlan plan_streamk(const TileConfig &c, int M, int N, int K, int num_cus, int d
 {
     SkPlan p = {};
     if (c.sk_fn[0][0] == nullptr || K <= 0 || M <= 0 || N <= 0) return p;
+    dmode = sk_dmode(dmode, K);
     const bool dl = sk_dl_of(c, dmode) != nullptr;
     const int bk = dl ? 16 : c.bk;
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
@@ -375,7 +379,7 @@ Choice choose(int variant, int M, int N, int K, int num_cus, int dmode)
     // Automatic stream-K only on the direct-load path: with unaligned
     // operands the register-staged segments run below the efficiency the
     // estimate assumes ((384, 14161, 1152) measured 4.5% slower with it).
-    if (dmode == kDirectNone || best < kSkMinCycles) return ch;
+    if (sk_dmode(dmode, K) == kDirectNone || best < kSkMinCycles) return ch;
     for (const TileConfig &c : kMfmaTiles) {
         if (sk_dl_of(c, dmode) == nullptr) continue;
         SkPlan sp = plan_streamk(c, M, N, K, num_cus, dmode);
@@ -793,7 +797,7 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
         if (rung < kLadderRungs - 1) return launch_ladder(rung, g, avec, bvec, stream);
         variant = SGEMM_VARIANT_VALU;
     }
-    const int dmode = avec && K % 16 == 0 ? (bvec ? kDirectAligned : kDirectShifted) : kDirectNone;
+    const int dmode = avec ? (bvec ? kDirectAligned : kDirectShifted) : kDirectNone;
     const Choice ch = choose(variant, M, N, K, cus, dmode);
     const TileConfig *c = ch.c;
     g.tiles_m = (int)ceil_div(M, c->bm);
@@ -816,7 +820,7 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
         } else {
             SkArgs sa = sp.args;
             sa.ws = ws;
-            const SkKernelFn dfn = sk_dl_of(*c, dmode);
+            const SkKernelFn dfn = sk_dl_of(*c, sk_dmode(dmode, K));
             const SkKernelFn fn = dfn ? dfn : c->sk_fn[avec][bvec];
             hipLaunchKernelGGL(fn, dim3((unsigned)sa.workers), dim3(threads), 0, stream, g, sa);
             const hipError_t le = hipGetLastError();
@@ -991,15 +995,15 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
                       variant - SGEMM_VARIANT_LADDER, r.name, r.tile_m, r.tile_n, r.threads,
                       (long long)ceil_div(M, r.tile_m) * ceil_div(N, r.tile_n));
     } else {
-        const int dmode = (lda & 3) == 0 && K % 16 == 0
-                              ? ((ldb & 3) == 0 ? kDirectAligned : kDirectShifted)
-                              : kDirectNone;
+        const int dmode = (lda & 3) == 0 ? ((ldb & 3) == 0 ? kDirectAligned : kDirectShifted)
+                                         : kDirectNone;
         const Choice ch = choose(variant, M, N, K, num_cus, dmode);
         const TileConfig *c = ch.c;
         const int tiles_m = (int)ceil_div(M, c->bm);
         const int tiles_n = (int)ceil_div(N, c->bn);
-        const bool dl = dl_of(*c, dmode) != nullptr;
         const SkPlan &sp = ch.sk;
+        const bool dl = sp.use ? sk_dl_of(*c, sk_dmode(dmode, K)) != nullptr
+                               : dl_of(*c, dmode) != nullptr;
         std::snprintf(text, sizeof text,
                       "%s bm=%d bn=%d bk=%d waves=%dx%d occ=%d vecA=%d vecB=%d grid=%lld "
                       "group=%d load=%s streamk=%d dp=%d split=%d",

@@ -182,7 +182,7 @@ def test_padded_leading_dimensions(variant):
                     lds=(K + pads[0], N + pads[1], N + pads[2]))
 
 
-# K a multiple of 16 with 16-byte aligned rows: the 160, 128, 64x256 and
+# K a multiple of 16 with 16-byte aligned rows (other K below): the 160, 128, 64x256 and
 # 64x64 ring families take the direct global -> LDS path, border tiles
 # through its clamped and masked copy.  K = 16 .. 64 covers one to
 # four slabs (every prologue case of the three-buffer pipeline); K = 80 an
@@ -211,6 +211,40 @@ def test_direct_load_path_integer_exact(variant):
             if variant in DIRECT_FAMILIES:
                 assert _plan_load(variant, M, N, K, *lds) == "direct"
             _full_check(A, B, C, 1.5, 0.5, variant, exact=True, lds=lds)
+
+
+# K not a multiple of 16 on the direct-load path (A rows aligned through
+# lda rounded up to a multiple of 4): the last K % 16 columns are one more
+# slab, zero-filled past K; K < 16 is that slab alone.  B rows aligned, then
+# not (the shifted form on the 128 tiles and the 64 x 64 ring).  Forced
+# stream-K runs its register-staged kernels for such K.
+K_TAIL_SHAPES = [(160, 160, 17), (321, 319, 50), (64, 64, 3), (130, 263, 1000),
+                 (257, 389, 31), (96, 500, 1)]
+
+
+@pytest.mark.parametrize("variant", [0] + DIRECT_FAMILIES)
+def test_direct_load_k_tail_integer_exact(variant):
+    for M, N, K in K_TAIL_SHAPES:
+        A = workloads.integers(M, K, 67 * M + K)
+        B = workloads.integers(K, N, 71 * N + K)
+        C = workloads.integers(M, N, 73 * M + N)
+        la = -(-K // 4) * 4
+        nb = -(-N // 4) * 4
+        for lds, boff in [((la, nb, N), 0), ((la + 4, N + 1, N + 2), 3)]:
+            if variant in DIRECT_FAMILIES and boff == 0:
+                # the stream-K forms take the register-staged path here
+                want = "direct" if variant < 48 else "regs"
+                assert _plan_load(variant, M, N, K, *lds) == want
+            _full_check(A, B, C, 1.5, 0.5, variant, exact=True, lds=lds, offsets=(0, boff, 0))
+
+
+@pytest.mark.parametrize("variant", DIRECT_FAMILIES)
+def test_direct_load_k_tail_uniform(variant):
+    for M, N, K in K_TAIL_SHAPES[1::2]:
+        A = workloads.uniform(M, K, 79 * M + K)
+        B = workloads.uniform(K, N, 83 * N + K)
+        C = workloads.uniform(M, N, 89 * M + N)
+        _full_check(A, B, C, -0.75, 1.25, variant, lds=(-(-K // 4) * 4, N, N))
 
 
 @pytest.mark.parametrize("variant", DIRECT_FAMILIES)

@@ -71,8 +71,9 @@ def test_random_problems_integer_exact(chunk):
 
 
 def _direct_cases(count=320, seed=4096):
-    """K a multiple of 16 and A rows aligned, so the direct-load kernels run:
-    ragged M and N (border tiles through the clamped, masked body), B rows
+    """A rows aligned, so the direct-load kernels run: K a multiple of 16 or
+    not (the zero-filled last slab), ragged M and N (border tiles through the
+    clamped, masked body), B rows
     at every alignment (the shifted form) and base offsets of B and C."""
     # AUTO and the tile entries that have direct-load kernels (160, 128,
     # 64x256, the 64x64 ring, the eight-wave 128), each one tile per
@@ -84,8 +85,8 @@ def _direct_cases(count=320, seed=4096):
         v = fams[i % len(fams)]
         M = int(rng.integers(1, 420))
         N = int(rng.integers(1, 700))
-        K = 16 * int(rng.integers(1, 24))
-        lda = K + 4 * int(rng.integers(0, 3))
+        K = 16 * int(rng.integers(1, 24)) if rng.random() < 0.6 else int(rng.integers(1, 380))
+        lda = -(-K // 4) * 4 + 4 * int(rng.integers(0, 3))
         aligned = rng.random() < 0.4  # else the shifted form (on the 128 tiles)
         ldb = (-(-N // 4) * 4 + 4 * int(rng.integers(0, 2))) if aligned else N + int(rng.integers(0, 8))
         ldc = N + int(rng.integers(0, 5))
