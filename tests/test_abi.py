@@ -257,6 +257,11 @@ def test_tune_reset_and_untuned_plans():
     (384, 14161, 1152, dict(bm="128", waves="2x4", load="shifted", vecB="0", streamk="256",
                             dp="256")),
     (256, 43265, 1152, dict(bm="128", waves="2x2", load="shifted", streamk="0")),
+    # the twelve-slab ring with a K tail, and shifted
+    (1000, 1000, 1000, dict(bm="64", occ="1", load="direct", streamk="0")),
+    (1000, 1001, 1024, dict(bm="64", occ="1", load="shifted", streamk="0")),
+    # K % 16 != 0: no direct-load stream-K
+    (384, 14161, 1156, dict(streamk="0")),
 ])
 def test_selector_choices(M, N, K, expect):
     """The cost model's choices on the configurations, as measured best on
