@@ -276,3 +276,16 @@ def test_valu_tile_choice():
     part-empty last round of resident workgroups."""
     assert plan(5120, 5120, 5120, variant=sg.SGEMM_VARIANT_VALU)["bm"] == "160"
     assert plan(4096, 4096, 4096, variant=sg.SGEMM_VARIANT_VALU)["bm"] == "128"
+
+
+def test_k_tail_plans():
+    """Direct-load one-tile kernels take any K; the stream-K ones only K a
+    multiple of 16, so a forced stream-K variant with a K tail runs the
+    register-staged stream-K kernel."""
+    assert plan(300, 200, 1000, variant=sg.SGEMM_VARIANT_MFMA_TILE + 1)["load"] == "direct"
+    assert plan(300, 200, 1000, variant=sg.SGEMM_VARIANT_STREAMK_TILE + 1)["load"] == "regs"
+    assert plan(300, 200, 1008, variant=sg.SGEMM_VARIANT_STREAMK_TILE + 1)["load"] == "direct"
+    assert plan(300, 201, 1000, variant=sg.SGEMM_VARIANT_MFMA_TILE + 1)["load"] == "shifted"
+    assert plan(300, 200, 7, variant=sg.SGEMM_VARIANT_MFMA_TILE + 6)["load"] == "direct"
+    # A rows not 16-byte aligned: no direct load
+    assert plan(300, 200, 1000, variant=sg.SGEMM_VARIANT_MFMA_TILE + 1, lda=1001)["load"] == "regs"
