@@ -286,6 +286,6 @@ def test_k_tail_plans():
     assert plan(300, 200, 1000, variant=sg.SGEMM_VARIANT_STREAMK_TILE + 1)["load"] == "regs"
     assert plan(300, 200, 1008, variant=sg.SGEMM_VARIANT_STREAMK_TILE + 1)["load"] == "direct"
     assert plan(300, 201, 1000, variant=sg.SGEMM_VARIANT_MFMA_TILE + 1)["load"] == "shifted"
-    assert plan(300, 200, 7, variant=sg.SGEMM_VARIANT_MFMA_TILE + 6)["load"] == "direct"
+    assert plan(300, 200, 7, variant=sg.SGEMM_VARIANT_MFMA_TILE + 6, lda=8)["load"] == "direct"
     # A rows not 16-byte aligned: no direct load
     assert plan(300, 200, 1000, variant=sg.SGEMM_VARIANT_MFMA_TILE + 1, lda=1001)["load"] == "regs"
