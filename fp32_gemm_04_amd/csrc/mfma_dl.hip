@@ -6,6 +6,8 @@
 
 namespace sgemm {
 
+// The 160 x 160 tile has no shifted form: with its four extra registers it
+// spills.
 KernelFn direct_kernel(int bm, int bn, int wm, int wn, int wpe, bool shifted)
 {
     if (shifted) {
@@ -15,6 +17,8 @@ KernelFn direct_kernel(int bm, int bn, int wm, int wn, int wpe, bool shifted)
             return mfma_dl_kernel<128, 128, 2, 4, 2, 3, true>;
         if (bm == 128 && bn == 128 && wm == 2 && wn == 2 && wpe == 2)
             return mfma_dl_kernel<128, 128, 2, 2, 2, 3, true>;
+        if (bm == 64 && bn == 256 && wm == 1 && wn == 4 && wpe == 2)
+            return mfma_dl_kernel<64, 256, 1, 4, 2, 3, true>;
         return nullptr;
     }
     if (bm == 64 && bn == 64 && wm == 2 && wn == 2 && wpe == 1)
@@ -37,6 +41,8 @@ SkKernelFn direct_sk_kernel(int bm, int bn, int wm, int wn, int wpe, bool shifte
             return mfma_dl_sk_kernel<128, 128, 2, 4, 2, 3, true>;
         if (bm == 128 && bn == 128 && wm == 2 && wn == 2 && wpe == 2)
             return mfma_dl_sk_kernel<128, 128, 2, 2, 2, 3, true>;
+        if (bm == 64 && bn == 256 && wm == 1 && wn == 4 && wpe == 2)
+            return mfma_dl_sk_kernel<64, 256, 1, 4, 2, 3, true>;
         return nullptr;
     }
     if (bm == 64 && bn == 64 && wm == 2 && wn == 2 && wpe == 1)

@@ -257,8 +257,8 @@ def test_direct_load_path_uniform(variant):
 
 
 # B rows that are not 16-byte aligned (ldb % 4 != 0 or a B base off
-# 16-byte alignment) with A aligned and K % 16 == 0: the 128 x 128 tiles and
-# the 64 x 64 ring take the shifted direct-load form, whose row misalignment
+# 16-byte alignment) with A aligned and K % 16 == 0: the 128 x 128, 64 x 256
+# and 64 x 64 ring tiles take the shifted direct-load form, whose row misalignment
 # d = 0..3 varies from row to row (ldb % 4 = 1, 2, 3) and with the base
 # offset.  Border tiles
 # (ragged M and N) run the same body with clamped sources and masked stores;
@@ -266,7 +266,7 @@ def test_direct_load_path_uniform(variant):
 # reaches C.
 SHIFTED_SHAPES = [(128, 128, 16), (256, 257, 32), (257, 389, 48), (384, 1001, 64),
                   (130, 263, 80), (384, 1041, 320)]
-SHIFTED_FAMILIES = [17, 22, 23, 49, 54, 55]
+SHIFTED_FAMILIES = [17, 20, 22, 23, 49, 52, 54, 55]
 
 
 @pytest.mark.parametrize("variant", [0] + SHIFTED_FAMILIES)
