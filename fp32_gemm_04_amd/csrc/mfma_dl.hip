@@ -12,7 +12,7 @@ KernelFn direct_kernel(int bm, int bn, int wm, int wn, int wpe, bool shifted)
 {
     if (shifted) {
         if (bm == 64 && bn == 64 && wm == 2 && wn == 2 && wpe == 1)
-            return mfma_dl_kernel<64, 64, 2, 2, 1, 12, true>;
+            return mfma_dl_kernel<64, 64, 2, 2, 1, 4, true>;
         if (bm == 128 && bn == 128 && wm == 2 && wn == 4 && wpe == 2)
             return mfma_dl_kernel<128, 128, 2, 4, 2, 3, true>;
         if (bm == 128 && bn == 128 && wm == 2 && wn == 2 && wpe == 2)
@@ -22,7 +22,7 @@ KernelFn direct_kernel(int bm, int bn, int wm, int wn, int wpe, bool shifted)
         return nullptr;
     }
     if (bm == 64 && bn == 64 && wm == 2 && wn == 2 && wpe == 1)
-        return mfma_dl_kernel<64, 64, 2, 2, 1, 12>;
+        return mfma_dl_kernel<64, 64, 2, 2, 1, 4>;
     if (bm == 128 && bn == 128 && wm == 2 && wn == 4 && wpe == 2)
         return mfma_dl_kernel<128, 128, 2, 4, 2, 3>;
     if (wpe != 2) return nullptr;
@@ -36,7 +36,7 @@ SkKernelFn direct_sk_kernel(int bm, int bn, int wm, int wn, int wpe, bool shifte
 {
     if (shifted) {
         if (bm == 64 && bn == 64 && wm == 2 && wn == 2 && wpe == 1)
-            return mfma_dl_sk_kernel<64, 64, 2, 2, 1, 12, true>;
+            return mfma_dl_sk_kernel<64, 64, 2, 2, 1, 4, true>;
         if (bm == 128 && bn == 128 && wm == 2 && wn == 4 && wpe == 2)
             return mfma_dl_sk_kernel<128, 128, 2, 4, 2, 3, true>;
         if (bm == 128 && bn == 128 && wm == 2 && wn == 2 && wpe == 2)
@@ -46,7 +46,7 @@ SkKernelFn direct_sk_kernel(int bm, int bn, int wm, int wn, int wpe, bool shifte
         return nullptr;
     }
     if (bm == 64 && bn == 64 && wm == 2 && wn == 2 && wpe == 1)
-        return mfma_dl_sk_kernel<64, 64, 2, 2, 1, 12>;
+        return mfma_dl_sk_kernel<64, 64, 2, 2, 1, 4>;
     if (bm == 128 && bn == 128 && wm == 2 && wn == 4 && wpe == 2)
         return mfma_dl_sk_kernel<128, 128, 2, 4, 2, 3>;
     if (wpe != 2) return nullptr;

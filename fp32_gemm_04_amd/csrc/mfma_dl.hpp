@@ -51,8 +51,9 @@
 // A slab's loads are issued about NBUF - 1.5 slabs before its operands are
 // read.  Three buffers suit tiles of 128 and 160, whose slabs take long
 // enough to cover the load latency; a 64 x 64 slab is 16 MFMAs per wave,
-// and with one tile per CU its kernel keeps twelve buffers (96 KB) so that
-// ten slabs are in flight.  The spacing matters: issued back to back right after the
+// and with one tile per CU its kernel keeps four buffers (three to five
+// measured alike; eight, twelve and sixteen slower, more loads ahead of the
+// first slab).  The spacing matters: issued back to back right after the
 // barrier, reads and loads stall the wave's MFMA issue (measured at 5120^3:
 // 125 TFLOPS clustered, 140 with reads and loads spread over the second
 // half, 143 with the loads moved to the first half).

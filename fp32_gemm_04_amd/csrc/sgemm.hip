@@ -151,9 +151,9 @@ int sk_dmode(int dmode, int K) { return K % 16 == 0 ? dmode : kDirectNone; }
 // The 64 x 64 tile with a three-stage pipeline at two workgroups per CU is
 // faster than the four-per-CU entry when a CU has one tile (1024^3: 27.6
 // against 31.1 us), slower when it has several, which its lower efficiency
-// encodes.  The last entry is the 64 x 64 direct-load tile with a twelve-slab
-// ring (96 KB of LDS, one workgroup per CU): with one tile per CU it keeps
-// ten slabs of loads in flight (1024^3: 24.3 against 27.6 us; 768^3: 19.6
+// encodes.  The last entry is the 64 x 64 direct-load tile with a four-slab
+// ring (one workgroup per CU; twelve slabs measured 6% slower, 1024^3: 24.3
+// against 22.8 us) and with one tile per CU (1024^3: 22.8 against 27.6 us; 768^3: 18.1
 // against 22.5).  Its register-staged kernels (the two-per-CU build) are
 // only run when forced: its efficiency of 0 keeps the selector off them.
 // The 128 x 128 direct-load tile with eight waves (two per SIMD, 64 x 32

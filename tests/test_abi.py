@@ -240,7 +240,7 @@ def test_tune_reset_and_untuned_plans():
 
 
 @pytest.mark.parametrize("M,N,K,expect", [
-    # one 64 x 64 tile per CU through the twelve-slab ring
+    # one 64 x 64 tile per CU through the four-slab ring
     (1024, 1024, 1024, dict(bm="64", bn="64", waves="2x2", occ="1", load="direct", streamk="0")),
     # one 128 x 128 tile per CU with eight waves
     (2048, 2048, 2048, dict(bm="128", waves="2x4", occ="1", load="direct", streamk="0")),
@@ -257,7 +257,7 @@ def test_tune_reset_and_untuned_plans():
     (384, 14161, 1152, dict(bm="128", waves="2x4", load="shifted", vecB="0", streamk="256",
                             dp="256")),
     (256, 43265, 1152, dict(bm="128", waves="2x2", load="shifted", streamk="0")),
-    # the twelve-slab ring with a K tail, and shifted
+    # the four-slab ring with a K tail, and shifted
     (1000, 1000, 1000, dict(bm="64", occ="1", load="direct", streamk="0")),
     (1000, 1001, 1024, dict(bm="64", occ="1", load="shifted", streamk="0")),
     # K % 16 != 0: no direct-load stream-K
