@@ -8,24 +8,27 @@ HBM before timing starts.  The line printed also carries:
     dense fp32 matrix peak, from HIP events around the timed launches, and
     the HBM traffic per launch measured with rocprofv3 counters when the
     stored counter summary matches the current kernel sources;
-  * cpu_baseline: the CPU reference timed on the host cores on a bounded
-    sample of the same product (the first rows of C);
+  * parity: the whole output of one more launch of the headline compared
+    with the CPU reference, element by element (max err/tol, pass);
+  * cpu_baseline: the CPU reference's wall time on the host cores for that
+    same whole product (the reference the parity check uses);
   * squares: 256^3 (alpha 1, beta 0), 1024^3 (alpha 1, beta 0, C preloaded)
     and every point of the square sweep 256 ... 5120 step 256 (alpha 1.5,
-    beta 0.5), each timed like the headline, launches back to back;
+    beta 0.5), each timed like the headline, launches back to back, and
+    each with its own parity check and CPU reference time;
   * device_copy: a plain device-to-device copy's bandwidth, the measured
     ceiling for mixed read and write traffic;
   * im2col: the six convolution-as-GEMM shapes, each timed back to back over
     rotating copies of its operands (and, for comparison, one launch at a
     time after a cache flush), with TFLOPS and the HBM bandwidth the
-    algorithmic bytes imply;
+    algorithmic bytes imply, a parity check and the CPU reference's time;
   * valu_comparison and ladder: the vector-FMA kernels on the headline
     workload, the register-tile comparison kernel and each rung of the
     pages' SIMT optimisation ladder (naive ... double-buffered);
     ladder_im2col: the rungs that match page 2's five kernels on its six
     im2col shapes.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-im2col]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-check] [--no-im2col]
                        [--no-valu] [--no-ladder] [--no-squares]
 """
 from __future__ import annotations
@@ -141,28 +144,60 @@ def device_copy(stream):
             "frac_hbm_peak": round(2 * n * 4 / sec / 1e9 / PEAK_HBM_GBPS, 4)}
 
 
-def cpu_baseline(case, A, B, C, budget_s):
-    """Time the CPU reference on the first R rows of the product."""
+def verify(sg, case, call_args, A, B, C, dC, stream, lib=None):
+    """Parity of the launch configuration just timed, and the CPU reference's
+    own time on the same product.
+
+    C is reset to its initial contents (NaN where the case does not preload
+    C: beta is 0 there, so C must not be read), the library runs the product
+    once, and every element of the output is compared with the CPU
+    reference: |gpu - ref| <= 1e-5 * (|alpha| * sum|a*b| + |beta*c|) + 1e-6.
+    The reference call is timed with the host wall clock; it computes the
+    whole product, sum|a*b| included, on every host core OpenMP is given."""
+    import torch
     import oracle
-    lib = oracle.load()
+    lib = lib or oracle.load()
+    if C is None:
+        dC.fill_(float("nan"))
+    else:
+        dC.copy_(torch.from_numpy(C))
+    torch.cuda.synchronize()
+    rc = sg.sgemm_f32(*call_args)
+    if rc != 0:
+        raise RuntimeError(sg.sgemm_status_string(rc))
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy()
+    t0 = time.perf_counter()
+    ref, absdot = oracle.sgemm(A, B, C, case.alpha, case.beta, with_absdot=True, lib=lib)
+    secs = time.perf_counter() - t0
+    tol = oracle.tolerance(case.alpha, case.beta, absdot, C)
+    del absdot
+    err = np.abs(out.astype(np.float64) - ref.astype(np.float64))
+    bits = bool(np.array_equal(out.view(np.uint32), ref.view(np.uint32)))
+    ratio = err / tol
+    del err, tol
+    worst = float(np.nanmax(ratio)) if ratio.size else 0.0
+    ok = bool(np.all(ratio <= 1.0))  # NaN fails
+    del ratio
+    parity = {"elements": int(out.size), "pass": ok, "max_err_over_tol": round(worst, 4),
+              "bit_identical_to_reference": bits}
     threads = oracle.num_threads(lib)
-    rows = max(1, min(case.M, threads))
-    while True:
-        t0 = time.perf_counter()
-        oracle.sgemm(A[:rows], B, None if C is None else C[:rows], case.alpha, case.beta,
-                     with_absdot=False, lib=lib)
-        dt = time.perf_counter() - t0
-        if dt >= budget_s / 2 or rows >= case.M:
-            break
-        rows = min(case.M, max(rows * 2, int(rows * budget_s * 0.8 / max(dt, 1e-3))))
-    flops = 2.0 * rows * case.N * case.K
-    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+    cpu = {"s": round(secs, 3), "tflops": round(case.flops / secs / 1e12, 5),
+           "threads": threads, "kind": "oracle", "work": "whole product with sum|a*b|"}
+    return parity, cpu
+
+
+def cpu_baseline(case, cpu):
+    """The CPU reference's time on the headline product (whole product,
+    measured by verify() in the same run), as the cpu_baseline object."""
+    return {"value": cpu["tflops"], "unit": "TFLOPS", "cores": cpu["threads"], "kind": "oracle",
             "cpu_model": cpu_model(),
-            "sample": "first %d of %d rows of C for M=N=K=%d, alpha=%g, beta=%g (%.1f s)"
-                      % (rows, case.M, case.M, case.alpha, case.beta, dt)}
+            "sample": "the whole %dx%dx%d product (alpha=%g, beta=%g) with its per-element "
+                      "sum|a*b|, %.1f s" % (case.M, case.N, case.K, case.alpha, case.beta,
+                                            cpu["s"])}
 
 
-def bench_squares(sg, stream):
+def bench_squares(sg, stream, check=True, known=None):
     """The square configurations: 256^3, 1024^3 and the sweep 256 ... 5120.
     Each size runs back to back for about 50 ms (clocks up, the launch
     pipeline full), then a timed run of about 20 ms of launches between two
@@ -172,7 +207,7 @@ def bench_squares(sg, stream):
     out = []
     for case in [workloads.SMALL, workloads.SQUARE1024] + workloads.SWEEP:
         log("square", case.name)
-        _, _, _, dA, dB, dC = device_operands(case)
+        A, B, C, dA, dB, dC = device_operands(case)
         args = (case.M, case.N, case.K, case.alpha, dA.data_ptr(), case.K, dB.data_ptr(),
                 case.N, case.beta, dC.data_ptr(), case.N, stream.cuda_stream)
 
@@ -195,17 +230,25 @@ def bench_squares(sg, stream):
         steps = int(min(2000, max(10, 0.02 / once)))
         ms = time_steps(step, steps, 0, stream)
         tflops = case.flops / (ms * 1e-3) / 1e12
-        out.append({"shape": [case.M, case.N, case.K], "alpha": case.alpha, "beta": case.beta,
-                    "steps": steps, "us": round(ms * 1e3, 2), "tflops": round(tflops, 2),
-                    "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4),
-                    "kernel": sg.sgemm_plan(0, case.M, case.N, case.K, case.K, case.N, case.N,
-                                            case.alpha, cus)[1]})
+        entry = {"shape": [case.M, case.N, case.K], "alpha": case.alpha, "beta": case.beta,
+                 "steps": steps, "us": round(ms * 1e3, 2), "tflops": round(tflops, 2),
+                 "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4),
+                 "kernel": sg.sgemm_plan(0, case.M, case.N, case.K, case.K, case.N, case.N,
+                                         case.alpha, cus)[1]}
+        if check and known and case.name in known:  # the headline, verified already
+            entry["parity"], entry["cpu"] = known[case.name]
+        elif check:
+            log("verify", case.name)
+            entry["parity"], entry["cpu"] = verify(sg, case, args, A, B, C, dC, stream)
+        if check:
+            entry["gpu_over_cpu"] = round(tflops / entry["cpu"]["tflops"], 1)
+        out.append(entry)
         del dA, dB, dC
         torch.cuda.empty_cache()
     return out
 
 
-def bench_im2col(sg, stream, reps):
+def bench_im2col(sg, stream, reps, check=True):
     """Each im2col shape, timed two ways.
 
     `us` (the figure the fractions use): the steady state of back-to-back
@@ -229,7 +272,7 @@ def bench_im2col(sg, stream, reps):
     out = []
     for case in workloads.SKINNY + workloads.MID:
         log("im2col", case.name)
-        _, _, _, dA, dB, dC = device_operands(case)
+        A, B, C, dA, dB, dC = device_operands(case)
         footprint = 4 * (case.M * case.K + case.K * case.N + case.M * case.N)
         nset = max(2, -(-1600 * 1024 * 1024 // footprint))
         sets = [(dA, dB, dC)] + [(dA.clone(), dB.clone(), dC.clone()) for _ in range(nset - 1)]
@@ -291,6 +334,11 @@ def bench_im2col(sg, stream, reps):
         gbps = case.alg_bytes / (ms * 1e-3) / 1e9
         roof_us = max(case.alg_bytes / (PEAK_HBM_GBPS * 1e9), case.flops / (PEAK_FP32_TFLOPS * 1e12)) * 1e6
         _, plan = sg.sgemm_plan(0, case.M, case.N, case.K, case.K, case.N, case.N, case.alpha, cus)
+        entry = {}
+        if check:
+            log("verify", case.name)
+            entry["parity"], entry["cpu"] = verify(sg, case, calls[0], A, B, C, dC, stream)
+            entry["gpu_over_cpu"] = round(tflops / entry["cpu"]["tflops"], 1)
         out.append({"shape": [case.M, case.N, case.K], "us": round(ms * 1e3, 2),
                     "launches": n, "operand_sets": nset,
                     "tflops": round(tflops, 2), "hbm_gbps": round(gbps, 1),
@@ -301,7 +349,7 @@ def bench_im2col(sg, stream, reps):
                     "frac_roofline_single_flushed": round(roof_us / (ms_single * 1e3), 4),
                     "us_tuned": round(ms_tuned * 1e3, 2), "tuned_variant": tuned_variant,
                     "frac_roofline_tuned": round(roof_us / (ms_tuned * 1e3), 4),
-                    "kernel": plan})
+                    "kernel": plan, **entry})
         del dA, dB, dC, sets, calls
         torch.cuda.empty_cache()
     return out
@@ -396,10 +444,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-reference baseline")
+    ap.add_argument("--no-check", "--no-cpu", dest="no_check", action="store_true",
+                    help="skip the parity checks against the CPU reference and its timing")
     ap.add_argument("--no-im2col", action="store_true", help="skip the im2col shapes")
     ap.add_argument("--im2col-reps", type=int, default=20)
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU reference work")
     ap.add_argument("--variant", type=int, default=0, help="force a kernel family (tuning)")
     ap.add_argument("--no-valu", action="store_true", help="skip the VALU-kernel comparison")
     ap.add_argument("--no-ladder", action="store_true", help="skip the SIMT-ladder table")
@@ -444,6 +492,13 @@ def main():
         if rc != 0:
             raise RuntimeError(sg.sgemm_status_string(rc))
 
+    # Clocks up before the counted warm-up: the inputs were just drawn on the
+    # host while the GPU sat idle.  About 0.3 s of back-to-back launches.
+    t_end = time.perf_counter() + 0.3
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     log("timing %d steps after %d warmup" % (args.steps, args.warmup))
     ms = time_steps(step, args.steps, args.warmup, stream)
     tflops = case.flops / (ms * 1e-3) / 1e12
@@ -485,14 +540,19 @@ def main():
     if not args.no_ladder:
         result["ladder"] = bench_ladder(sg, case, call_args, stream, tflops)
         result["ladder_im2col"] = bench_ladder_im2col(sg, stream)
+    known = {}
+    if not args.no_check and args.variant == 0:
+        log("verify the headline; CPU reference time")
+        parity, cpu = verify(sg, case, call_args, A, B, C, dC, stream)
+        result["parity"] = parity
+        result["cpu_baseline"] = cpu_baseline(case, cpu)
+        known[case.name] = (parity, cpu)
+    del A, B, C
     if not args.no_squares:
-        result["squares"] = bench_squares(sg, stream)
+        result["squares"] = bench_squares(sg, stream, check=not args.no_check, known=known)
     if not args.no_im2col:
         result["device_copy"] = device_copy(stream)
-        result["im2col"] = bench_im2col(sg, stream, args.im2col_reps)
-    if not args.no_cpu:
-        log("cpu baseline")
-        result["cpu_baseline"] = cpu_baseline(case, A, B, C, args.cpu_budget)
+        result["im2col"] = bench_im2col(sg, stream, args.im2col_reps, check=not args.no_check)
     print(json.dumps(result), flush=True)
     return 0
 

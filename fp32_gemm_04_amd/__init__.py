@@ -27,6 +27,9 @@ SGEMM_LADDER_RUNGS = 8
 LADDER_RUNG_NAMES = ("naive", "coalesced", "lds", "tile1d", "tile2d", "regcache", "vec4", "dbuf")
 SGEMM_ERR_BAD_VARIANT = -100
 SGEMM_ERR_VARIANT_SHAPE = -101
+SGEMM_ERR_WORKSPACE = -102
+SGEMM_ERR_NO_SLOT = -103
+SGEMM_ERR_CAPTURING = -104
 
 EXPORTS = ("sgemm_f32", "sgemm_f32_variant", "sgemm_plan", "sgemm_tune", "sgemm_tune_reset",
            "sgemm_num_mfma_tiles", "sgemm_status_string")

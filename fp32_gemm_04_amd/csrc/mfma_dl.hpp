@@ -43,8 +43,8 @@
 //
 // Pipeline of slab t (its operands already in registers):
 //   k-steps 0, 1: MFMAs, with the loads of slab t+NBUF-1 spread over them,
-//     into the buffer slab t-1 used (every wave took slab t-1's operands
-//     into registers before the previous barrier, so the buffer is free).
+//     into the buffer slab t-1 used (every wave's reads of slab t-1's
+//     operands had returned at the previous barrier, so the buffer is free).
 //   Wait until this wave's loads of slab t+1 have landed; barrier.
 //   k-steps 2, 3: MFMAs, with slab t+1's operand reads placed one per MFMA,
 //     in the order the next slab first uses them.
@@ -79,12 +79,16 @@ __device__ __forceinline__ void load_lds16(const float *src, uint32_t lds)
                  : "memory", "m0");
 }
 
-// Wait until at most N of this wave's vector memory loads are in flight,
-// then meet the workgroup at a barrier.
+// Wait until at most N of this wave's vector memory loads are in flight and
+// all of its LDS reads have returned, then meet the workgroup at a barrier.
+// The LDS wait makes the ring's reuse rule hold by construction: the loads
+// issued after barrier t overwrite the buffer of slab t, whose last operand
+// reads every wave issued before barrier t, so they must have completed
+// there (they were issued half a slab earlier, so the wait costs nothing).
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier()
 {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
 // Wait until at most min(k, KMAX) slabs of L loads each are in flight (none
@@ -262,7 +266,7 @@ __device__ __forceinline__ void mfma_dl_body(const GemmArgs &g, int m0, int n0, 
     auto slab = [&](auto P, int t, int buf) {
         constexpr int p = decltype(P)::value;
         // First half: the loads of slab t+NBUF-1 into the buffer slab t-1
-        // used (every wave passed barrier t-1 with its operands in registers).
+        // used (every wave's reads of it had returned at barrier t-1).
         const bool more = t >= 1 && t + NBUF - 1 < nslab;
         const uint32_t bb = buffer_bytes(buf == 0 ? NBUF - 1 : buf - 1);
         ksteps(0, 2, afs[p], bfs[p], [&](int n) {

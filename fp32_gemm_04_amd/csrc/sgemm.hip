@@ -2,8 +2,10 @@
 // kernel launches behind the C ABI declared in include/sgemm.h.
 //
 // Every kernel lives in the headers included below; this file only decides
-// which one runs and with what grid.  No call here allocates, frees, copies
-// or synchronises: work is queued on the caller's stream.
+// which one runs and with what grid.  sgemm_f32 and sgemm_f32_variant
+// allocate, free, copy and synchronise nothing: work is queued on the
+// caller's stream, and stream-K partial tiles go to a static device array
+// (`scratch`).  Only sgemm_tune allocates (a scratch C) and synchronises.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -345,13 +347,19 @@ SkPlan plan_streamk(const TileConfig &c, int M, int N, int K, int num_cus, int d
     return p;
 }
 
+// Bytes of one stream-K workspace slot (see `scratch` below).
+constexpr size_t kSkSlotBytes = (size_t)2 * 512 * 128 * 128 * sizeof(float);  // 64 MiB
+
 // The kernel a call runs: a tile config, one tile per workgroup or stream-K.
 struct Choice {
     const TileConfig *c;
     SkPlan sk;
 };
 
-Choice choose(int variant, int M, int N, int K, int num_cus, int dmode)
+// allow_sk false: no stream-K (a forced stream-K variant runs its tile one
+// tile per workgroup).  The selector never takes a stream-K plan whose
+// partial tiles would not fit a workspace slot.
+Choice choose(int variant, int M, int N, int K, int num_cus, int dmode, bool allow_sk = true)
 {
     Choice ch = {nullptr, {}};
     if (variant == SGEMM_VARIANT_VALU) {
@@ -360,6 +368,7 @@ Choice choose(int variant, int M, int N, int K, int num_cus, int dmode)
     }
     if (variant >= SGEMM_VARIANT_STREAMK_TILE) {
         ch.c = &kMfmaTiles[variant - SGEMM_VARIANT_STREAMK_TILE];
+        if (!allow_sk) return ch;
         ch.sk = plan_streamk(*ch.c, M, N, K, num_cus, dmode);
         ch.sk.use = ch.sk.args.workers > 0;
         return ch;
@@ -379,11 +388,11 @@ Choice choose(int variant, int M, int N, int K, int num_cus, int dmode)
     // Automatic stream-K only on the direct-load path: with unaligned
     // operands the register-staged segments run below the efficiency the
     // estimate assumes ((384, 14161, 1152) measured 4.5% slower with it).
-    if (sk_dmode(dmode, K) == kDirectNone || best < kSkMinCycles) return ch;
+    if (!allow_sk || sk_dmode(dmode, K) == kDirectNone || best < kSkMinCycles) return ch;
     for (const TileConfig &c : kMfmaTiles) {
         if (sk_dl_of(c, dmode) == nullptr) continue;
         SkPlan sp = plan_streamk(c, M, N, K, num_cus, dmode);
-        if (sp.args.workers > 0 && sp.cycles / kSkMargin < best) {
+        if (sp.args.workers > 0 && sp.ws_bytes <= kSkSlotBytes && sp.cycles / kSkMargin < best) {
             sp.use = true;
             ch = {&c, sp};
             best = sp.cycles / kSkMargin;
@@ -392,70 +401,104 @@ Choice choose(int variant, int M, int N, int K, int num_cus, int dmode)
     return ch;
 }
 
-// Stream-K workspaces, one per (device, stream): calls on one stream run in
-// order and share it; calls on different streams never do.  Allocated on
-// first need and grown.  At most kMaxWorkspacesPerDevice are kept per
-// device: a new stream beyond that takes over the least recently used one
-// (hipFree waits until the device has finished every queued use of it).
-constexpr int kMaxWorkspacesPerDevice = 16;
-struct Workspace {
-    int device;
-    hipStream_t stream;
-    void *ptr;
-    size_t bytes;
-    uint64_t last_use;
-};
-std::mutex g_ws_mutex;
-std::vector<Workspace> g_ws;
-uint64_t g_ws_clock = 0;
+// Stream-K partial tiles live in `scratch`, a device array that the HIP
+// runtime places when it loads this code object and keeps until the process
+// ends, one copy per device.  No call allocates, frees or synchronises for
+// it.  The array is split into kSkSlots slots, each large enough for every
+// stream-K plan the tile table makes on 256 CUs (2 x 512 workers x 128 x 128
+// floats).  A slot belongs to one stream at a time: calls on that stream use
+// it in stream order, and after each use the slot's event is recorded on the
+// stream.  A call on another stream may take a slot over only once that
+// event has completed (hipEventQuery: no wait), so no queued or running work
+// still reads it.  When every slot is busy on other streams, or the stream
+// is being captured into a graph (a replay could run anywhere, at any time),
+// the selector's choice runs without stream-K and a forced stream-K variant
+// returns an error.  Nothing in a slot needs clearing: the fixup reads only
+// partials that the same call's first kernel wrote.
+constexpr int kSkSlots = 4;
+constexpr int64_t kSkSlotFloats = (int64_t)(kSkSlotBytes / sizeof(float));
+static __device__ __align__(256) float scratch[kSkSlots * kSkSlotFloats];
 
-hipError_t workspace(hipStream_t stream, size_t bytes, float **out)
+constexpr int kMaxDevices = 64;
+
+struct SkSlot {
+    bool owned;          // owner holds a stream
+    hipStream_t owner;
+    hipEvent_t done;     // recorded on owner after each use
+};
+struct SkPool {
+    bool ready;          // set-up ran (successfully or not)
+    hipError_t error;    // set-up status; slots are unusable unless hipSuccess
+    float *base;         // this device's address of `scratch`
+    SkSlot slot[kSkSlots];
+};
+std::mutex g_pool_mutex;
+SkPool g_pool[kMaxDevices];
+
+// Once per device, with that device current, under g_pool_mutex: find this
+// device's copy of `scratch` and create the slots' events.  In host code the
+// name `scratch` is only a stand-in for the symbol; kernels get `base`.
+hipError_t pool_setup(int dev)
 {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace *slot = nullptr, *lru = nullptr;
-    int on_device = 0;
-    for (Workspace &w : g_ws) {
-        if (w.device != dev) continue;
-        ++on_device;
-        if (w.stream == stream) slot = &w;
-        if (lru == nullptr || w.last_use < lru->last_use) lru = &w;
+    SkPool &p = g_pool[dev];
+    if (p.ready) return p.error;
+    p.ready = true;
+    p.base = nullptr;
+    hipError_t e = hipGetSymbolAddress((void **)&p.base, HIP_SYMBOL(scratch));
+    for (int i = 0; i < kSkSlots && e == hipSuccess; ++i) {
+        p.slot[i].owned = false;
+        e = hipEventCreateWithFlags(&p.slot[i].done, hipEventDisableTiming);
     }
-    bool taken_over = false;
-    if (slot == nullptr && on_device >= kMaxWorkspacesPerDevice) {
-        slot = lru;  // taken over by this stream
-        slot->stream = stream;
-        taken_over = true;
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        p.base = nullptr;
     }
-    if (slot != nullptr) {
-        if (slot->bytes < bytes) {
-            // Work queued earlier may still read the old block; hipFree waits
-            // for the device to finish with it.
-            e = hipFree(slot->ptr);
-            if (e != hipSuccess) return e;
-            slot->ptr = nullptr;
-            slot->bytes = 0;
-            e = hipMalloc(&slot->ptr, bytes);
-            if (e != hipSuccess) return e;
-            slot->bytes = bytes;
-        } else if (taken_over) {
-            // Taken over without growing: the previous stream's queued work
-            // may still be using it, so wait for the device first.
-            e = hipDeviceSynchronize();
-            if (e != hipSuccess) return e;
+    p.error = e;
+    return e;
+}
+
+// Whether work queued on `stream` is being captured into a graph.  A failed
+// query counts as capturing.
+bool stream_capturing(hipStream_t stream)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return cs != hipStreamCaptureStatusNone;
+}
+
+// A slot for a stream-K call of `bytes` on `stream` (device dev), with
+// g_pool_mutex held by the caller: the stream's own slot, else one whose
+// last use has completed.  Returns 0 with *slot set, or the reason there is
+// none (an SGEMM_ERR_* value).
+int sk_slot(int dev, hipStream_t stream, size_t bytes, int *slot)
+{
+    if (bytes > kSkSlotBytes) return SGEMM_ERR_WORKSPACE;
+    if (dev < 0 || dev >= kMaxDevices || pool_setup(dev) != hipSuccess) return SGEMM_ERR_NO_SLOT;
+    if (stream_capturing(stream)) return SGEMM_ERR_CAPTURING;
+    SkPool &p = g_pool[dev];
+    for (int i = 0; i < kSkSlots; ++i)
+        if (p.slot[i].owned && p.slot[i].owner == stream) {
+            *slot = i;
+            return 0;
         }
-        slot->last_use = ++g_ws_clock;
-        *out = static_cast<float *>(slot->ptr);
-        return hipSuccess;
+    for (int i = 0; i < kSkSlots; ++i) {
+        bool idle = !p.slot[i].owned;
+        if (!idle) {
+            const hipError_t q = hipEventQuery(p.slot[i].done);
+            if (q != hipSuccess && q != hipErrorNotReady) (void)hipGetLastError();
+            idle = q == hipSuccess;
+        }
+        if (idle) {
+            p.slot[i].owned = true;
+            p.slot[i].owner = stream;
+            *slot = i;
+            return 0;
+        }
     }
-    void *ptr = nullptr;
-    e = hipMalloc(&ptr, bytes);
-    if (e != hipSuccess) return e;
-    g_ws.push_back({dev, stream, ptr, bytes, ++g_ws_clock});
-    *out = static_cast<float *>(ptr);
-    return hipSuccess;
+    return SGEMM_ERR_NO_SLOT;
 }
 
 // Argument checks of the C ABI (no HIP call).  Returns 0 or -p.
@@ -531,7 +574,6 @@ int launch_ladder(int rung, GemmArgs g, bool avec, bool bvec, hipStream_t stream
 }
 
 // Per-device compute-unit count, queried once per device.
-constexpr int kMaxDevices = 64;
 std::atomic<int> g_num_cus[kMaxDevices];
 
 hipError_t device_cus(int *cus)
@@ -550,7 +592,15 @@ hipError_t device_cus(int *cus)
     e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     if (n < 1) n = 1;
-    if (dev >= 0 && dev < kMaxDevices) g_num_cus[dev].store(n, std::memory_order_relaxed);
+    if (dev >= 0 && dev < kMaxDevices) {
+        // First call on this device: set up its stream-K workspace slots too
+        // (a failure only keeps stream-K off on this device).
+        {
+            std::lock_guard<std::mutex> lock(g_pool_mutex);
+            (void)pool_setup(dev);
+        }
+        g_num_cus[dev].store(n, std::memory_order_relaxed);
+    }
     *cus = n;
     return hipSuccess;
 }
@@ -731,6 +781,41 @@ void record_tuned(const TuneKey &key, int variant)
     g_tuned_count.store((int)g_tuned.size(), std::memory_order_release);
 }
 
+// The stream-K kernel and, when tiles are split, the fixup, on `stream`;
+// partial tiles go to slot `slot` of `pool` (none when no units are shared),
+// whose event is then recorded on the stream.  The caller holds
+// g_pool_mutex when a slot is passed.
+int launch_streamk(const Choice &ch, GemmArgs g, int cus, int dmode, bool avec, bool bvec,
+                   hipStream_t stream, SkPool *pool, int slot)
+{
+    const TileConfig *c = ch.c;
+    g.tiles_m = (int)ceil_div(g.M, c->bm);
+    g.tiles_n = (int)ceil_div(g.N, c->bn);
+    g.group_m = group_rows(*c, g.tiles_m, g.tiles_n, cus);
+    const int64_t blocks = (int64_t)g.tiles_m * g.tiles_n;
+    if (blocks > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
+    SkArgs sa = ch.sk.args;
+    sa.ws = pool != nullptr ? pool->base + (int64_t)slot * kSkSlotFloats : nullptr;
+    const SkKernelFn dfn = sk_dl_of(*c, sk_dmode(dmode, g.K));
+    const SkKernelFn fn = dfn ? dfn : c->sk_fn[avec][bvec];
+    hipLaunchKernelGGL(fn, dim3((unsigned)sa.workers), dim3(c->threads), 0, stream, g, sa);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && ch.sk.split_tiles > 0) {
+        hipLaunchKernelGGL(sk_fixup_kernel,
+                           dim3((unsigned)(blocks - sa.dp_tiles),
+                                (unsigned)ceil_div(c->bm * c->bn, kSkFixupElems)),
+                           dim3(256), 0, stream, g, sa, c->bm, c->bn);
+        e = hipGetLastError();
+    }
+    // Recorded even after a failed launch: the slot may hold queued work
+    // from the first kernel.
+    if (pool != nullptr) {
+        const hipError_t re = hipEventRecord(pool->slot[slot].done, stream);
+        if (e == hipSuccess) e = re;
+    }
+    return (int)e;
+}
+
 // use_tuned: an AUTO call takes the tuned variant of its key if there is one.
 int launch(int variant, int M, int N, int K, float alpha, const float *A, int lda,
            const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream,
@@ -798,44 +883,36 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A, int ld
         variant = SGEMM_VARIANT_VALU;
     }
     const int dmode = avec ? (bvec ? kDirectAligned : kDirectShifted) : kDirectNone;
-    const Choice ch = choose(variant, M, N, K, cus, dmode);
+    // A forced stream-K variant reports why it cannot have a workspace slot;
+    // the selector's choice (or a tuned one) then runs without stream-K.
+    const bool force_sk = variant >= SGEMM_VARIANT_STREAMK_TILE && !from_tuned;
+    Choice ch = choose(variant, M, N, K, cus, dmode);
+    if (ch.sk.use) {
+        std::unique_lock<std::mutex> lock(g_pool_mutex, std::defer_lock);
+        int slot = -1, why = 0;
+        int dev = 0;
+        if (ch.sk.ws_bytes > 0) {  // no shared units (whole rounds only): no workspace
+            lock.lock();
+            const hipError_t de = hipGetDevice(&dev);
+            if (de != hipSuccess) return (int)de;
+            why = sk_slot(dev, stream, ch.sk.ws_bytes, &slot);
+        }
+        if (why == 0)
+            return launch_streamk(ch, g, cus, dmode, avec, bvec, stream,
+                                  slot >= 0 ? &g_pool[dev] : nullptr, slot);
+        if (force_sk) return why;
+        lock.unlock();
+        ch = choose(variant, M, N, K, cus, dmode, false);
+    }
     const TileConfig *c = ch.c;
     g.tiles_m = (int)ceil_div(M, c->bm);
     g.tiles_n = (int)ceil_div(N, c->bn);
     g.group_m = group_rows(*c, g.tiles_m, g.tiles_n, cus);
     const int64_t blocks = (int64_t)g.tiles_m * g.tiles_n;
     if (blocks > 0x7fffffff) return (int)hipErrorInvalidConfiguration;
-    const int threads = c->threads;
-
-    // A forced stream-K variant reports a workspace failure; the selector's
-    // choice (or a tuned one) falls back to one tile per workgroup.
-    const bool force_sk = variant >= SGEMM_VARIANT_STREAMK_TILE && !from_tuned;
-    const SkPlan &sp = ch.sk;
-    if (sp.use) {
-        float *ws = nullptr;  // no shared units (whole rounds only): no workspace
-        const hipError_t we = sp.ws_bytes > 0 ? workspace(stream, sp.ws_bytes, &ws) : hipSuccess;
-        if (we != hipSuccess) {
-            if (force_sk) return (int)we;
-            (void)hipGetLastError();  // fall back to one tile per workgroup
-        } else {
-            SkArgs sa = sp.args;
-            sa.ws = ws;
-            const SkKernelFn dfn = sk_dl_of(*c, sk_dmode(dmode, K));
-            const SkKernelFn fn = dfn ? dfn : c->sk_fn[avec][bvec];
-            hipLaunchKernelGGL(fn, dim3((unsigned)sa.workers), dim3(threads), 0, stream, g, sa);
-            const hipError_t le = hipGetLastError();
-            if (le != hipSuccess) return (int)le;
-            if (sp.split_tiles > 0)
-                hipLaunchKernelGGL(sk_fixup_kernel,
-                                   dim3((unsigned)(blocks - sa.dp_tiles),
-                                        (unsigned)ceil_div(c->bm * c->bn, kSkFixupElems)),
-                                   dim3(256), 0, stream, g, sa, c->bm, c->bn);
-            return (int)hipGetLastError();
-        }
-    }
     const KernelFn dfn = dl_of(*c, dmode);
     const KernelFn fn = dfn ? dfn : c->fn[avec][bvec];
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), 0, stream, g);
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(c->threads), 0, stream, g);
     return (int)hipGetLastError();
 }
 
@@ -1006,14 +1083,14 @@ extern "C" int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, in
                                : dl_of(*c, dmode) != nullptr;
         std::snprintf(text, sizeof text,
                       "%s bm=%d bn=%d bk=%d waves=%dx%d occ=%d vecA=%d vecB=%d grid=%lld "
-                      "group=%d load=%s streamk=%d dp=%d split=%d",
+                      "group=%d load=%s streamk=%d dp=%d split=%d ws=%zu",
                       c->family, c->bm, c->bn, dl ? 16 : c->bk, c->wm, c->wn, c->occupancy,
                       (lda & 3) == 0,
                       (ldb & 3) == 0, (long long)tiles_m * tiles_n,
                       group_rows(*c, tiles_m, tiles_n, num_cus),
                       !dl ? "regs" : dmode == kDirectShifted ? "shifted" : "direct",
                       sp.use ? sp.args.workers : 0, sp.use ? sp.args.dp_tiles : 0,
-                      sp.use ? sp.split_tiles : 0);
+                      sp.use ? sp.split_tiles : 0, sp.use ? sp.ws_bytes : (size_t)0);
     }
     if (tuned != SGEMM_VARIANT_AUTO) {
         const size_t n = std::strlen(text);
@@ -1059,6 +1136,11 @@ extern "C" const char *sgemm_status_string(int status)
     case -13: return "invalid reps (< 1)";
     case SGEMM_ERR_BAD_VARIANT: return "unknown kernel variant";
     case SGEMM_ERR_VARIANT_SHAPE: return "the forced kernel variant cannot run this shape";
+    case SGEMM_ERR_WORKSPACE:
+        return "stream-K partial tiles would not fit a workspace slot of the library";
+    case SGEMM_ERR_NO_SLOT:
+        return "every stream-K workspace slot of the device is busy with other streams' work";
+    case SGEMM_ERR_CAPTURING: return "stream-K is not run on a stream being captured into a graph";
     default: break;
     }
     if (status > 0) return hipGetErrorString((hipError_t)status);

@@ -59,6 +59,11 @@ enum sgemm_variant {
 /* Status values other than 0 and the hipError_t codes. */
 #define SGEMM_ERR_BAD_VARIANT (-100)   /* variant value unknown */
 #define SGEMM_ERR_VARIANT_SHAPE (-101) /* variant cannot run this shape */
+/* A forced stream-K variant (SGEMM_VARIANT_STREAMK_TILE + i) that cannot have
+ * a workspace slot (see "Workspace" under sgemm_f32); nothing was queued: */
+#define SGEMM_ERR_WORKSPACE (-102) /* its partial tiles exceed a slot */
+#define SGEMM_ERR_NO_SLOT (-103)   /* every slot is busy with other streams' work */
+#define SGEMM_ERR_CAPTURING (-104) /* the stream is being captured into a graph */
 
 /*
  * sgemm_f32 -- C <- alpha * A * B + beta * C, all row-major fp32.
@@ -79,25 +84,30 @@ enum sgemm_variant {
  * queues kernels on `stream` and returns.  Results are visible once the
  * stream has been synchronised.
  *
- * Workspace: shapes that the selector runs stream-K (when whole tiles would
- * leave the last round of resident workgroups part-empty; see
- * SGEMM_VARIANT_STREAMK_TILE) keep partial tiles in a workspace of up to
- * 2 x (resident workgroups) x (tile floats), 64 MiB for 128 x 128 tiles on
- * 256 CUs.  The library owns one per (device, stream): the first call that
- * needs it allocates it with hipMalloc, a call that needs more frees and
- * reallocates it (hipFree waits for the device), and it is kept until the
- * process ends.  Calls on one stream share it, in stream order; calls on
- * different streams never do.  At most 16 are kept per device: a call on a
- * further stream takes over the least recently used one, after waiting for
- * the device to finish the work queued on it.  If the allocation fails the call runs one
- * tile per workgroup instead.  Make the first such call on a stream outside
- * graph capture.  Other shapes allocate nothing.
+ * Workspace: the call allocates, frees and synchronises nothing.  Shapes
+ * that the selector runs stream-K (when whole tiles would leave the last
+ * round of resident workgroups part-empty; see SGEMM_VARIANT_STREAMK_TILE)
+ * keep partial tiles in a workspace slot: 64 MiB of a 256 MiB static device
+ * array that the HIP runtime places when it loads the library's code and
+ * keeps until the process ends, one copy per device.  A slot serves one
+ * stream at a time, in stream order; after each use an event is recorded on
+ * that stream, and a call on another stream takes the slot over only once
+ * that event has completed (a query, not a wait).  So calls on different
+ * streams never share partials, whatever they overlap.  When all four slots
+ * of the device are busy with other streams' queued work, or when `stream`
+ * is being captured into a graph, the selector's choice runs one tile per
+ * workgroup instead (same result for integer data; within the accuracy
+ * bound below otherwise); forced stream-K variants return
+ * SGEMM_ERR_NO_SLOT or SGEMM_ERR_CAPTURING then.  A slot is tied to the
+ * stream handle: destroying a stream with stream-K work still queued and
+ * creating another that gets the same handle is not supported.
  *
  * Graph capture: the call only launches kernels on `stream` (no copies, no
- * memsets, no synchronisation), so it may be captured into a HIP graph and
- * replayed, once the stream's stream-K workspace exists (an earlier call of
- * a stream-K shape on that stream, outside capture).  A replay computes what
- * an eager call computes, bit for bit.  sgemm_tune may not be captured.
+ * memsets, no synchronisation, no allocation, no event records under
+ * capture), so it may be captured into a HIP graph and replayed on any
+ * stream; a captured call holds no pointer into the workspace.  A replay
+ * computes what an eager call of the captured plan computes, bit for bit.
+ * sgemm_tune may not be captured.
  *
  * Pointers need only float (4-byte) alignment; 16-byte aligned operands
  * with leading dimensions divisible by 4 take 128-bit load paths.
@@ -119,15 +129,19 @@ enum sgemm_variant {
  *
  * Accuracy: each element is a fp32 sum of fp32 products (matrix-core
  * accumulation) scaled by alpha plus beta times the old value; stream-K
- * adds the partial sums of a tile in a fixed order, so results repeat bit
- * for bit from call to call.  It is
+ * adds the partial sums of a tile in a fixed order, so a plan's results
+ * repeat bit for bit from call to call.  (A stream-K shape called while
+ * every workspace slot is busy on other streams, or under capture, runs
+ * one tile per workgroup, whose fp32 sums may round differently; with
+ * one stream doing stream-K work at a time, its plan never changes.)  It is
  * within 1e-5 * (|alpha| * sum_k |A(i,k) B(k,j)| + |beta C(i,j)|) + 1e-6 of
  * the exact result for data like the benchmark's, and exact for integer
  * data whose partial sums stay below 2^24.
  *
  * Thread safety: re-entrant; the shared state is a per-device cache of the
- * compute-unit count, filled once, the workspace table, under a mutex, and
- * the table of tuned choices (sgemm_tune), under another.
+ * compute-unit count, filled once, the workspace slots, under a mutex held
+ * while a stream-K call queues its kernels, and the table of tuned choices
+ * (sgemm_tune), under another.
  */
 int sgemm_f32(int M, int N, int K, float alpha, const float *A, int lda,
               const float *B, int ldb, float beta, float *C, int ldc,
@@ -154,11 +168,12 @@ int sgemm_f32_variant(int variant, int M, int N, int K, float alpha,
  * `num_cus` compute units, assuming 16-byte aligned base pointers.
  * Writes a NUL-terminated text such as
  *   "mfma bm=160 bn=160 bk=16 waves=2x2 occ=2 vecA=1 vecB=1 grid=1024 group=8
- *    load=direct streamk=0 dp=0 split=0"
+ *    load=direct streamk=0 dp=0 split=0 ws=0"
  * (on one line: tile, waves, workgroups per CU, 128-bit paths, tiles, raster
  * group, slab load path -- "direct" straight to LDS, "shifted" the same for
  * B rows not 16-byte aligned, "regs" through registers -- stream-K
- * workgroups, tiles run whole, tiles split)
+ * workgroups, tiles run whole, tiles split, workspace bytes of the partial
+ * tiles -- the plan of a call that finds a free workspace slot)
  * into buf (at most buflen bytes, truncated if needed).  The leading word
  * names the kernel: "none" (nothing to do), "scale" (K == 0 or alpha == 0),
  * "mfma", "valu", "skinny", "stream16" or "ladder".  Returns 0, or the same negative codes as
@@ -200,8 +215,8 @@ int sgemm_plan(int variant, int M, int N, int K, int lda, int ldb, int ldc,
  * 4).  sgemm_f32 and SGEMM_VARIANT_AUTO look the key up while any choice is
  * recorded; sgemm_plan(SGEMM_VARIANT_AUTO, ...) describes the tuned kernel
  * and appends " tuned=<variant>".  Forced variants are never redirected.
- * A tuned stream-K choice whose workspace cannot be allocated falls back
- * to one tile per workgroup, as the selector's choice does.
+ * A tuned stream-K choice that finds no free workspace slot (or a stream
+ * under capture) runs one tile per workgroup, as the selector's choice does.
  *
  * Quick-return problems (M, N or K zero, or alpha zero) are computed as by
  * sgemm_f32 and record nothing.  Returns the argument checks of sgemm_f32,

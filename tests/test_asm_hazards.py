@@ -22,18 +22,30 @@ the fall-through path (early_reads).
 """
 import os
 import re
-import shutil
 import subprocess
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-CSRC = os.path.join(ROOT, "fp32_gemm_04_amd", "csrc")
-HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S"]
+
+
+def _shipped_build():
+    """The library's own build description (fp32_gemm_04_amd/_build.py), loaded
+    by path so that importing it needs no built library: the scan compiles
+    exactly the translation units and flags that are shipped."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_sgemm_build_for_scan", os.path.join(ROOT, "fp32_gemm_04_amd", "_build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+_BUILD = _shipped_build()
+FLAGS = list(_BUILD.FLAGS) + ["--cuda-device-only", "-S"]
+CSRC = _BUILD.CSRC
+HIPCC = _BUILD.HIPCC
 
 SGPR = re.compile(r"\bs\[(\d+):(\d+)\]|\bs(\d+)\b")
 
@@ -212,10 +224,7 @@ def early_reads(asm):
     return found
 
 
-SOURCES = [
-    ("sgemm.hip", []),
-    ("mfma_dl.hip", ["-Xarch_device", "-mllvm=--misched=gcn-max-ilp"]),
-]
+SOURCES = [(name, list(extra)) for name, extra in _BUILD.SOURCES.items()]
 
 
 @pytest.fixture(scope="module")

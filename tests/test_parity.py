@@ -1,11 +1,12 @@
 """GPU parity: libsgemm against the CPU reference, element by element.
 
-Small and medium shapes (several tiles plus ragged tails) are compared in
-full; the full-size workloads (the 5120 sweep, the six im2col shapes) are
-compared at sampled elements the reference computes one by one, plus row
-and column checksums that cover every element.  Integer-valued inputs must
-match bit for bit; uniform inputs must satisfy
+Every output element of every workload is compared with the reference's own
+value for it: the small and medium shapes, every point of the square sweep
+(5120^3 included) and the six im2col shapes at their full sizes, each on
+uniform and on integer data.  Integer-valued inputs must match bit for bit;
+uniform inputs must satisfy
 |gpu - ref| <= 1e-5 * (|alpha| * sum_k |a_ik b_kj| + |beta c_ij|) + 1e-6.
+Bytes of C outside its M x N window must keep their NaN guard values.
 """
 import numpy as np
 import pytest
@@ -44,12 +45,13 @@ def _full_check(A, B, C, alpha, beta, variant=0, exact=False, **kw):
     return out
 
 
-# AUTO, VALU, SKINNY, the five forced MFMA tiles, the same five run
+# AUTO, MFMA (the tile kernel, tile chosen by shape), VALU, SKINNY, the
+# forced MFMA tiles, the same tiles run
 # stream-K (variant 48 + i), and the eight rungs of the pages' SIMT ladder
 # (variant 32 + r).
 NUM_TILES = 8  # entries of the MFMA tile table (checked against the library in test_abi)
 STREAMK_FAMILIES = [48 + i for i in range(NUM_TILES)]
-FAMILIES = ([0, 2, 3] + [16 + i for i in range(NUM_TILES)] + STREAMK_FAMILIES
+FAMILIES = ([0, 1, 2, 3] + [16 + i for i in range(NUM_TILES)] + STREAMK_FAMILIES
             + [32 + r for r in range(8)])
 
 
@@ -71,66 +73,37 @@ def test_square1024_with_c_preloaded(integer):
     _full_check(A, B, C, case.alpha, case.beta, exact=integer)
 
 
-def _sample_points(M, N, n, seed):
-    rng = np.random.default_rng(seed)
-    rows = np.concatenate([rng.integers(0, M, n), [0, 0, M - 1, M - 1], np.full(64, M - 1),
-                           rng.integers(0, M, 64)])
-    cols = np.concatenate([rng.integers(0, N, n), [0, N - 1, 0, N - 1], rng.integers(0, N, 64),
-                           np.full(64, N - 1)])
-    return rows, cols
-
-
-def _checksums(A, B, C_before, out, alpha, beta, chunk=1 << 20):
-    """Row and column sums of an integer-data result, exactly, in float64:
-    out @ 1 = alpha * A @ (B @ 1) + beta * C @ 1, and likewise for columns.
-    Every element of the output enters one row sum and one column sum."""
-    A64 = A.astype(np.float64)
-    N = B.shape[1]
-    rows_expect = alpha * (A64 @ B.sum(axis=1, dtype=np.float64))
-    colsum_a = A64.sum(axis=0)
-    cols_expect = np.empty(N, np.float64)
-    for j in range(0, N, chunk):
-        cols_expect[j:j + chunk] = alpha * (colsum_a @ B[:, j:j + chunk].astype(np.float64))
-    if beta != 0.0:
-        rows_expect = rows_expect + beta * C_before.sum(axis=1, dtype=np.float64)
-        cols_expect = cols_expect + beta * C_before.sum(axis=0, dtype=np.float64)
-    assert np.array_equal(out.sum(axis=1, dtype=np.float64), rows_expect), "row checksum"
-    assert np.array_equal(out.sum(axis=0, dtype=np.float64), cols_expect), "column checksum"
-
-
-def _sampled_case(case, integer, npts=4096):
+def _full_size_case(case, integer):
+    """The whole M x N output of a workload against the reference's."""
     A, B, C = workloads.operands(case, integer)
     out, dC = run(A, B, C, case.alpha, case.beta, name=case.name)
-    rows, cols = _sample_points(case.M, case.N, npts, workloads.seed(case, 3))
-    ref, t = oracle.sgemm_points(A, B, C, case.alpha, case.beta, rows, cols)
-    got = out[rows, cols]
+    ref, t = oracle.sgemm(A, B, C, case.alpha, case.beta, with_absdot=not integer)
     if integer:
-        assert_bits_equal(got, ref, case.name)
-        _checksums(A, B, C, out, case.alpha, case.beta)
+        assert_bits_equal(out, ref, case.name)
+        say("%s integer: %d elements bit for bit" % (case.name, out.size))
     else:
-        cb = C[rows, cols] if C is not None else None
-        assert_within_tolerance(got, ref, t, case.alpha, case.beta, cb, case.name)
-    assert not np.isnan(out).any()
-    assert dC.outside_is_nan()
+        worst = assert_within_tolerance(out, ref, t, case.alpha, case.beta, C, case.name)
+        say("%s uniform: %d elements, max err/tol %.3g" % (case.name, out.size, worst))
+    assert dC.outside_is_nan(), "C written outside its M x N window"
 
 
 @pytest.mark.parametrize("case", workloads.SWEEP, ids=[c.name for c in workloads.SWEEP])
 def test_square_sweep_uniform(case):
-    _sampled_case(case, integer=False)
+    _full_size_case(case, integer=False)
 
 
 @pytest.mark.parametrize("case", workloads.SWEEP, ids=[c.name for c in workloads.SWEEP])
 def test_square_sweep_integer(case):
     # Exact for every n: partial sums of products of [-4, 4] integers stay
     # below 2^24 even at K = 5120, and 1.5x + 0.5c is dyadic.
-    _sampled_case(case, integer=True)
+    _full_size_case(case, integer=True)
 
 
 @pytest.mark.parametrize("integer", [False, True], ids=["uniform", "integer"])
 @pytest.mark.parametrize("case", workloads.SKINNY + workloads.MID,
                          ids=[c.name for c in workloads.SKINNY + workloads.MID])
 def test_im2col_shapes(case, integer):
-    _sampled_case(case, integer)
+    _full_size_case(case, integer)
 
 
 def test_im2col_shape_full_compare_small_n():

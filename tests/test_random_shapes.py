@@ -25,7 +25,8 @@ def _need_gpu():
 def _families():
     import fp32_gemm_04_amd as sg
     n = sg.sgemm_num_mfma_tiles()
-    return ([sg.SGEMM_VARIANT_AUTO, sg.SGEMM_VARIANT_VALU, sg.SGEMM_VARIANT_SKINNY]
+    return ([sg.SGEMM_VARIANT_AUTO, sg.SGEMM_VARIANT_MFMA, sg.SGEMM_VARIANT_VALU,
+             sg.SGEMM_VARIANT_SKINNY]
             + [sg.SGEMM_VARIANT_MFMA_TILE + i for i in range(n)]
             + [sg.SGEMM_VARIANT_STREAMK_TILE + i for i in range(n)]
             + [sg.SGEMM_VARIANT_LADDER + r for r in range(sg.SGEMM_LADDER_RUNGS)])

@@ -1,8 +1,9 @@
-"""Streams and threads: stream-K calls on different streams use different
-workspaces, a workspace grows when a later call needs more, and concurrent
-calls from two host threads give the same bits as the same calls made one at
-a time.  Stream-K sums partial tiles in a fixed order, so every comparison
-here is bit for bit."""
+"""Streams and threads: stream-K calls on different streams never share
+partial tiles (each stream holds one of the library's workspace slots, taken
+over only once its last use has completed), a slot serves calls of any size
+on its stream, and concurrent calls from two host threads give the same bits
+as the same calls made one at a time.  Stream-K sums partial tiles in a fixed
+order, so every comparison here is bit for bit."""
 import threading
 
 import numpy as np
@@ -67,18 +68,22 @@ def test_two_streams_concurrently():
     assert_bits_equal(C2.cpu().numpy(), ref2.cpu().numpy(), "stream b")
 
 
-def test_workspace_grows_on_one_stream():
-    """A stream-K call with small tiles, then one needing a larger workspace,
-    then the small one again, on one fresh stream: all match the reference."""
+def test_one_slot_serves_every_size_on_its_stream():
+    """Stream-K calls with small tiles, then larger ones, then the small ones
+    again, queued on one fresh stream without synchronising: each result
+    matches the reference."""
     import fp32_gemm_04_amd as sg
     s = torch.cuda.Stream()
-    for i, (variant, M, N, K) in enumerate([(53, 160, 300, 640), (48, 480, 1000, 1280),
+    jobs = []
+    for i, (variant, M, N, K) in enumerate([(53, 160, 300, 640), (49, 480, 1000, 1280),
                                             (53, 160, 300, 640)]):
         A, B, C = _operands(M, N, K, 820 + 10 * i)
         Cin = C.cpu().numpy()
-        say("workspace growth step %d: variant %d M=%d N=%d K=%d" % (i, variant, M, N, K))
+        say("one stream, step %d: variant %d M=%d N=%d K=%d" % (i, variant, M, N, K))
         _launch(sg, variant, A, B, C, 0.5, -1.0, s)
-        s.synchronize()
+        jobs.append((A, B, C, Cin))
+    s.synchronize()
+    for i, (A, B, C, Cin) in enumerate(jobs):
         ref, absdot = oracle.sgemm(A.cpu().numpy(), B.cpu().numpy(), Cin, 0.5, -1.0)
         tol = oracle.tolerance(0.5, -1.0, absdot, Cin)
         err = np.abs(C.cpu().numpy().astype(np.float64) - ref.astype(np.float64))
@@ -123,23 +128,84 @@ def test_two_host_threads():
         assert_bits_equal(C.cpu().numpy(), ref.cpu().numpy(), "thread %d" % j)
 
 
-def test_more_streams_than_kept_workspaces():
-    """Stream-K calls on 20 streams in turn (twice round), more than the 16
-    workspaces the library keeps per device: later streams take over the
-    least recently used ones, after the device has finished the work queued
-    on them.  Every result equals the one-stream run."""
+def _int_operands(M, N, K, seed):
+    A = workloads.integers(M, K, seed)
+    B = workloads.integers(K, N, seed + 1)
+    return A, B, torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+
+
+def test_more_streams_than_slots_auto():
+    """A shape the selector runs stream-K, called on 20 streams in turn (twice
+    round) without synchronising: the library holds four workspace slots per
+    device, so streams that find them all busy run one tile per workgroup.
+    On integer data every plan gives the reference's bits."""
     import fp32_gemm_04_amd as sg
-    variant, M, N, K = 49, 384, 1000, 1152
-    A, B, C0 = _operands(M, N, K, 860)
-    ref = C0.clone()
-    _launch(sg, variant, A, B, ref, 1.0, 0.0, torch.cuda.current_stream())
-    torch.cuda.synchronize()
+    M, N, K = 384, 3000, 1152
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = sg.sgemm_plan(0, M, N, K, K, N, N, 1.0, cus)[1]
+    assert " ws=0" not in plan and "streamk=0" not in plan, plan
+    A, B, dA, dB = _int_operands(M, N, K, 860)
+    ref, _ = oracle.sgemm(A, B)
     streams = [torch.cuda.Stream() for _ in range(20)]
-    outs = [torch.empty_like(C0) for _ in streams]
-    say("stream-K on 20 streams, two rounds")
+    outs = [torch.full((M, N), float("nan"), device="cuda") for _ in streams]
+    say("AUTO stream-K shape on 20 streams, two rounds")
     for _ in range(2):
         for s, C in zip(streams, outs):
-            _launch(sg, variant, A, B, C, 1.0, 0.0, s)
+            _launch(sg, 0, dA, dB, C, 1.0, 0.0, s)
     torch.cuda.synchronize()
     for i, C in enumerate(outs):
-        assert_bits_equal(C.cpu().numpy(), ref.cpu().numpy(), "stream %d" % i)
+        assert_bits_equal(C.cpu().numpy(), ref, "stream %d" % i)
+
+
+def test_forced_streamk_without_free_slot():
+    """A forced stream-K variant either runs (a slot was free or idle) or
+    returns SGEMM_ERR_NO_SLOT having queued nothing; once the device is idle,
+    a call on yet another stream takes an idle slot over and runs."""
+    import fp32_gemm_04_amd as sg
+    variant, M, N, K = 49, 384, 1000, 1152
+    A, B, dA, dB = _int_operands(M, N, K, 870)
+    ref, _ = oracle.sgemm(A, B)
+    streams = [torch.cuda.Stream() for _ in range(8)]
+    outs = [torch.full((M, N), float("nan"), device="cuda") for _ in streams]
+    say("forced stream-K on 8 streams without synchronising")
+    codes = []
+    for s, C in zip(streams, outs):
+        codes.append(sg.sgemm_f32_variant(variant, M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(),
+                                          N, 0.0, C.data_ptr(), N, s.cuda_stream))
+    torch.cuda.synchronize()
+    assert set(codes) <= {0, sg.SGEMM_ERR_NO_SLOT}, codes
+    assert codes[:4].count(0) >= 1
+    for i, (rc, C) in enumerate(zip(codes, outs)):
+        got = C.cpu().numpy()
+        if rc == 0:
+            assert_bits_equal(got, ref, "stream %d" % i)
+        else:
+            assert np.isnan(got).all(), "stream %d: a refused call wrote C" % i
+    s = torch.cuda.Stream()
+    C = torch.full((M, N), float("nan"), device="cuda")
+    say("forced stream-K on a ninth stream after the device went idle")
+    rc = sg.sgemm_f32_variant(variant, M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0,
+                              C.data_ptr(), N, s.cuda_stream)
+    assert rc == 0, sg.sgemm_status_string(rc)
+    s.synchronize()
+    assert_bits_equal(C.cpu().numpy(), ref, "ninth stream")
+
+
+def test_forced_streamk_beyond_a_slot_refuses():
+    """A forced stream-K plan whose partial tiles exceed a workspace slot (the
+    160 x 160 tile shared over 512 workers: 100 MiB) returns
+    SGEMM_ERR_WORKSPACE and queues nothing; sgemm_plan reports its bytes."""
+    import fp32_gemm_04_amd as sg
+    M, N, K = 480, 1000, 1280
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = sg.sgemm_plan(48, M, N, K, K, N, N, 1.0, cus)[1]
+    ws = int(dict(kv.split("=") for kv in plan.split()[1:])["ws"])
+    assert ws > 64 << 20, plan
+    A, B, dA, dB = _int_operands(M, N, K, 880)
+    C = torch.full((M, N), float("nan"), device="cuda")
+    say("forced 160 x 160 stream-K beyond a slot")
+    rc = sg.sgemm_f32_variant(48, M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0,
+                              C.data_ptr(), N, torch.cuda.current_stream().cuda_stream)
+    assert rc == sg.SGEMM_ERR_WORKSPACE, rc
+    torch.cuda.synchronize()
+    assert np.isnan(C.cpu().numpy()).all()
