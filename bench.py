@@ -50,7 +50,7 @@ import workloads  # noqa: E402
 METRIC = "SGEMM TFLOPS at 5120³ + im2col shapes; % of FP32 peak / HBM roofline"
 PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 matrix peak, and its fp32 vector peak
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_dl_5120.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
 def log(*a):
@@ -67,16 +67,20 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """Bytes per launch from the committed counter summary, or None if stale."""
+def stored_traffic(name):
+    """HBM bytes per call of configuration `name` from the committed counter
+    records (scaled FETCH_SIZE + WRITE_SIZE), or None if there is none or it
+    was taken on other kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
+            records = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != source_hash():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    for rec in records:
+        if rec.get("config") == name and rec.get("source_hash") == source_hash():
+            if "FETCH_SIZE_bytes" in rec and "WRITE_SIZE_bytes" in rec:
+                return round(rec["FETCH_SIZE_bytes"] + rec["WRITE_SIZE_bytes"])
+    return None
 
 
 def time_steps(fn, steps, warmup, stream):
@@ -197,11 +201,83 @@ def cpu_baseline(case, cpu):
                                             cpu["s"])}
 
 
+def square_timing(sg, args, stream):
+    """A square configuration's time per launch (ms) and launch count: back
+    to back for about 50 ms (clocks up, the launch pipeline full), then about
+    20 ms of launches between two HIP events, as for the headline."""
+    import torch
+
+    def step():
+        rc = sg.sgemm_f32(*args)
+        if rc != 0:
+            raise RuntimeError(sg.sgemm_status_string(rc))
+
+    step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    once = max(time.perf_counter() - t0, 1e-6)
+    t_end = time.perf_counter() + 0.05
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    steps = int(min(2000, max(10, 0.02 / once)))
+    return time_steps(step, steps, 0, stream), steps
+
+
+def im2col_operand_sets(case, dA, dB, dC, stream):
+    """Enough copies of the operands (at least 1.6 GB in all) that launches
+    over them in turn read their inputs from HBM; the calls' arguments."""
+    footprint = 4 * (case.M * case.K + case.K * case.N + case.M * case.N)
+    nset = max(2, -(-1600 * 1024 * 1024 // footprint))
+    sets = [(dA, dB, dC)] + [(dA.clone(), dB.clone(), dC.clone()) for _ in range(nset - 1)]
+    calls = [(case.M, case.N, case.K, case.alpha, a.data_ptr(), case.K, b.data_ptr(),
+              case.N, case.beta, c.data_ptr(), case.N, stream.cuda_stream) for a, b, c in sets]
+    return sets, calls
+
+
+def im2col_steady(sg, calls, stream, n=None):
+    """Steady-state time per launch (ms) over the operand sets in turn: about
+    0.1 s of back-to-back launches to bring the clocks up, then three runs of
+    about 0.15 s of launches between two HIP events; the median run, and the
+    launches per run."""
+    import torch
+    nset = len(calls)
+    rc = sg.sgemm_f32(*calls[0])
+    if rc != 0:
+        raise RuntimeError(sg.sgemm_status_string(rc))
+    t_end = time.perf_counter() + 0.1
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            sg.sgemm_f32(*calls[i % nset])
+            i += 1
+        torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    if n is None:
+        e0.record(stream)
+        for c in calls:
+            sg.sgemm_f32(*c)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        n = max(nset, int(0.15 / max(e0.elapsed_time(e1) * 1e-3 / nset, 1e-6)))
+    runs = []
+    for _ in range(3):
+        e0.record(stream)
+        for k in range(n):
+            sg.sgemm_f32(*calls[k % nset])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        runs.append(e0.elapsed_time(e1) / n)
+    return float(np.median(runs)), n
+
+
 def bench_squares(sg, stream, check=True, known=None):
-    """The square configurations: 256^3, 1024^3 and the sweep 256 ... 5120.
-    Each size runs back to back for about 50 ms (clocks up, the launch
-    pipeline full), then a timed run of about 20 ms of launches between two
-    HIP events, as for the headline."""
+    """The square configurations: 256^3, 1024^3 and the sweep 256 ... 5120,
+    each timed by square_timing."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = []
@@ -211,24 +287,7 @@ def bench_squares(sg, stream, check=True, known=None):
         args = (case.M, case.N, case.K, case.alpha, dA.data_ptr(), case.K, dB.data_ptr(),
                 case.N, case.beta, dC.data_ptr(), case.N, stream.cuda_stream)
 
-        def step():
-            rc = sg.sgemm_f32(*args)
-            if rc != 0:
-                raise RuntimeError(sg.sgemm_status_string(rc))
-
-        step()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        step()
-        torch.cuda.synchronize()
-        once = max(time.perf_counter() - t0, 1e-6)
-        t_end = time.perf_counter() + 0.05
-        while time.perf_counter() < t_end:
-            for _ in range(10):
-                step()
-            torch.cuda.synchronize()
-        steps = int(min(2000, max(10, 0.02 / once)))
-        ms = time_steps(step, steps, 0, stream)
+        ms, steps = square_timing(sg, args, stream)
         tflops = case.flops / (ms * 1e-3) / 1e12
         entry = {"shape": [case.M, case.N, case.K], "alpha": case.alpha, "beta": case.beta,
                  "steps": steps, "us": round(ms * 1e3, 2), "tflops": round(tflops, 2),
@@ -253,9 +312,8 @@ def bench_im2col(sg, stream, reps, check=True):
 
     `us` (the figure the fractions use): the steady state of back-to-back
     launches over enough copies of the operands (at least 1.6 GB in all) that
-    every launch reads its inputs from HBM, about 0.15 s of launches between
-    two HIP events, median of three such runs.  Each launch also pays for
-    writing back what the one before it left dirty in the caches.
+    every launch reads its inputs from HBM (im2col_steady).  Each launch also
+    pays for writing back what the one before it left dirty in the caches.
 
     `us_tuned`: the same steady state after sgemm_tune (the library's
     autotuner) chose the kernel for the shape; `tuned_variant` is its choice
@@ -273,40 +331,11 @@ def bench_im2col(sg, stream, reps, check=True):
     for case in workloads.SKINNY + workloads.MID:
         log("im2col", case.name)
         A, B, C, dA, dB, dC = device_operands(case)
-        footprint = 4 * (case.M * case.K + case.K * case.N + case.M * case.N)
-        nset = max(2, -(-1600 * 1024 * 1024 // footprint))
-        sets = [(dA, dB, dC)] + [(dA.clone(), dB.clone(), dC.clone()) for _ in range(nset - 1)]
-        calls = [(case.M, case.N, case.K, case.alpha, a.data_ptr(), case.K, b.data_ptr(),
-                  case.N, case.beta, c.data_ptr(), case.N, stream.cuda_stream) for a, b, c in sets]
-        rc = sg.sgemm_f32(*calls[0])
-        assert rc == 0, sg.sgemm_status_string(rc)
-        # Warm-up: the inputs were just drawn on the host, the GPU sat idle
-        # meanwhile and its clocks drop; a few launches are not enough for
-        # them to come back up.  Run the product back to back for ~0.1 s.
-        t_end = time.perf_counter() + 0.1
-        i = 0
-        while time.perf_counter() < t_end:
-            for _ in range(10):
-                sg.sgemm_f32(*calls[i % nset])
-                i += 1
-            torch.cuda.synchronize()
+        sets, calls = im2col_operand_sets(case, dA, dB, dC, stream)
+        nset = len(calls)
+        ms, n = im2col_steady(sg, calls, stream)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for c in calls:
-            sg.sgemm_f32(*c)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        n = max(nset, int(0.15 / max(e0.elapsed_time(e1) * 1e-3 / nset, 1e-6)))
-        runs = []
-        for _ in range(3):
-            e0.record(stream)
-            for k in range(n):
-                sg.sgemm_f32(*calls[k % nset])
-            e1.record(stream)
-            torch.cuda.synchronize()
-            runs.append(e0.elapsed_time(e1) / n)
-        ms = float(np.median(runs))
         single = []
         for _ in range(reps):
             flush.sum()  # evict the caches without leaving dirty lines behind
@@ -320,16 +349,8 @@ def bench_im2col(sg, stream, reps, check=True):
         # same steady-state timing with its choice; the table is reset after.
         rc, tuned_variant, _ = sg.sgemm_tune(*calls[0], 5)
         assert rc == 0, sg.sgemm_status_string(rc)
-        runs_tuned = []
-        for _ in range(3):
-            e0.record(stream)
-            for k in range(n):
-                sg.sgemm_f32(*calls[k % nset])
-            e1.record(stream)
-            torch.cuda.synchronize()
-            runs_tuned.append(e0.elapsed_time(e1) / n)
+        ms_tuned, _ = im2col_steady(sg, calls, stream, n)
         sg.sgemm_tune_reset()
-        ms_tuned = float(np.median(runs_tuned))
         tflops = case.flops / (ms * 1e-3) / 1e12
         gbps = case.alg_bytes / (ms * 1e-3) / 1e9
         roof_us = max(case.alg_bytes / (PEAK_HBM_GBPS * 1e9), case.flops / (PEAK_FP32_TFLOPS * 1e12)) * 1e6
@@ -349,7 +370,7 @@ def bench_im2col(sg, stream, reps, check=True):
                     "frac_roofline_single_flushed": round(roof_us / (ms_single * 1e3), 4),
                     "us_tuned": round(ms_tuned * 1e3, 2), "tuned_variant": tuned_variant,
                     "frac_roofline_tuned": round(roof_us / (ms_tuned * 1e3), 4),
-                    "kernel": plan, **entry})
+                    "kernel": plan, "traffic": stored_traffic(case.name), **entry})
         del dA, dB, dC, sets, calls
         torch.cuda.empty_cache()
     return out
@@ -416,6 +437,104 @@ def bench_ladder_im2col(sg, stream):
     return out
 
 
+def config_by_name(name):
+    for case in workloads.ALL:
+        if case.name == name:
+            return case
+    raise SystemExit("no configuration named %r (names: %s)"
+                     % (name, ", ".join(c.name for c in workloads.ALL)))
+
+
+def profile_config(sg, name, stream, min_launches=50):
+    """One configuration timed exactly as the full run times it (square_timing,
+    or im2col_steady over rotating operand sets), for a kernel-trace run of
+    its own.  The timed launches are the process's last library launches;
+    the line printed says how many there were and what the HIP events gave."""
+    import torch
+    case = config_by_name(name)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    _, _, _, dA, dB, dC = device_operands(case)
+    if case in workloads.SKINNY + workloads.MID:
+        sets, calls = im2col_operand_sets(case, dA, dB, dC, stream)
+        ms, n = im2col_steady(sg, calls, stream)
+        timed = 3 * n
+    else:
+        args = (case.M, case.N, case.K, case.alpha, dA.data_ptr(), case.K, dB.data_ptr(),
+                case.N, case.beta, dC.data_ptr(), case.N, stream.cuda_stream)
+
+        def step():
+            rc = sg.sgemm_f32(*args)
+            if rc != 0:
+                raise RuntimeError(sg.sgemm_status_string(rc))
+        ms, steps = square_timing(sg, args, stream)
+        if steps < min_launches:
+            ms = time_steps(step, min_launches, 0, stream)
+            steps = min_launches
+        timed = steps
+    print(json.dumps({"profile_config": name, "shape": [case.M, case.N, case.K],
+                      "alpha": case.alpha, "beta": case.beta, "flops": case.flops,
+                      "alg_bytes": case.alg_bytes, "timed_launches": timed,
+                      "us_event": round(ms * 1e3, 3),
+                      "kernel": sg.sgemm_plan(0, case.M, case.N, case.K, case.K, case.N, case.N,
+                                              case.alpha, cus)[1],
+                      "source_hash": source_hash()}), flush=True)
+
+
+def summarize_profiles(root):
+    """Markdown table from profile_config runs under rocprofv3: `root`/NAME.json
+    holds the line profile_config printed, `root`/NAME/ the kernel trace
+    (CSV).  For each library kernel, the mean duration over the timed
+    launches (the last ones of the process) is set beside the HIP-event time
+    per call of the same run."""
+    import csv
+    import glob
+    rows = []
+    for jpath in sorted(glob.glob(os.path.join(root, "*.json"))):
+        with open(jpath) as f:
+            lines = [l for l in f.read().splitlines() if l.startswith("{")]
+        if not lines:
+            continue
+        rec = json.loads(lines[-1])
+        name = rec["profile_config"]
+        traces = glob.glob(os.path.join(root, name, "**", "*kernel_trace.csv"), recursive=True)
+        if not traces:
+            rows.append((name, rec, [], "no kernel trace"))
+            continue
+        with open(traces[0], newline="") as f:
+            reader = csv.DictReader(f)
+            keys = {k.lower(): k for k in reader.fieldnames}
+            kn, ks, ke = keys["kernel_name"], keys["start_timestamp"], keys["end_timestamp"]
+            disp = [(r[kn], int(r[ks]), int(r[ke])) for r in reader]
+        disp.sort(key=lambda d: d[1])
+        lib = [d for d in disp if "sgemm::" in d[0]]  # the library's kernels only
+        per = {}
+        for kname, t0, t1 in lib:
+            per.setdefault(kname, []).append(t1 - t0)
+        kernels = []
+        for kname, durs in per.items():
+            last = durs[-rec["timed_launches"]:]
+            kernels.append((kname, len(last), float(np.mean(last)) / 1e3))
+        kernels.sort(key=lambda k: -k[2])
+        rows.append((name, rec, kernels, ""))
+    out = ["| config | kernel | timed dispatches | rocprof mean (us) | sum per call (us) | "
+           "HIP events per call (us) | fraction of roofline (rocprof) |",
+           "|---|---|---|---|---|---|---|"]
+    for name, rec, kernels, note in rows:
+        if not kernels:
+            out.append("| %s | %s | | | | %.2f | |" % (name, note, rec["us_event"]))
+            continue
+        per_call = sum(k[2] * k[1] for k in kernels) / rec["timed_launches"]
+        roof = max(rec["alg_bytes"] / (PEAK_HBM_GBPS * 1e3), rec["flops"] / (PEAK_FP32_TFLOPS * 1e6))
+        for i, (kname, n, us) in enumerate(kernels):
+            short = kname if len(kname) < 90 else kname[:87] + "..."
+            if i == 0:
+                out.append("| %s | `%s` | %d | %.2f | %.2f | %.2f | %.4f |"
+                           % (name, short, n, us, per_call, rec["us_event"], roof / per_call))
+            else:
+                out.append("| | `%s` | %d | %.2f | | | |" % (short, n, us))
+    return "\n".join(out)
+
+
 def traffic_probe(sg, case, call_args, stream):
     """Launch sequence for the HBM-traffic counter passes (run under rocprofv3
     --pmc FETCH_SIZE, then WRITE_SIZE): three plain copies of 1 GiB, whose
@@ -434,9 +553,86 @@ def traffic_probe(sg, case, call_args, stream):
         if rc != 0:
             raise RuntimeError(sg.sgemm_status_string(rc))
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_probe": True, "copy_bytes_each_way": n * 4,
-                      "shape": [case.M, case.N, case.K], "algorithmic_bytes": case.alg_bytes,
-                      "source_hash": source_hash()}), flush=True)
+    reads = 4.0 * (case.M * case.K + case.K * case.N) + (4.0 * case.M * case.N if case.beta else 0)
+    print(json.dumps({"traffic_probe": True, "config": case.name, "copy_bytes_each_way": n * 4,
+                      "shape": [case.M, case.N, case.K], "alpha": case.alpha, "beta": case.beta,
+                      "algorithmic_bytes": case.alg_bytes, "algorithmic_read_bytes": reads,
+                      "algorithmic_write_bytes": 4.0 * case.M * case.N,
+                      "kernel": sg.sgemm_plan(0, case.M, case.N, case.K, case.K, case.N, case.N,
+                                              case.alpha, 256)[1],
+                      "launches": 3, "source_hash": source_hash()}), flush=True)
+
+
+def summarize_traffic(root):
+    """HBM traffic per launch from counter passes over traffic_probe: for
+    config NAME, `root`/NAME.json holds the probe's line and
+    `root`/NAME_FETCH_SIZE/ and `root`/NAME_WRITE_SIZE/ the counter CSVs of
+    one pass each.  Counter values are scaled by what the same counter reads
+    for the probe's plain copies of known size.  Returns (markdown, records)."""
+    import csv
+    import glob
+
+    def counter(path_dir, name):
+        files = glob.glob(os.path.join(path_dir, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            return None
+        vals = {}  # dispatch -> (kernel, value)
+        with open(files[0], newline="") as f:
+            reader = csv.DictReader(f)
+            keys = {k.lower(): k for k in reader.fieldnames}
+            for r in reader:
+                if r[keys["counter_name"]] != name:
+                    continue
+                d = int(r[keys["dispatch_id"]])
+                k, v = vals.get(d, (r[keys["kernel_name"]], 0.0))
+                vals[d] = (k, v + float(r[keys["counter_value"]]))
+        return [vals[d] for d in sorted(vals)]
+
+    records = []
+    for jpath in sorted(glob.glob(os.path.join(root, "*.json"))):
+        with open(jpath) as f:
+            lines = [l for l in f.read().splitlines() if l.startswith("{")]
+        if not lines:
+            continue
+        rec = json.loads(lines[-1])
+        if not rec.get("traffic_probe"):
+            continue
+        name = rec["config"]
+        out = dict(rec)
+        for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals = counter(os.path.join(root, "%s_%s" % (name, cname)), cname)
+            if not vals:
+                continue
+            copies = [v for k, v in vals if "copyBuffer" in k]
+            lib = [(k, v) for k, v in vals if "sgemm::" in k]
+            if not copies or not lib:
+                continue
+            expect_kib = rec["copy_bytes_each_way"] / 1024.0
+            scale = expect_kib / float(np.median(copies))
+            # Per call: every library kernel of one call (stream-K: two).
+            per_kernel = {}
+            for k, v in lib:
+                per_kernel.setdefault(k, []).append(v)
+            per_call_kib = sum(float(np.median(v)) for v in per_kernel.values())
+            out[cname + "_KiB"] = round(per_call_kib, 1)
+            out[cname + "_scale"] = round(scale, 4)
+            out[cname + "_bytes"] = per_call_kib * 1024.0 * scale
+            out["kernels"] = sorted(k.split("(")[0] for k in per_kernel)
+        records.append(out)
+    md = ["| config | kernels | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | "
+          "algorithmic read MB | written MB (scaled) | algorithmic write MB | traffic / algorithmic |",
+          "|---|---|---|---|---|---|---|---|---|"]
+    for r in records:
+        if "FETCH_SIZE_bytes" not in r or "WRITE_SIZE_bytes" not in r:
+            md.append("| %s | counters missing | | | | | | | |" % r["config"])
+            continue
+        tot = r["FETCH_SIZE_bytes"] + r["WRITE_SIZE_bytes"]
+        md.append("| %s | %s | %.0f | %.0f | %.1f | %.1f | %.1f | %.1f | %.2f |" % (
+            r["config"], ", ".join("`%s`" % k for k in r["kernels"]), r["FETCH_SIZE_KiB"],
+            r["WRITE_SIZE_KiB"], r["FETCH_SIZE_bytes"] / 1e6, r["algorithmic_read_bytes"] / 1e6,
+            r["WRITE_SIZE_bytes"] / 1e6, r["algorithmic_write_bytes"] / 1e6,
+            tot / r["algorithmic_bytes"]))
+    return "\n".join(md), records
 
 
 def main():
@@ -452,12 +648,31 @@ def main():
     ap.add_argument("--no-valu", action="store_true", help="skip the VALU-kernel comparison")
     ap.add_argument("--no-ladder", action="store_true", help="skip the SIMT-ladder table")
     ap.add_argument("--no-squares", action="store_true", help="skip the square sweep")
+    ap.add_argument("--profile-config", metavar="NAME",
+                    help="only time the named configuration as the full run does (for a "
+                         "kernel-trace run of its own)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="print the markdown summary of profile-config runs under DIR (no GPU)")
     ap.add_argument("--traffic-probe", nargs="?", const="headline", default=None,
-                    metavar="M,N,K",
+                    metavar="NAME|M,N,K",
                     help="only run the launch sequence for the HBM-traffic counter passes "
-                         "(the headline, or the im2col shape M,N,K)")
+                         "(the headline, a configuration by name, or the im2col shape M,N,K)")
+    ap.add_argument("--summarize-traffic", metavar="DIR",
+                    help="print the markdown summary of traffic counter passes under DIR (no GPU)")
+    ap.add_argument("--traffic-json", metavar="FILE",
+                    help="with --summarize-traffic: also write the per-config records as JSON")
     args = ap.parse_args()
 
+    if args.summarize_profiles:
+        print(summarize_profiles(args.summarize_profiles))
+        return 0
+    if args.summarize_traffic:
+        md, records = summarize_traffic(args.summarize_traffic)
+        print(md)
+        if args.traffic_json:
+            with open(args.traffic_json, "w") as f:
+                json.dump(records, f, indent=1)
+        return 0
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(an N-split of B and C needs no collective; see the design notes).",
@@ -469,14 +684,20 @@ def main():
 
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
+    if args.profile_config:
+        profile_config(sg, args.profile_config, torch.cuda.current_stream())
+        return 0
     case = workloads.HEADLINE
     if args.traffic_probe not in (None, "headline"):
-        want = [int(v) for v in args.traffic_probe.split(",")]
-        found = [c for c in workloads.SKINNY + workloads.MID if [c.M, c.N, c.K] == want]
-        if not found:
-            print("no im2col shape %s" % args.traffic_probe, file=sys.stderr)
-            return 2
-        case = found[0]
+        if "," in args.traffic_probe:
+            want = [int(v) for v in args.traffic_probe.split(",")]
+            found = [c for c in workloads.SKINNY + workloads.MID if [c.M, c.N, c.K] == want]
+            if not found:
+                print("no im2col shape %s" % args.traffic_probe, file=sys.stderr)
+                return 2
+            case = found[0]
+        else:
+            case = config_by_name(args.traffic_probe)
     log("device", props.name, "CUs", props.multi_processor_count)
     A, B, C, dA, dB, dC = device_operands(case)
     stream = torch.cuda.current_stream()
@@ -504,7 +725,7 @@ def main():
     tflops = case.flops / (ms * 1e-3) / 1e12
     _, plan = sg.sgemm_plan(args.variant, case.M, case.N, case.K, case.K, case.N, case.N,
                             case.alpha, props.multi_processor_count)
-    traffic = stored_traffic()
+    traffic = stored_traffic(case.name)
     roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_TFLOPS, 4),
                 "traffic": traffic, "kernel": plan,

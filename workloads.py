@@ -54,7 +54,7 @@ class Case:
 
 
 def _sweep() -> List[Case]:
-    return [Case(2, i, n, n, n, 1.5, 0.5, True, "square%d" % n)
+    return [Case(2, i, n, n, n, 1.5, 0.5, True, "sweep%d" % n)
             for i, n in enumerate(range(256, 5121, 256))]
 
 
