@@ -4,18 +4,23 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library never uses it, and it
 imports nothing from the GPU library: the two share no code.
 
-The arithmetic lives in ``sgemm_ref.c`` (plain C, fp64 accumulation, one
-rounding at the end); this module only builds that file with gcc and
-marshals numpy arrays into it.
+The arithmetic lives in ``sgemm_ref.c`` and ``conv_ref.c`` (plain C, fp64
+accumulation, one rounding at the end); this module only builds those files
+with gcc and marshals numpy arrays into them.
 
 What is computed, for row-major fp32 matrices::
 
     C[i, j] <- alpha * sum_k A[i, k] * B[k, j] + beta * C[i, j]
 
 following the CPU reference loop of "matmul_opt.cu" (cnblogs post) and the
-alpha/beta epilogue of the NVIDIA_SGEMM_PRACTICE README (kernel 1 section).
-Every function here is pinned by ``tests/test_oracle.py`` against closed
-forms, integer brute force and float64 library products.
+alpha/beta epilogue of the NVIDIA_SGEMM_PRACTICE README (kernel 1 section),
+and the 2-D convolution (cross-correlation, NCHW input, zero padding) that
+the UNIVERSAL_SGEMM_CUDA README's convolution-as-GEMM shapes stand for,
+with its im2col lowering.  The GEMM functions are pinned by
+``tests/test_oracle.py`` against closed forms, integer brute force and
+float64 library products; the convolution functions by
+``tests/test_oracle_conv.py`` against scipy's correlation, padded sliding
+windows, 1x1 products and closed forms.
 """
 from __future__ import annotations
 
@@ -28,16 +33,17 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "sgemm_ref.c")
+CONV_SOURCE = os.path.join(_HERE, "conv_ref.c")
 LIBRARY = os.path.join(_HERE, "liboracle.so")
 
 # -ffp-contract=off: no fused multiply-add anywhere in the reference sums.
 CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
 
-def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+def build(source: str = SOURCE, output: str = LIBRARY, conv_source: str = CONV_SOURCE) -> str:
     """Compile the reference with gcc; returns the path of the shared object."""
     tmp = output + ".tmp%d" % os.getpid()
-    subprocess.run(["gcc", *CFLAGS, "-o", tmp, source, "-lm"], check=True)
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, source, conv_source, "-lm"], check=True)
     os.replace(tmp, output)
     return output
 
@@ -69,6 +75,14 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     ]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
+    c_int, c_long = ctypes.c_int, ctypes.c_long
+    lib.oracle_conv_out_size.restype = c_int
+    lib.oracle_conv_out_size.argtypes = [c_int] * 4
+    lib.oracle_im2col.restype = None
+    lib.oracle_im2col.argtypes = [c_int] * 10 + [f32p, f32p, c_long]
+    lib.oracle_conv2d.restype = c_int
+    lib.oracle_conv2d.argtypes = ([c_int] * 11 + [ctypes.c_float, f32p, f32p, c_long,
+                                                  ctypes.c_float, f32p, c_long, f64p, c_long])
     if path == LIBRARY:
         _lib = lib
     return lib
@@ -194,3 +208,66 @@ def tolerance(alpha: float, beta: float, absdot: np.ndarray, c_before) -> np.nda
     if beta != 0.0:
         scale = scale + np.abs(float(beta) * np.asarray(c_before, dtype=np.float64))
     return 1e-5 * scale + 1e-6
+
+
+def conv_out_size(size: int, k: int, stride: int, pad: int,
+                  lib: Optional[ctypes.CDLL] = None) -> int:
+    """Output extent along one axis: (size + 2 pad - k) // stride + 1."""
+    if size + 2 * pad < k or stride < 1 or k < 1:
+        raise ValueError("filter larger than the padded input, or bad stride")
+    return int((lib or load()).oracle_conv_out_size(size, k, stride, pad))
+
+
+def _geometry(X, R, S, stride, pad, lib=None):
+    if X.dtype != np.float32 or X.ndim != 4 or not X.flags.c_contiguous:
+        raise TypeError("X must be a packed (batch, C, H, W) float32 array")
+    sh, sw = (stride, stride) if np.isscalar(stride) else stride
+    ph, pw = (pad, pad) if np.isscalar(pad) else pad
+    batch, C, H, W = X.shape
+    OH, OW = conv_out_size(H, R, sh, ph, lib), conv_out_size(W, S, sw, pw, lib)
+    return batch, C, H, W, int(sh), int(sw), int(ph), int(pw), OH, OW
+
+
+def im2col(X: np.ndarray, R: int, S: int, stride=1, pad=0,
+           lib: Optional[ctypes.CDLL] = None) -> np.ndarray:
+    """The (C*R*S) x (batch*OH*OW) matrix of taps of the convolution of X
+    (packed NCHW float32) with an R x S filter: row k = (c*R + r)*S + s,
+    column n = (b*OH + oh)*OW + ow; zeros where a tap leaves the image."""
+    lib = lib or load()
+    batch, C, H, W, sh, sw, ph, pw, OH, OW = _geometry(X, R, S, stride, pad, lib)
+    B = np.empty((C * R * S, batch * OH * OW), dtype=np.float32)
+    if B.size:
+        lib.oracle_im2col(batch, C, H, W, R, S, sh, sw, ph, pw, _fptr(X), _fptr(B), B.shape[1])
+    return B
+
+
+def conv2d(X: np.ndarray, Wt: np.ndarray, R: int, S: int, stride=1, pad=0,
+           Y: Optional[np.ndarray] = None, alpha: float = 1.0, beta: float = 0.0,
+           with_absdot: bool = True,
+           lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """Return (out, absdot): out = fl32(alpha * conv(X, F) + beta * Y) with
+    X packed (batch, C, H, W), the filters as the M x (C*R*S) matrix Wt (rows
+    may be strided, F[m][c][r][s] at Wt[m, (c*R + r)*S + s]) and out an
+    M x (batch*OH*OW) matrix in (b, oh, ow) column order, as the lowered
+    product writes it.  Y (same shape, read only when beta != 0) is copied,
+    never modified.  absdot[m, n] = sum_k |w * x| in float64."""
+    lib = lib or load()
+    batch, C, H, W, sh, sw, ph, pw, OH, OW = _geometry(X, R, S, stride, pad, lib)
+    M, K = Wt.shape
+    if K != C * R * S:
+        raise ValueError("Wt must have C*R*S columns")
+    ldw = _ld(Wt, "Wt")
+    N = batch * OH * OW
+    out = np.zeros((M, N), dtype=np.float32) if Y is None else np.array(Y, dtype=np.float32)
+    if out.shape != (M, N):
+        raise ValueError("Y has the wrong shape")
+    t = np.zeros((M, N), dtype=np.float64) if with_absdot else None
+    if M == 0 or N == 0:
+        return out, t
+    rc = lib.oracle_conv2d(batch, C, H, W, M, R, S, sh, sw, ph, pw, ctypes.c_float(alpha),
+                           _fptr(X), _fptr(Wt), ldw, ctypes.c_float(beta), _fptr(out), N,
+                           t.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+                           if t is not None else None, N)
+    if rc != 0:
+        raise MemoryError("reference convolution could not allocate its row buffers")
+    return out, t
