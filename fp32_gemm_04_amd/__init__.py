@@ -31,8 +31,15 @@ SGEMM_ERR_WORKSPACE = -102
 SGEMM_ERR_NO_SLOT = -103
 SGEMM_ERR_CAPTURING = -104
 
+SCONV_VARIANT_AUTO = 0
+SCONV_VARIANT_STEM = 1
+SCONV_VARIANT_GENERAL = 2
+
 EXPORTS = ("sgemm_f32", "sgemm_f32_variant", "sgemm_plan", "sgemm_tune", "sgemm_tune_reset",
-           "sgemm_num_mfma_tiles", "sgemm_status_string")
+           "sgemm_num_mfma_tiles", "sgemm_status_string",
+           # include/sconv.h
+           "sconv2d_f32", "sconv2d_f32_variant", "sgemm_im2col_f32", "sconv2d_plan",
+           "sconv2d_num_stem_kernels")
 
 if not os.path.exists(LIBRARY):
     raise ImportError("libsgemm.so is not built; run __graft_entry__.build() "
@@ -67,6 +74,20 @@ _lib.sgemm_num_mfma_tiles.restype = ctypes.c_int
 _lib.sgemm_num_mfma_tiles.argtypes = []
 _lib.sgemm_status_string.restype = ctypes.c_char_p
 _lib.sgemm_status_string.argtypes = [ctypes.c_int]
+_conv_args = ([ctypes.c_int] * 11 + [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_void_p])
+_lib.sconv2d_f32.restype = ctypes.c_int
+_lib.sconv2d_f32.argtypes = _conv_args
+_lib.sconv2d_f32_variant.restype = ctypes.c_int
+_lib.sconv2d_f32_variant.argtypes = [ctypes.c_int] + _conv_args
+_lib.sgemm_im2col_f32.restype = ctypes.c_int
+_lib.sgemm_im2col_f32.argtypes = ([ctypes.c_int] * 10 + [ctypes.c_void_p, ctypes.c_void_p,
+                                                         ctypes.c_int, ctypes.c_void_p])
+_lib.sconv2d_plan.restype = ctypes.c_int
+_lib.sconv2d_plan.argtypes = [ctypes.c_int] * 13 + [ctypes.c_char_p, ctypes.c_int]
+_lib.sconv2d_num_stem_kernels.restype = ctypes.c_int
+_lib.sconv2d_num_stem_kernels.argtypes = []
 
 
 class SgemmError(RuntimeError):
@@ -162,3 +183,98 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant: int = SGEMM_VA
     if rc != 0:
         raise SgemmError(rc)
     return C
+
+
+# ------------------------------------------------------------ convolution
+
+def sconv2d_f32(batch, channels, height, width, out_channels, kernel_h, kernel_w, stride_h,
+                stride_w, pad_h, pad_w, alpha, X, Wt, ldw, beta, Y, ldy, stream=0) -> int:
+    """C ABI ``sconv2d_f32``; pointers and stream are integers.  Returns the status."""
+    return _lib.sconv2d_f32(batch, channels, height, width, out_channels, kernel_h, kernel_w,
+                            stride_h, stride_w, pad_h, pad_w, alpha, X, Wt, ldw, beta, Y, ldy,
+                            stream)
+
+
+def sconv2d_f32_variant(variant, batch, channels, height, width, out_channels, kernel_h,
+                        kernel_w, stride_h, stride_w, pad_h, pad_w, alpha, X, Wt, ldw, beta, Y,
+                        ldy, stream=0) -> int:
+    """C ABI ``sconv2d_f32_variant``.  Returns the status."""
+    return _lib.sconv2d_f32_variant(variant, batch, channels, height, width, out_channels,
+                                    kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w, alpha,
+                                    X, Wt, ldw, beta, Y, ldy, stream)
+
+
+def sgemm_im2col_f32(batch, channels, height, width, kernel_h, kernel_w, stride_h, stride_w,
+                     pad_h, pad_w, X, B, ldb, stream=0) -> int:
+    """C ABI ``sgemm_im2col_f32``.  Returns the status."""
+    return _lib.sgemm_im2col_f32(batch, channels, height, width, kernel_h, kernel_w, stride_h,
+                                 stride_w, pad_h, pad_w, X, B, ldb, stream)
+
+
+def sconv2d_plan(variant, batch, channels, height, width, out_channels, kernel_h, kernel_w,
+                 stride_h, stride_w, pad_h, pad_w, num_cus):
+    """C ABI ``sconv2d_plan``.  Returns (status, text)."""
+    buf = ctypes.create_string_buffer(256)
+    rc = _lib.sconv2d_plan(variant, batch, channels, height, width, out_channels, kernel_h,
+                           kernel_w, stride_h, stride_w, pad_h, pad_w, num_cus, buf, len(buf))
+    return rc, buf.value.decode()
+
+
+def sconv2d_num_stem_kernels() -> int:
+    """C ABI ``sconv2d_num_stem_kernels``."""
+    return _lib.sconv2d_num_stem_kernels()
+
+
+def _pair(v):
+    return (v, v) if isinstance(v, int) else tuple(v)
+
+
+def conv2d(X, Wt, kernel, stride=1, pad=0, Y=None, alpha: float = 1.0, beta: float = 0.0,
+           variant: int = SCONV_VARIANT_AUTO, stream=None):
+    """Y <- alpha * conv(X, filters) + beta * Y for float32 device tensors:
+    X packed (batch, C, H, W); Wt the filters as an out_channels x (C*R*S)
+    matrix (or (out_channels, C, R, S), packed); Y an out_channels x
+    (batch*OH*OW) matrix (allocated, zero, when None).  Returns Y; raises
+    SgemmError on a non-zero status."""
+    import torch
+    R, S = _pair(kernel)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    batch, C, H, W = X.shape
+    if not X.is_contiguous():
+        raise ValueError("X must be packed NCHW")
+    M = Wt.shape[0]
+    W2 = Wt.reshape(M, -1) if Wt.dim() == 4 else Wt
+    OH = (H + 2 * ph - R) // sh + 1
+    OW = (W + 2 * pw - S) // sw + 1
+    if Y is None:
+        Y = torch.zeros((M, batch * OH * OW), dtype=torch.float32, device=X.device)
+    s = stream if stream is not None else torch.cuda.current_stream(X.device)
+    rc = _lib.sconv2d_f32_variant(variant, batch, C, H, W, M, R, S, sh, sw, ph, pw, alpha,
+                                  X.data_ptr(), W2.data_ptr(), _ld(W2, "Wt"), beta, Y.data_ptr(),
+                                  _ld(Y, "Y"), s.cuda_stream)
+    if rc != 0:
+        raise SgemmError(rc)
+    return Y
+
+
+def im2col(X, kernel, stride=1, pad=0, B=None, stream=None):
+    """The (C*R*S) x (batch*OH*OW) im2col matrix of a packed NCHW float32
+    device tensor (into B, allocated when None).  Returns B."""
+    import torch
+    R, S = _pair(kernel)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    batch, C, H, W = X.shape
+    if not X.is_contiguous():
+        raise ValueError("X must be packed NCHW")
+    OH = (H + 2 * ph - R) // sh + 1
+    OW = (W + 2 * pw - S) // sw + 1
+    if B is None:
+        B = torch.empty((C * R * S, batch * OH * OW), dtype=torch.float32, device=X.device)
+    s = stream if stream is not None else torch.cuda.current_stream(X.device)
+    rc = _lib.sgemm_im2col_f32(batch, C, H, W, R, S, sh, sw, ph, pw, X.data_ptr(), B.data_ptr(),
+                               _ld(B, "B"), s.cuda_stream)
+    if rc != 0:
+        raise SgemmError(rc)
+    return B

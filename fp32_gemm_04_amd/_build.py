@@ -27,6 +27,7 @@ FLAGS = [
 SOURCES = {
     "sgemm.hip": [],
     "mfma_dl.hip": ["-Xarch_device", "-mllvm=--misched=gcn-max-ilp"],
+    "conv.hip": [],
 }
 
 

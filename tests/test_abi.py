@@ -11,13 +11,18 @@ import pytest
 import fp32_gemm_04_amd as sg
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "sgemm.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sgemm_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for header in HEADERS:
+        text = open(header).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:sgemm|sconv2d)_\w+)\s*\(",
+                                text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
@@ -180,7 +185,7 @@ def test_ladder_rungs():
 
 
 def test_ladder_constants_match_header():
-    text = open(HEADER).read()
+    text = open(os.path.join(ROOT, "include", "sgemm.h")).read()
     assert re.search(r"SGEMM_VARIANT_LADDER\s*=\s*%d\b" % sg.SGEMM_VARIANT_LADDER, text)
     assert re.search(r"#define SGEMM_LADDER_RUNGS %d\b" % sg.SGEMM_LADDER_RUNGS, text)
     assert len(sg.LADDER_RUNG_NAMES) == sg.SGEMM_LADDER_RUNGS
