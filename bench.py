@@ -22,6 +22,11 @@ HBM before timing starts.  The line printed also carries:
     rotating copies of its operands (and, for comparison, one launch at a
     time after a cache flush), with TFLOPS and the HBM bandwidth the
     algorithmic bytes imply, a parity check and the CPU reference's time;
+  * conv: the convolution readings of the im2col shapes, as sconv2d_f32
+    (implicit GEMM), as sgemm_im2col_f32 alone and as the lowered path
+    (im2col, then sgemm_f32), with the roofline fraction of the algorithmic
+    bytes (input + filters + output), a parity check and the CPU reference
+    convolution's time;
   * valu_comparison and ladder: the vector-FMA kernels on the headline
     workload, the register-tile comparison kernel and each rung of the
     pages' SIMT optimisation ladder (naive ... double-buffered);
@@ -29,7 +34,7 @@ HBM before timing starts.  The line printed also carries:
     im2col shapes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-check] [--no-im2col]
-                       [--no-valu] [--no-ladder] [--no-squares]
+                       [--no-valu] [--no-ladder] [--no-squares] [--no-conv]
 """
 from __future__ import annotations
 
@@ -376,6 +381,136 @@ def bench_im2col(sg, stream, reps, check=True):
     return out
 
 
+def steady_state(launch, nset, stream, n=None):
+    """Steady-state time per call (ms) of launch(i), i cycling over nset
+    operand sets: about 0.1 s of back-to-back calls to bring the clocks up,
+    then three runs of about 0.15 s between two HIP events; the median run,
+    and the calls per run."""
+    import torch
+    launch(0)
+    t_end = time.perf_counter() + 0.1
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            launch(i % nset)
+            i += 1
+        torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    if n is None:
+        e0.record(stream)
+        for k in range(nset):
+            launch(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        n = max(nset, int(0.15 / max(e0.elapsed_time(e1) * 1e-3 / nset, 1e-6)))
+    runs = []
+    for _ in range(3):
+        e0.record(stream)
+        for k in range(n):
+            launch(k % nset)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        runs.append(e0.elapsed_time(e1) / n)
+    return float(np.median(runs)), n
+
+
+def bench_conv(sg, stream, check=True):
+    """The convolution readings of the im2col shapes, three ways each:
+    sconv2d_f32 (implicit GEMM: the input, the filters and the output cross
+    HBM once), sgemm_im2col_f32 alone (the im2col matrix written), and the
+    lowered path (sgemm_im2col_f32, then sgemm_f32 on the matrix).  Steady
+    state over rotating input and output copies (at least 1.6 GB), as for
+    the im2col shapes.  The convolution's whole output is compared with the
+    CPU reference convolution, whose time is reported."""
+    import torch
+    import oracle
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = []
+    for case in workloads.CONV_STEMS + workloads.CONV_MID:
+        log("conv", case.name)
+        X, Wt = workloads.conv_operands(case)
+        g = case.geometry
+        dW = torch.from_numpy(Wt).cuda()
+        per_set = 4 * (X.size + case.M * case.N)
+        nset = int(min(64, max(2, -(-1600 * 1024 * 1024 // per_set))))
+        dX = [torch.from_numpy(X).cuda()] + []
+        dX += [dX[0].clone() for _ in range(nset - 1)]
+        dY = [torch.zeros((case.M, case.N), dtype=torch.float32, device="cuda")
+              for _ in range(nset)]
+
+        def conv(i):
+            rc = sg.sconv2d_f32(*g, 1.0, dX[i].data_ptr(), dW.data_ptr(), case.K, 0.0,
+                                dY[i].data_ptr(), case.N, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(sg.sgemm_status_string(rc))
+
+        ms, n = steady_state(conv, nset, stream)
+        _, plan = sg.sconv2d_plan(0, *g, cus)
+        roof_us = max(case.alg_bytes / (PEAK_HBM_GBPS * 1e9),
+                      case.flops / (PEAK_FP32_TFLOPS * 1e12)) * 1e6
+        tflops = case.flops / (ms * 1e-3) / 1e12
+        entry = {"name": case.name, "geometry": dict(zip(
+            ["batch", "C", "H", "W", "M", "R", "S", "sh", "sw", "ph", "pw"], g)),
+            "gemm_shape": [case.M, case.N, case.K], "kernel": plan,
+            "us": round(ms * 1e3, 2), "calls": n, "operand_sets": nset,
+            "tflops": round(tflops, 2), "alg_bytes": case.alg_bytes,
+            "hbm_gbps": round(case.alg_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4),
+            "frac_roofline": round(roof_us / (ms * 1e3), 4)}
+        if check:
+            log("verify", case.name)
+            conv(0)
+            torch.cuda.synchronize()
+            got = dY[0].cpu().numpy()
+            t0 = time.perf_counter()
+            ref, absdot = oracle.conv2d(X, Wt, case.R, case.S, (case.sh, case.sw),
+                                        (case.ph, case.pw))
+            secs = time.perf_counter() - t0
+            tol = oracle.tolerance(1.0, 0.0, absdot, None)
+            ratio = np.abs(got.astype(np.float64) - ref.astype(np.float64)) / tol
+            del absdot, tol
+            entry["parity"] = {"elements": int(got.size), "pass": bool(np.all(ratio <= 1.0)),
+                               "max_err_over_tol": round(float(np.nanmax(ratio)), 4)}
+            entry["cpu"] = {"s": round(secs, 3), "tflops": round(case.flops / secs / 1e12, 5),
+                            "threads": oracle.num_threads(), "kind": "oracle",
+                            "work": "whole direct convolution with sum|w*x|"}
+            entry["gpu_over_cpu"] = round(tflops / entry["cpu"]["tflops"], 1)
+            del got, ref, ratio
+        del dY
+        torch.cuda.empty_cache()
+        # The lowered path: im2col matrix, then the product.
+        B = [torch.empty((case.K, case.N), dtype=torch.float32, device="cuda") for _ in range(2)]
+        Y = torch.empty((case.M, case.N), dtype=torch.float32, device="cuda")
+
+        def im2col(i):
+            rc = sg.sgemm_im2col_f32(case.batch, case.C, case.H, case.W, case.R, case.S,
+                                     case.sh, case.sw, case.ph, case.pw, dX[i % nset].data_ptr(),
+                                     B[i % 2].data_ptr(), case.N, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(sg.sgemm_status_string(rc))
+
+        def lowered(i):
+            im2col(i)
+            rc = sg.sgemm_f32(case.M, case.N, case.K, 1.0, dW.data_ptr(), case.K,
+                              B[i % 2].data_ptr(), case.N, 0.0, Y.data_ptr(), case.N,
+                              stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(sg.sgemm_status_string(rc))
+
+        im_ms, _ = steady_state(im2col, 2 * nset, stream)
+        low_ms, _ = steady_state(lowered, 2 * nset, stream)
+        im_bytes = 4.0 * (X.size + case.K * case.N)
+        entry.update({"im2col_us": round(im_ms * 1e3, 2),
+                      "im2col_hbm_gbps": round(im_bytes / (im_ms * 1e-3) / 1e9, 1),
+                      "lowered_us": round(low_ms * 1e3, 2),
+                      "lowered_over_conv": round(low_ms / ms, 3)})
+        out.append(entry)
+        del dX, B, Y, dW
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_ladder(sg, case, call_args, stream, mfma_tflops):
     """Each rung of the pages' SIMT ladder (sgemm_f32_variant(SGEMM_VARIANT_LADDER + r))
     on the headline workload: one untimed launch, then the median of a few
@@ -648,6 +783,7 @@ def main():
     ap.add_argument("--no-valu", action="store_true", help="skip the VALU-kernel comparison")
     ap.add_argument("--no-ladder", action="store_true", help="skip the SIMT-ladder table")
     ap.add_argument("--no-squares", action="store_true", help="skip the square sweep")
+    ap.add_argument("--no-conv", action="store_true", help="skip the convolution readings")
     ap.add_argument("--profile-config", metavar="NAME",
                     help="only time the named configuration as the full run does (for a "
                          "kernel-trace run of its own)")
@@ -774,6 +910,8 @@ def main():
     if not args.no_im2col:
         result["device_copy"] = device_copy(stream)
         result["im2col"] = bench_im2col(sg, stream, args.im2col_reps, check=not args.no_check)
+    if not args.no_conv:
+        result["conv"] = bench_conv(sg, stream, check=not args.no_check)
     print(json.dumps(result), flush=True)
     return 0
 

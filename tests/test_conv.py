@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
+import workloads
 from tests.gpu_helpers import GUARD, assert_bits_equal, assert_within_tolerance, say
 
 pytestmark = pytest.mark.gpu
@@ -231,21 +232,17 @@ def test_im2col_matches_reference_and_feeds_sgemm():
         assert_bits_equal(Yg.cpu().numpy(), conv, "im2col + sgemm against sconv2d, case %d" % i)
 
 
-# The two stem readings at full size (N = 128 * 112 * 112 = 1605632).
-FULL = [
-    ("resnet_stem_64x1605632x147", (128, 3, 224, 224, 64, 7, 7, (2, 2), (3, 3))),
-    ("mobilenet_stem_32x1605632x27", (128, 3, 224, 224, 32, 3, 3, (2, 2), (1, 1))),
-]
-
-
+# The two stem readings at full size (N = 128 * 112 * 112 = 1605632), and
+# the mid-size readings through the general kernel.
 @pytest.mark.parametrize("integer", [False, True], ids=["uniform", "integer"])
-@pytest.mark.parametrize("name,g", FULL, ids=[f[0] for f in FULL])
-def test_full_size_stem(name, g, integer):
-    batch, C, H, W, M, R, S, stride, pad = g
-    gen = _ints if integer else _uniform
-    X = gen((batch, C, H, W), 70 + M)
-    Wt = gen((M, C * R * S), 71 + M)
-    assert _stem_applies(g)
-    out = check(X, Wt, R, S, stride, pad, 0, integer)
-    assert out.shape == (M, 1605632)
-    say("%s %s: %d elements" % (name, "integer" if integer else "uniform", out.size))
+@pytest.mark.parametrize("case", workloads.CONV_STEMS + workloads.CONV_MID,
+                         ids=[c.name for c in workloads.CONV_STEMS + workloads.CONV_MID])
+def test_full_size_readings(case, integer):
+    X, Wt = workloads.conv_operands(case, integer)
+    g = case.geometry
+    b, C, H, W, M, R, S, sh, sw, ph, pw = g
+    if case in workloads.CONV_STEMS:
+        assert _stem_applies((b, C, H, W, M, R, S, (sh, sw), (ph, pw)))
+    out = check(X, Wt, case.R, case.S, (case.sh, case.sw), (case.ph, case.pw), 0, integer)
+    assert out.shape == (case.M, case.N)
+    say("%s %s: %d elements" % (case.name, "integer" if integer else "uniform", out.size))

@@ -17,6 +17,16 @@ uniformly from {-4, ..., 4} for the bit-exact variant.
 
 Seeds: ``10000*config + 100*sub + role`` with role 0 = A, 1 = B, 2 = C, plus
 50 for the integer variant.
+
+The convolution readings of those shapes (``ConvCase``; the page names no
+layers, so these geometries are readings of the shapes' factors): 128
+images of 3 x 224 x 224 with 64 filters of 7 x 7 at stride 2, pad 3, give
+the (64, 1605632, 147) product, and with 32 filters of 3 x 3 at stride 2,
+pad 1 the (32, 1605632, 27) one; one 128-channel image of 119 x 119 (or
+208 x 208) with 384 (or 256) filters of 3 x 3 at stride 1, pad 1 gives the
+(384, 14161, 1152) (or (256, 43264, 1152)) product.  Inputs and filters are
+uniform on [-1, 1) (or integers in [-4, 4]); seeds as above with config 5,
+role 0 = filters, 1 = input.
 """
 from __future__ import annotations
 
@@ -131,3 +141,73 @@ def device_integers(rows: int, cols: int, seed_value: int):
     gen.manual_seed(seed_value)
     return torch.randint(-4, 5, (rows, cols), generator=gen, device="cuda",
                          dtype=torch.float32)
+
+
+@dataclass(frozen=True)
+class ConvCase:
+    """A convolution: `batch` images of C x H x W, M filters of C x R x S,
+    strides (sh, sw), zero padding (ph, pw); the output is the M x N matrix
+    (N = batch*OH*OW) of the lowered product with K = C*R*S."""
+    sub: int
+    name: str
+    batch: int
+    C: int
+    H: int
+    W: int
+    M: int
+    R: int
+    S: int
+    sh: int
+    sw: int
+    ph: int
+    pw: int
+
+    @property
+    def OH(self) -> int:
+        return (self.H + 2 * self.ph - self.R) // self.sh + 1
+
+    @property
+    def OW(self) -> int:
+        return (self.W + 2 * self.pw - self.S) // self.sw + 1
+
+    @property
+    def N(self) -> int:
+        return self.batch * self.OH * self.OW
+
+    @property
+    def K(self) -> int:
+        return self.C * self.R * self.S
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+    @property
+    def alg_bytes(self) -> float:
+        """Input, filters and output, each moved once (beta = 0)."""
+        return 4.0 * (self.batch * self.C * self.H * self.W + self.M * self.K + self.M * self.N)
+
+    @property
+    def geometry(self) -> Tuple[int, ...]:
+        return (self.batch, self.C, self.H, self.W, self.M, self.R, self.S, self.sh, self.sw,
+                self.ph, self.pw)
+
+
+CONV_STEMS = [
+    ConvCase(0, "conv7x7s2_64x1605632x147", 128, 3, 224, 224, 64, 7, 7, 2, 2, 3, 3),
+    ConvCase(1, "conv3x3s2_32x1605632x27", 128, 3, 224, 224, 32, 3, 3, 2, 2, 1, 1),
+]
+CONV_MID = [
+    ConvCase(2, "conv3x3s1_384x14161x1152", 1, 128, 119, 119, 384, 3, 3, 1, 1, 1, 1),
+    ConvCase(3, "conv3x3s1_256x43264x1152", 1, 128, 208, 208, 256, 3, 3, 1, 1, 1, 1),
+]
+
+
+def conv_operands(case: ConvCase, integer: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """(X packed NCHW, filters as the M x K matrix) for a convolution case."""
+    gen = integers if integer else uniform
+    base = 10000 * 5 + 100 * case.sub + (50 if integer else 0)
+    Wt = gen(case.M, case.K, base + 0)
+    X = gen(case.batch * case.C, case.H * case.W, base + 1).reshape(case.batch, case.C, case.H,
+                                                                      case.W)
+    return np.ascontiguousarray(X), Wt
