@@ -429,22 +429,9 @@ def bench_conv(sg, stream, check=True):
     out = []
     for case in workloads.CONV_STEMS + workloads.CONV_MID:
         log("conv", case.name)
-        X, Wt = workloads.conv_operands(case)
         g = case.geometry
-        dW = torch.from_numpy(Wt).cuda()
-        per_set = 4 * (X.size + case.M * case.N)
-        nset = int(min(64, max(2, -(-1600 * 1024 * 1024 // per_set))))
-        dX = [torch.from_numpy(X).cuda()] + []
-        dX += [dX[0].clone() for _ in range(nset - 1)]
-        dY = [torch.zeros((case.M, case.N), dtype=torch.float32, device="cuda")
-              for _ in range(nset)]
-
-        def conv(i):
-            rc = sg.sconv2d_f32(*g, 1.0, dX[i].data_ptr(), dW.data_ptr(), case.K, 0.0,
-                                dY[i].data_ptr(), case.N, stream.cuda_stream)
-            if rc != 0:
-                raise RuntimeError(sg.sgemm_status_string(rc))
-
+        X, Wt, dX, dW, dY, conv = conv_sets(sg, case, stream)
+        nset = len(dX)
         ms, n = steady_state(conv, nset, stream)
         _, plan = sg.sconv2d_plan(0, *g, cus)
         roof_us = max(case.alg_bytes / (PEAK_HBM_GBPS * 1e9),
@@ -573,11 +560,33 @@ def bench_ladder_im2col(sg, stream):
 
 
 def config_by_name(name):
-    for case in workloads.ALL:
+    for case in workloads.ALL + workloads.CONV_STEMS + workloads.CONV_MID:
         if case.name == name:
             return case
-    raise SystemExit("no configuration named %r (names: %s)"
-                     % (name, ", ".join(c.name for c in workloads.ALL)))
+    raise SystemExit("no configuration named %r (names: %s)" % (name, ", ".join(
+        c.name for c in workloads.ALL + workloads.CONV_STEMS + workloads.CONV_MID)))
+
+
+def conv_sets(sg, case, stream, nset=None):
+    """Rotating input/output copies of a convolution reading (at least
+    1.6 GB in all, unless nset is given) and a launch(i) running sconv2d_f32
+    on set i."""
+    import torch
+    X, Wt = workloads.conv_operands(case)
+    dW = torch.from_numpy(Wt).cuda()
+    per_set = 4 * (X.size + case.M * case.N)
+    if nset is None:
+        nset = int(min(64, max(2, -(-1600 * 1024 * 1024 // per_set))))
+    dX = [torch.from_numpy(X).cuda()]
+    dX += [dX[0].clone() for _ in range(nset - 1)]
+    dY = [torch.zeros((case.M, case.N), dtype=torch.float32, device="cuda") for _ in range(nset)]
+
+    def launch(i):
+        rc = sg.sconv2d_f32(*case.geometry, 1.0, dX[i].data_ptr(), dW.data_ptr(), case.K, 0.0,
+                            dY[i].data_ptr(), case.N, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(sg.sgemm_status_string(rc))
+    return X, Wt, dX, dW, dY, launch
 
 
 def profile_config(sg, name, stream, min_launches=50):
@@ -588,6 +597,16 @@ def profile_config(sg, name, stream, min_launches=50):
     import torch
     case = config_by_name(name)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if isinstance(case, workloads.ConvCase):
+        _, _, dX, _, _, launch = conv_sets(sg, case, stream)
+        ms, n = steady_state(launch, len(dX), stream)
+        print(json.dumps({"profile_config": name, "shape": [case.M, case.N, case.K],
+                          "geometry": list(case.geometry), "flops": case.flops,
+                          "alg_bytes": case.alg_bytes, "timed_launches": 3 * n,
+                          "us_event": round(ms * 1e3, 3),
+                          "kernel": sg.sconv2d_plan(0, *case.geometry, cus)[1],
+                          "source_hash": source_hash()}), flush=True)
+        return
     _, _, _, dA, dB, dC = device_operands(case)
     if case in workloads.SKINNY + workloads.MID:
         sets, calls = im2col_operand_sets(case, dA, dB, dC, stream)
@@ -670,6 +689,30 @@ def summarize_profiles(root):
     return "\n".join(out)
 
 
+def conv_traffic_probe(sg, case, stream):
+    """As traffic_probe, for a convolution reading: three 1 GiB copies, then
+    three sconv2d_f32 calls on one input/output set."""
+    import torch
+    n = (1 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
+    _, _, dX, _, _, launch = conv_sets(sg, case, stream, nset=1)
+    for _ in range(3):
+        launch(0)
+    torch.cuda.synchronize()
+    reads = 4.0 * (case.batch * case.C * case.H * case.W + case.M * case.K)
+    print(json.dumps({"traffic_probe": True, "config": case.name, "copy_bytes_each_way": n * 4,
+                      "shape": [case.M, case.N, case.K], "geometry": list(case.geometry),
+                      "algorithmic_bytes": case.alg_bytes, "algorithmic_read_bytes": reads,
+                      "algorithmic_write_bytes": 4.0 * case.M * case.N,
+                      "kernel": sg.sconv2d_plan(0, *case.geometry, 256)[1],
+                      "launches": 3, "source_hash": source_hash()}), flush=True)
+
+
 def traffic_probe(sg, case, call_args, stream):
     """Launch sequence for the HBM-traffic counter passes (run under rocprofv3
     --pmc FETCH_SIZE, then WRITE_SIZE): three plain copies of 1 GiB, whose
@@ -738,7 +781,9 @@ def summarize_traffic(root):
             vals = counter(os.path.join(root, "%s_%s" % (name, cname)), cname)
             if not vals:
                 continue
-            copies = [v for k, v in vals if "copyBuffer" in k]
+            # The probe's 1 GiB copies are the three largest copies of the run
+            # (operand set-up may add smaller ones).
+            copies = sorted((v for k, v in vals if "copyBuffer" in k), reverse=True)[:3]
             lib = [(k, v) for k, v in vals if "sgemm::" in k]
             if not copies or not lib:
                 continue
@@ -834,6 +879,9 @@ def main():
             case = found[0]
         else:
             case = config_by_name(args.traffic_probe)
+            if isinstance(case, workloads.ConvCase):
+                conv_traffic_probe(sg, case, torch.cuda.current_stream())
+                return 0
     log("device", props.name, "CUs", props.multi_processor_count)
     A, B, C, dA, dB, dC = device_operands(case)
     stream = torch.cuda.current_stream()
