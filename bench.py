@@ -713,6 +713,62 @@ def conv_traffic_probe(sg, case, stream):
                       "launches": 3, "source_hash": source_hash()}), flush=True)
 
 
+kNumXcdCounted = 8  # GRBM_GUI_ACTIVE comes summed over the MI355X's 8 XCDs
+
+
+def summarize_counters(root):
+    """Counter passes over traffic_probe (or any run of a configuration):
+    `root`/NAME_PASS/ holds the counter CSV of one pass for configuration
+    NAME.  For the library's kernels, each counter's median over the
+    dispatches, and per MFMA instruction the other instruction counts.
+    Returns markdown."""
+    import csv
+    import glob
+    per = {}  # config -> {counter: [values]}
+    for d in sorted(glob.glob(os.path.join(root, "*_*"))):
+        if not os.path.isdir(d):
+            continue
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            continue
+        name = os.path.basename(d).rsplit("_", 1)[0]
+        vals, durs = {}, {}
+        with open(files[0], newline="") as f:
+            reader = csv.DictReader(f)
+            keys = {k.lower(): k for k in reader.fieldnames}
+            for r in reader:
+                if "sgemm::" not in r[keys["kernel_name"]]:
+                    continue
+                did = int(r[keys["dispatch_id"]])
+                key = (r[keys["counter_name"]], did)
+                vals[key] = vals.get(key, 0.0) + float(r[keys["counter_value"]])
+                if "start_timestamp" in keys:
+                    durs[did] = int(r[keys["end_timestamp"]]) - int(r[keys["start_timestamp"]])
+        for (cname, did), v in vals.items():
+            per.setdefault(name, {}).setdefault(cname, []).append(v)
+            if cname == "GRBM_GUI_ACTIVE" and did in durs:
+                # Active cycles are counted per XCD (8), summed here.
+                per[name].setdefault("clock_GHz", []).append(v / kNumXcdCounted / durs[did])
+        if durs:
+            per[name].setdefault("duration_us (counted run)", []).extend(d / 1e3 for d in durs.values())
+    out = []
+    for name, counters in per.items():
+        med = {c: float(np.median(v)) for c, v in counters.items()}
+        out.append("### %s\n" % name)
+        out.append("| counter | median per call |")
+        out.append("|---|---|")
+        for c in sorted(med):
+            out.append("| %s | %.6g |" % (c, med[c]))
+        mf = med.get("SQ_INSTS_MFMA")
+        if mf:
+            ratios = ["%s %.2f" % (c[9:] if c.startswith("SQ_INSTS_") else c, med[c] / mf)
+                      for c in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD",
+                                "SQ_INSTS_VMEM_WR", "SQ_INSTS_LDS", "SQ_INSTS_SMEM") if c in med]
+            out.append("\nPer MFMA instruction: " + ", ".join(ratios) + ".")
+        out.append("")
+    return "\n".join(out)
+
+
 def traffic_probe(sg, case, call_args, stream):
     """Launch sequence for the HBM-traffic counter passes (run under rocprofv3
     --pmc FETCH_SIZE, then WRITE_SIZE): three plain copies of 1 GiB, whose
@@ -840,12 +896,17 @@ def main():
                          "(the headline, a configuration by name, or the im2col shape M,N,K)")
     ap.add_argument("--summarize-traffic", metavar="DIR",
                     help="print the markdown summary of traffic counter passes under DIR (no GPU)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print the markdown summary of counter passes under DIR (no GPU)")
     ap.add_argument("--traffic-json", metavar="FILE",
                     help="with --summarize-traffic: also write the per-config records as JSON")
     args = ap.parse_args()
 
     if args.summarize_profiles:
         print(summarize_profiles(args.summarize_profiles))
+        return 0
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
         return 0
     if args.summarize_traffic:
         md, records = summarize_traffic(args.summarize_traffic)
