@@ -58,12 +58,13 @@ struct StemEntry {
 // Windows for 224-wide images: 232 columns hold the image and its padding
 // (column 4 is input column 0); 13 rows (7 x 7, stride 2) or 9 (3 x 3,
 // stride 2) cover the four output rows a 256-position strip of a 112-wide
-// output touches.  LDS: 75 KB (two workgroups per CU) and 30 KB (four).
+// output touches.  LDS: 75 KB (7 x 7) and 30 KB (3 x 3); two workgroups
+// per CU (four waves each: the register budget of two waves per SIMD).
 const StemEntry kStems[] = {
     SGEMM_STEM(2, 3, 7, 7, 2, 2, 232, 13, 2),
     SGEMM_STEM(1, 3, 7, 7, 2, 2, 232, 13, 2),
     SGEMM_STEM(2, 3, 3, 3, 2, 2, 232, 9, 2),
-    SGEMM_STEM(1, 3, 3, 3, 2, 2, 232, 9, 4),
+    SGEMM_STEM(1, 3, 3, 3, 2, 2, 232, 9, 2),
 };
 constexpr int kNumStems = (int)(sizeof(kStems) / sizeof(kStems[0]));
 
@@ -128,6 +129,10 @@ int conv_launch(int variant, const Geometry &q, float alpha, const float *X, con
     if (q.M > 0 && N > 0 && (Y == nullptr || ((uintptr_t)Y & 3u) != 0)) return -17;
     if ((int64_t)ldy < (N > 1 ? N : 1)) return -18;
     const StemEntry *stem = stem_for(q, OH, OW);
+    // The stem kernel addresses X and Y with 32-bit byte offsets.
+    const int64_t x_bytes = 4 * (int64_t)q.batch * q.C * q.H * q.W;
+    const int64_t y_bytes = 4 * (int64_t)q.M * ldy;
+    if (x_bytes >= (1ll << 32) || y_bytes >= (1ll << 32)) stem = nullptr;
     if (variant == SCONV_VARIANT_STEM && stem == nullptr) return SGEMM_ERR_VARIANT_SHAPE;
     if (q.M == 0 || N == 0) return 0;
 
@@ -266,6 +271,10 @@ extern "C" int sconv2d_plan(int variant, int batch, int channels, int height, in
     if (bad != 0) return bad;
     if (num_cus < 1 || (buf == nullptr && buflen > 0) || buflen < 0) return -12;
     const StemEntry *stem = stem_for(q, OH, OW);
+    // Packed output (ldy = N) assumed, as for the call's own size check.
+    if (4 * (int64_t)batch * channels * height * width >= (1ll << 32) ||
+        4 * (int64_t)out_channels * N >= (1ll << 32))
+        stem = nullptr;
     if (variant == SCONV_VARIANT_STEM && stem == nullptr) return SGEMM_ERR_VARIANT_SHAPE;
     char text[200];
     if (out_channels == 0 || N == 0) {

@@ -198,7 +198,9 @@ __global__ void __launch_bounds__(256) conv_gemm_kernel(ConvArgs a, int tiles_m,
 // channel, ROWS rows, WPITCH columns with the image at column COL0 and
 // zeros around it -- into an LDS window once; then each of its four waves
 // computes M x 64 outputs (MB x 2 blocks of v_mfma_f32_32x32x2_f32), taking
-// the B operand of every MFMA straight from the window.
+// the B operand of every MFMA straight from the window.  The next strip's
+// window is fetched into registers before the strip's MFMAs and written to
+// LDS after them, so its latency is hidden behind the matrix work.
 //
 // Taps are paired: the MFMA's two k values are taps f = 2t and 2t + 1, one
 // per half-wave.  In the window, tap f of output position q sits at
@@ -245,6 +247,8 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
 {
     using G = StemGeom<CH, R, S, WPITCH, ROWS>;
     constexpr int KP = G::KP, TP = G::TP;
+    constexpr int G4 = WPITCH / 4;                          // 16-byte groups per window row
+    constexpr int NST = (CH * ROWS * G4 + 255) / 256;       // groups staged per thread
     static_assert(WPITCH % 4 == 0, "window rows must be 16-byte multiples");
     static_assert(G::WIN * 4 + 16 < 65536, "LDS offsets must fit the immediate field");
     __shared__ __attribute__((aligned(16))) float As[2 * 32 * MB * TP];
@@ -262,43 +266,109 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
 
     const int ohw = a.OH * a.OW;
     const bool vec_x = ((reinterpret_cast<uintptr_t>(a.X) & 15u) == 0) && (a.W % 4 == 0);
+    // Two adjacent positions per lane can be one 64-bit store.
+    const bool vec_y = ((reinterpret_cast<uintptr_t>(a.Y) & 7u) == 0) && (a.ldy % 2 == 0) &&
+                       (ohw % 2 == 0);
     const int64_t s0 = (int64_t)blockIdx.x * total_strips / gridDim.x;
     const int64_t s1 = (int64_t)(blockIdx.x + 1) * total_strips / gridDim.x;
     const float *a_lane = As + (h * 32 * MB + j) * TP;
 
+    // The window of strip st, fetched into registers: this thread's groups
+    // e = tid + 256 i of the CH * ROWS rows of G4 16-byte groups.
+    // Input loads and output stores address the kernel argument's base with
+    // 32-bit byte offsets (the host takes this kernel only for inputs and
+    // outputs below 4 GiB), which keeps 64-bit address arithmetic out of the
+    // registers the tap loop needs.
+    //
+    // The window of strip st is fetched into registers (this thread's
+    // 16-byte groups e = tid + 256 i of the CH * ROWS rows of G4 groups)
+    // before the strip's MFMAs and written to LDS after them.  The loads
+    // are unconditional, from a clamped address where the data lie outside
+    // the image, and which of them hold data is kept as bits of one
+    // register: a lane-dependent branch around a load would keep its
+    // execution mask alive across the MFMA loop.
+    const char *xbase = reinterpret_cast<const char *>(a.X);
+    char *ybase = reinterpret_cast<char *>(a.Y);
+    // A thread's groups keep their channel, window row and columns from strip
+    // to strip: their byte offsets from the strip's first window row, and
+    // which of their elements fall inside the image's columns, are worked
+    // out once.
+    uint32_t goff[NST];
+    uint64_t col_ok = 0;  // bit 4 i + q: element q of group i is an image column
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+        const int e = tid + 256 * i;
+        const int rowid = e / G4, g = e - rowid * G4;
+        const int c = rowid / ROWS, rr = rowid % ROWS;
+        const int iw0 = 4 * g - kStemCol0;
+        goff[i] = (uint32_t)((c * a.H + rr) * a.W + iw0) * 4u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool ok = e < CH * ROWS * G4 && iw0 + q >= 0 && iw0 + q < a.W &&
+                            (vec_x ? iw0 >= 0 && iw0 + 3 < a.W : true);
+            col_ok |= (ok ? 1ull : 0ull) << (4 * i + q);
+        }
+    }
+    f32x4 pre[NST];
+    uint64_t valid = 0;  // col_ok and the group's row inside the image
+    auto fetch = [&](int64_t st) {
+        const int b = (int)(st / strips_per_image);
+        const int p0 = (int)(st - (int64_t)b * strips_per_image) * kStemStrip;
+        const int ih_lo = (p0 / a.OW) * SH - a.ph;
+        // Byte offset of (image b, channel 0, row ih_lo, column 0); may
+        // wrap when ih_lo < 0, where only rows inside the image are read.
+        const uint32_t sbase = (uint32_t)((b * a.C * a.H + ih_lo) * a.W) * 4u;
+        valid = 0;
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+            const int rr = ((tid + 256 * i) / G4) % ROWS;
+            const bool row_ok = (unsigned)(ih_lo + rr) < (unsigned)a.H;
+            const uint64_t ok4 = row_ok ? (col_ok >> (4 * i)) & 15ull : 0ull;
+            valid |= ok4 << (4 * i);
+            if (vec_x) {
+                pre[i] = *reinterpret_cast<const f32x4 *>(xbase + (ok4 ? sbase + goff[i] : 0u));
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    pre[i][q] = *reinterpret_cast<const float *>(
+                        xbase + ((ok4 >> q) & 1 ? sbase + goff[i] + 4u * q : 0u));
+            }
+        }
+    };
+    auto place = [&]() {
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+            const int e = tid + 256 * i;
+            if (e < CH * ROWS * G4) {
+                f32x4 v;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    v[q] = (valid >> (4 * i + q)) & 1 ? pre[i][q] : 0.f;
+                *reinterpret_cast<f32x4 *>(win + 4 * e) = v;
+            }
+        }
+    };
+
+    if (s0 < s1) {
+        fetch(s0);
+        place();
+    }
+    __syncthreads();  // the weights and the first window are in LDS
     for (int64_t st = s0; st < s1; ++st) {
         const int b = (int)(st / strips_per_image);
         const int p0 = (int)(st - (int64_t)b * strips_per_image) * kStemStrip;
         const int oh_lo = p0 / a.OW;
-        const int ih_lo = oh_lo * SH - a.ph;
+        // The next strip's window travels while this one is computed.
+        if (st + 1 < s1) fetch(st + 1);
 
-        __syncthreads();  // every wave is done with the previous window
-        constexpr int G4 = WPITCH / 4;
-        for (int e = tid; e < CH * ROWS * G4; e += 256) {
-            const int rowid = e / G4, g = e - rowid * G4;
-            const int c = rowid / ROWS, ih = ih_lo + rowid % ROWS;
-            const int iw0 = 4 * g - kStemCol0;
-            f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (ih >= 0 && ih < a.H) {
-                const float *xr = a.X + (((int64_t)b * a.C + c) * a.H + ih) * a.W;
-                if (vec_x && iw0 >= 0 && iw0 + 3 < a.W) {
-                    v = *reinterpret_cast<const f32x4 *>(xr + iw0);
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (iw0 + q >= 0 && iw0 + q < a.W) v[q] = xr[iw0 + q];
-                }
-            }
-            *reinterpret_cast<f32x4 *>(win + rowid * WPITCH + 4 * g) = v;
-        }
-        __syncthreads();
-
-        // Per-lane window bases for the wave's two column blocks (positions
-        // past the image clamp to its last one; their outputs are not stored).
+        // Per-lane window bases.  Lane j of a wave holds positions 2j and
+        // 2j + 1 of the wave's 64 (column blocks cb = 0, 1 interleaved), so its
+        // two outputs of a row are adjacent.  Positions past the image clamp
+        // to its last one; their outputs are not stored.
         int base[2][4];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-            int q = p0 + wave * 64 + cb * 32 + j;
+            int q = p0 + wave * 64 + 2 * j + cb;
             q = q < ohw ? q : ohw - 1;
             const int oh = q / a.OW, ow = q - oh * a.OW;
             const int pb = (oh - oh_lo) * SH * WPITCH + ow * SW - a.pw + kStemCol0;
@@ -335,25 +405,38 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
                                                                        acc[mb][cb], 0, 0, 0);
         }
 
-        // Epilogue: a half-wave writes 32 consecutive positions of a row of Y.
+        // Epilogue: a half-wave writes 64 consecutive positions of a row of
+        // Y, two per lane.
         const float alpha = a.alpha, beta = a.beta;
+        const int q0 = p0 + wave * 64 + 2 * j;
+        const uint32_t n0 = (uint32_t)(b * ohw + q0);
+        const uint32_t ldy = (uint32_t)a.ldy;
+        const bool both = q0 + 1 < ohw;
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            const int q = p0 + wave * 64 + cb * 32 + j;
-            if (q >= ohw) continue;
-            const int64_t n = (int64_t)b * ohw + q;
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int row = mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-                    if (row >= a.M) continue;
-                    float *py = a.Y + (int64_t)row * a.ldy + n;
-                    float v = alpha * acc[mb][cb][i];
-                    if (beta != 0.f) v = fmaf(beta, *py, v);
-                    __builtin_nontemporal_store(v, py);
+            for (int i = 0; i < 16; ++i) {
+                const int row = mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+                if (row >= a.M || q0 >= ohw) continue;
+                float *py = reinterpret_cast<float *>(ybase + ((uint32_t)row * ldy + n0) * 4u);
+                float v0 = alpha * acc[mb][0][i], v1 = alpha * acc[mb][1][i];
+                if (vec_y && both) {
+                    f32x2 v = {v0, v1};
+                    if (beta != 0.f) v += beta * *reinterpret_cast<const f32x2 *>(py);
+                    __builtin_nontemporal_store(v, reinterpret_cast<f32x2 *>(py));
+                } else {
+                    if (beta != 0.f) v0 = fmaf(beta, py[0], v0);
+                    __builtin_nontemporal_store(v0, py);
+                    if (both) {
+                        if (beta != 0.f) v1 = fmaf(beta, py[1], v1);
+                        __builtin_nontemporal_store(v1, py + 1);
+                    }
                 }
-        }
+            }
+
+        __syncthreads();  // every wave is done with this window
+        if (st + 1 < s1) place();
+        __syncthreads();
     }
 }
 

@@ -44,7 +44,8 @@ enum sconv_variant {
                                * positions; only the geometries it is built for
                                * (3 channels, 7x7 or 3x3 filters at stride 2,
                                * pad <= 4, images up to 224 + padding wide,
-                               * out_channels <= 64); others return
+                               * out_channels <= 64, X and Y under 4 GiB);
+                               * others return
                                * SGEMM_ERR_VARIANT_SHAPE (include/sgemm.h) */
     SCONV_VARIANT_GENERAL = 2 /* any geometry: 64 x 64 output tiles, taps gathered
                                * from X into LDS in slabs of 16 */
