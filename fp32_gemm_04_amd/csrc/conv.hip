@@ -247,13 +247,12 @@ extern "C" int sgemm_im2col_f32(int batch, int channels, int height, int width, 
     a.OW = OW;
     a.K = channels * kernel_h * kernel_w;
     a.N = N;
-    const int kgroup = a.K < 32 ? a.K : 32;
     const int64_t gx = ceil_div64(N, 1024);
-    const int64_t gy = ceil_div64(a.K, kgroup);
+    const int64_t gy = ceil_div64(a.K, kIm2colRows);
     if (gx > INT_MAX || gy > 65535) return (int)hipErrorInvalidConfiguration;
     const int vec = (((uintptr_t)B & 15u) == 0 && ldb % 4 == 0) ? 1 : 0;
     hipLaunchKernelGGL(im2col_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, a,
-                       B, (int64_t)ldb, kgroup, vec);
+                       B, (int64_t)ldb, 0, vec);
     return (int)hipGetLastError();
 }
 

@@ -40,17 +40,22 @@ typedef void (*ConvKernelFn)(ConvArgs, int, int);
 
 // ---------------------------------------------------------------- im2col
 
-// Each thread writes columns n0 .. n0+3 of rows k0 .. k1-1 of B (K x N,
-// row pitch ldb), non-temporal (B is written once, for a later kernel).
-// vec: B's base is 16-byte aligned and ldb % 4 == 0, so a whole group of
-// four is one 128-bit store.
-__global__ void __launch_bounds__(256) im2col_kernel(ConvArgs a, float *B, int64_t ldb, int kgroup,
-                                                     int vec)
+// Each thread writes columns n0 .. n0+3 of rows k0 .. k0+3 of B (K x N, row
+// pitch ldb), non-temporal (B is written once, for a later kernel): its 16
+// input loads are all issued before its 4 stores, so each thread keeps 16
+// loads in flight.  Rows k0 .. k0+3 are the same for the whole workgroup
+// (blockIdx.y); consecutive workgroups write consecutive 4 KB pieces of
+// those rows.  vec: B's base is 16-byte aligned and ldb % 4 == 0, so a
+// group of four columns is one 128-bit store.
+constexpr int kIm2colRows = 4;
+
+__global__ void __launch_bounds__(256) im2col_kernel(ConvArgs a, float *__restrict__ B,
+                                                     int64_t ldb, int, int vec)
 {
+    const float *__restrict__ X = a.X;
     const int64_t n0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (n0 >= a.N) return;
-    const int k0 = blockIdx.y * kgroup;
-    const int k1 = k0 + kgroup < a.K ? k0 + kgroup : a.K;
+    const int k0 = blockIdx.y * kIm2colRows;
     const int ohw = a.OH * a.OW;
     int ihb[4], iwb[4];
     int64_t xb[4];
@@ -65,30 +70,29 @@ __global__ void __launch_bounds__(256) im2col_kernel(ConvArgs a, float *B, int64
         iwb[q] = ow * a.sw - a.pw;
         xb[q] = (int64_t)b * a.C * a.H * a.W;
     }
-    int c = k0 / (a.R * a.S), r = (k0 / a.S) % a.R, s = k0 % a.S;
-    for (int k = k0; k < k1; ++k) {
-        f32x4 v;
+    f32x4 v[kIm2colRows];
+#pragma unroll
+    for (int kk = 0; kk < kIm2colRows; ++kk) {
+        const int k = k0 + kk < a.K ? k0 + kk : a.K - 1;
+        const int c = k / (a.R * a.S), r = (k / a.S) % a.R, s = k % a.S;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int ih = ihb[q] + r, iw = iwb[q] + s;
-            v[q] = (ih >= 0 && ih < a.H && iw >= 0 && iw < a.W)
-                       ? a.X[xb[q] + ((int64_t)c * a.H + ih) * a.W + iw]
-                       : 0.f;
+            v[kk][q] = (ih >= 0 && ih < a.H && iw >= 0 && iw < a.W)
+                           ? X[xb[q] + ((int64_t)c * a.H + ih) * a.W + iw]
+                           : 0.f;
         }
-        float *dst = B + (int64_t)k * ldb + n0;
+    }
+#pragma unroll
+    for (int kk = 0; kk < kIm2colRows; ++kk) {
+        if (k0 + kk >= a.K) break;
+        float *dst = B + (int64_t)(k0 + kk) * ldb + n0;
         if (vec && n0 + 3 < a.N) {
-            __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(dst));
+            __builtin_nontemporal_store(v[kk], reinterpret_cast<f32x4 *>(dst));
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (n0 + q < a.N) __builtin_nontemporal_store(v[q], dst + q);
-        }
-        if (++s == a.S) {
-            s = 0;
-            if (++r == a.R) {
-                r = 0;
-                ++c;
-            }
+                if (n0 + q < a.N) __builtin_nontemporal_store(v[kk][q], dst + q);
         }
     }
 }
