@@ -445,6 +445,21 @@ def bench_conv(sg, stream, check=True):
             "hbm_gbps": round(case.alg_bytes / (ms * 1e-3) / 1e9, 1),
             "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4),
             "frac_roofline": round(roof_us / (ms * 1e3), 4)}
+        if plan.startswith("direct") or plan.startswith("tile"):
+            # The other implicit forms on the same sets, for comparison: the
+            # register-staged tile kernel and the general 64 x 64 kernel.
+            forms = [("general_us", sg.SCONV_VARIANT_GENERAL)]
+            if plan.startswith("direct"):
+                forms.insert(0, ("tile_us", sg.SCONV_VARIANT_TILE))
+            for key, v in forms:
+                def other(i, v=v):
+                    rc = sg.sconv2d_f32_variant(v, *g, 1.0, dX[i].data_ptr(), dW.data_ptr(),
+                                                case.K, 0.0, dY[i].data_ptr(), case.N,
+                                                stream.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(sg.sgemm_status_string(rc))
+                o_ms, _ = steady_state(other, nset, stream)
+                entry[key] = round(o_ms * 1e3, 2)
         if check:
             log("verify", case.name)
             conv(0)
@@ -567,10 +582,10 @@ def config_by_name(name):
         c.name for c in workloads.ALL + workloads.CONV_STEMS + workloads.CONV_MID)))
 
 
-def conv_sets(sg, case, stream, nset=None):
+def conv_sets(sg, case, stream, nset=None, variant=0):
     """Rotating input/output copies of a convolution reading (at least
-    1.6 GB in all, unless nset is given) and a launch(i) running sconv2d_f32
-    on set i."""
+    1.6 GB in all, unless nset is given) and a launch(i) running
+    sconv2d_f32_variant(variant) (0: what sconv2d_f32 picks) on set i."""
     import torch
     X, Wt = workloads.conv_operands(case)
     dW = torch.from_numpy(Wt).cuda()
@@ -582,8 +597,9 @@ def conv_sets(sg, case, stream, nset=None):
     dY = [torch.zeros((case.M, case.N), dtype=torch.float32, device="cuda") for _ in range(nset)]
 
     def launch(i):
-        rc = sg.sconv2d_f32(*case.geometry, 1.0, dX[i].data_ptr(), dW.data_ptr(), case.K, 0.0,
-                            dY[i].data_ptr(), case.N, stream.cuda_stream)
+        rc = sg.sconv2d_f32_variant(variant, *case.geometry, 1.0, dX[i].data_ptr(),
+                                    dW.data_ptr(), case.K, 0.0, dY[i].data_ptr(), case.N,
+                                    stream.cuda_stream)
         if rc != 0:
             raise RuntimeError(sg.sgemm_status_string(rc))
     return X, Wt, dX, dW, dY, launch

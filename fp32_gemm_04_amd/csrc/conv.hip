@@ -1,6 +1,6 @@
-// libsgemm convolution entry points: argument checks, the choice between
-// the stem kernel and the general implicit-GEMM kernel, and the im2col
-// producer, behind the C ABI declared in include/sconv.h.  Like the GEMM
+// libsgemm convolution entry points: argument checks, the choice among the
+// stem kernel, the MFMA tile kernels and the general implicit-GEMM kernel,
+// and the im2col producer, behind the C ABI declared in include/sconv.h.  Like the GEMM
 // entry points, nothing here allocates, frees, copies or synchronises: work
 // is queued on the caller's stream.
 #include <hip/hip_runtime.h>
@@ -36,8 +36,11 @@ int check_geometry(const Geometry &q, int *OH, int *OW, int64_t *N)
     if (q.sw < 1) return -9;
     if (q.ph < 0) return -10;
     if (q.pw < 0) return -11;
-    if ((int64_t)q.H + 2 * q.ph < q.R) return -6;
-    if ((int64_t)q.W + 2 * q.pw < q.S) return -7;
+    if ((int64_t)q.H + 2 * (int64_t)q.ph < q.R) return -6;
+    if ((int64_t)q.W + 2 * (int64_t)q.pw < q.S) return -7;
+    // Padded extents stay in int, so every input coordinate a kernel forms does.
+    if ((int64_t)q.H + 2 * (int64_t)q.ph > INT_MAX) return -10;
+    if ((int64_t)q.W + 2 * (int64_t)q.pw > INT_MAX) return -11;
     if ((int64_t)q.C * q.R * q.S > INT_MAX) return -2;
     *OH = (q.H + 2 * q.ph - q.R) / q.sh + 1;
     *OW = (q.W + 2 * q.pw - q.S) / q.sw + 1;
@@ -91,6 +94,109 @@ const StemEntry *stem_for(const Geometry &q, int OH, int OW)
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The MFMA tile kernels built: tile and waves; all run two waves per SIMD
+// (two 4-wave workgroups or one 8-wave workgroup per CU).
+struct TileEntry {
+    int bm, bn, waves;
+    ConvKernelFn fn;
+};
+
+#define SGEMM_CONV_TILE(BM, BN, WM, WN) {BM, BN, WM * WN, conv_tile_kernel<BM, BN, WM, WN, 2>}
+
+const TileEntry kTiles[] = {
+    SGEMM_CONV_TILE(128, 128, 2, 2),
+    SGEMM_CONV_TILE(192, 128, 4, 2),
+    SGEMM_CONV_TILE(64, 128, 1, 4),
+};
+
+// The direct-to-LDS forms: filter, tile, waves (two waves per SIMD too).
+struct DlEntry {
+    int R, S, bm, bn, waves;
+    ConvKernelFn fn;
+};
+
+#define SGEMM_CONV_DL(BM, BN, WM, WN, R, S) \
+    {R, S, BM, BN, WM * WN, conv_dl_kernel<BM, BN, WM, WN, 2, R, S>}
+
+const DlEntry kDlTiles[] = {
+    SGEMM_CONV_DL(128, 128, 2, 2, 3, 3), SGEMM_CONV_DL(192, 128, 4, 2, 3, 3),
+    SGEMM_CONV_DL(64, 128, 1, 4, 3, 3),  SGEMM_CONV_DL(128, 128, 2, 2, 1, 1),
+    SGEMM_CONV_DL(192, 128, 4, 2, 1, 1), SGEMM_CONV_DL(64, 128, 1, 4, 1, 1),
+};
+
+// The general kernel's rate relative to the tile kernels' (measured on the
+// 3 x 3 readings: about 0.3 against 0.6 and more of the matrix peak).
+constexpr int64_t kGeneralCost = 2;
+
+// Work of the busiest CU, in multiply-adds per tap: ceil(tiles / CUs)
+// tiles of bm x bn each (the tiles are spread evenly over the CUs, and
+// those sharing a CU share its matrix cores).
+int64_t tile_cost(int64_t M, int64_t N, int bm, int bn, int cus)
+{
+    const int64_t tiles = ceil_div64(M, bm) * ceil_div64(N, bn);
+    return ceil_div64(tiles, cus) * bm * bn;
+}
+
+// Whether the tile kernels can address the problem: X and the filter rows
+// it reads under 2^31 bytes (raw buffer offsets), N short of INT_MAX by a
+// tile.
+bool tile_fits(const Geometry &q, int64_t N, int ldw)
+{
+    const int64_t x_bytes = 4 * (int64_t)q.batch * q.C * q.H * q.W;
+    const int64_t w_bytes = 4 * ((int64_t)(q.M > 0 ? q.M - 1 : 0) * ldw + (int64_t)q.C * q.R * q.S);
+    return x_bytes < (1ll << 31) && w_bytes < (1ll << 31) && N <= INT_MAX - 256;
+}
+
+// The tile kernel for this problem, or null for the general kernel: among
+// those built, the least busiest-CU work, scaled by the channel padding of
+// the tile kernels' 16-channel slabs, against the general kernel's 64 x 64
+// tiles at kGeneralCost.
+const TileEntry *tile_for(const Geometry &q, int64_t N, int cus)
+{
+    const int64_t K = (int64_t)q.C * q.R * q.S;
+    const int64_t Kpad = (int64_t)((q.C + 15) / 16) * 16 * q.R * q.S;
+    const TileEntry *best = nullptr;
+    // Compared in units of work * K.
+    int64_t best_cost = kGeneralCost * tile_cost(q.M, N, kConvTile, kConvTile, cus) * K;
+    for (const TileEntry &e : kTiles) {
+        const int64_t c = tile_cost(q.M, N, e.bm, e.bn, cus) * Kpad;
+        if (c < best_cost) {
+            best = &e;
+            best_cost = c;
+        }
+    }
+    return best;
+}
+
+// The direct-to-LDS kernel for this problem, or null: the filter must be one
+// built, K a multiple of 16, the filter rows 16-byte aligned, and the tile
+// kernels' limits hold; among those built, the least busiest-CU work.
+const DlEntry *dl_for(const Geometry &q, int64_t N, const float *Wt, int ldw, int cus)
+{
+    const int64_t K = (int64_t)q.C * q.R * q.S;
+    if (K % 16 != 0 || ldw % 4 != 0 || ((uintptr_t)Wt & 15u) != 0 || !tile_fits(q, N, ldw))
+        return nullptr;
+    const DlEntry *best = nullptr;
+    for (const DlEntry &e : kDlTiles) {
+        if (e.R != q.R || e.S != q.S) continue;
+        if (best == nullptr ||
+            tile_cost(q.M, N, e.bm, e.bn, cus) < tile_cost(q.M, N, best->bm, best->bn, cus))
+            best = &e;
+    }
+    return best;
+}
+
+// The tile kernel with the least busiest-CU work, for the forced tile form.
+const TileEntry *tile_forced(const Geometry &q, int64_t N, int cus)
+{
+    const TileEntry *best = nullptr;
+    for (const TileEntry &e : kTiles)
+        if (best == nullptr ||
+            tile_cost(q.M, N, e.bm, e.bn, cus) < tile_cost(q.M, N, best->bm, best->bn, cus))
+            best = &e;
+    return best;
+}
+
 // Per-device compute-unit count, cached.
 constexpr int kConvMaxDevices = 64;
 int g_conv_cus[kConvMaxDevices];
@@ -116,7 +222,7 @@ hipError_t conv_device_cus(int *cus)
 int conv_launch(int variant, const Geometry &q, float alpha, const float *X, const float *Wt,
                 int ldw, float beta, float *Y, int ldy, hipStream_t stream)
 {
-    if (variant < SCONV_VARIANT_AUTO || variant > SCONV_VARIANT_GENERAL) return SGEMM_ERR_BAD_VARIANT;
+    if (variant < SCONV_VARIANT_AUTO || variant > SCONV_VARIANT_DIRECT) return SGEMM_ERR_BAD_VARIANT;
     int OH = 0, OW = 0;
     int64_t N = 0;
     const int bad = check_geometry(q, &OH, &OW, &N);
@@ -134,6 +240,10 @@ int conv_launch(int variant, const Geometry &q, float alpha, const float *X, con
     const int64_t y_bytes = 4 * (int64_t)q.M * ldy;
     if (x_bytes >= (1ll << 32) || y_bytes >= (1ll << 32)) stem = nullptr;
     if (variant == SCONV_VARIANT_STEM && stem == nullptr) return SGEMM_ERR_VARIANT_SHAPE;
+    const bool tile_ok = tile_fits(q, N, ldw);
+    if (variant == SCONV_VARIANT_TILE && !tile_ok) return SGEMM_ERR_VARIANT_SHAPE;
+    if (variant == SCONV_VARIANT_DIRECT && dl_for(q, N, Wt, ldw, 1) == nullptr)
+        return SGEMM_ERR_VARIANT_SHAPE;
     if (q.M == 0 || N == 0) return 0;
 
     if (alpha == 0.0f) {
@@ -168,10 +278,10 @@ int conv_launch(int variant, const Geometry &q, float alpha, const float *X, con
     a.alpha = alpha;
     a.beta = beta;
 
-    if (stem != nullptr && variant != SCONV_VARIANT_GENERAL) {
-        int cus = 0;
-        const hipError_t e = conv_device_cus(&cus);
-        if (e != hipSuccess) return (int)e;
+    int cus = 0;
+    const hipError_t ce = conv_device_cus(&cus);
+    if (ce != hipSuccess) return (int)ce;
+    if (stem != nullptr && (variant == SCONV_VARIANT_AUTO || variant == SCONV_VARIANT_STEM)) {
         const int spi = (int)ceil_div64((int64_t)OH * OW, kStemStrip);
         const int64_t total = (int64_t)spi * q.batch;
         if (total > INT_MAX) return (int)hipErrorInvalidConfiguration;
@@ -180,6 +290,33 @@ int conv_launch(int variant, const Geometry &q, float alpha, const float *X, con
         const int64_t grid = total < resident ? total : resident;
         hipLaunchKernelGGL(stem->fn, dim3((unsigned)grid), dim3(256), 0, stream, a, spi,
                            (int)total);
+        return (int)hipGetLastError();
+    }
+    const TileEntry *tile = !tile_ok                          ? nullptr
+                            : variant == SCONV_VARIANT_TILE ? tile_forced(q, N, cus)
+                            : variant == SCONV_VARIANT_AUTO ? tile_for(q, N, cus)
+                                                            : nullptr;
+    // The direct-to-LDS form where it applies, in the tile kernels' place.
+    const DlEntry *dl = variant == SCONV_VARIANT_DIRECT ? dl_for(q, N, Wt, ldw, cus)
+                        : (variant == SCONV_VARIANT_AUTO && tile != nullptr)
+                            ? dl_for(q, N, Wt, ldw, cus)
+                            : nullptr;
+    if (dl != nullptr) {
+        const int tiles_m = (int)ceil_div64(q.M, dl->bm);
+        const int tiles_n = (int)ceil_div64(N, dl->bn);
+        const int64_t blocks = (int64_t)tiles_m * tiles_n;
+        if (blocks > INT_MAX) return (int)hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(dl->fn, dim3((unsigned)blocks), dim3(64 * dl->waves), 0, stream, a,
+                           tiles_m, tiles_n);
+        return (int)hipGetLastError();
+    }
+    if (tile != nullptr) {
+        const int tiles_m = (int)ceil_div64(q.M, tile->bm);
+        const int tiles_n = (int)ceil_div64(N, tile->bn);
+        const int64_t blocks = (int64_t)tiles_m * tiles_n;
+        if (blocks > INT_MAX) return (int)hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(tile->fn, dim3((unsigned)blocks), dim3(64 * tile->waves), 0, stream, a,
+                           tiles_m, tiles_n);
         return (int)hipGetLastError();
     }
     const int tiles_m = (int)ceil_div64(q.M, kConvTile);
@@ -261,7 +398,7 @@ extern "C" int sconv2d_plan(int variant, int batch, int channels, int height, in
                             int stride_w, int pad_h, int pad_w, int num_cus, char *buf, int buflen)
 {
     using namespace sgemm;
-    if (variant < SCONV_VARIANT_AUTO || variant > SCONV_VARIANT_GENERAL) return SGEMM_ERR_BAD_VARIANT;
+    if (variant < SCONV_VARIANT_AUTO || variant > SCONV_VARIANT_DIRECT) return SGEMM_ERR_BAD_VARIANT;
     const Geometry q = {batch,    channels, height,   width,    out_channels, kernel_h,
                         kernel_w, stride_h, stride_w, pad_h,    pad_w};
     int OH = 0, OW = 0;
@@ -275,10 +412,27 @@ extern "C" int sconv2d_plan(int variant, int batch, int channels, int height, in
         4 * (int64_t)out_channels * N >= (1ll << 32))
         stem = nullptr;
     if (variant == SCONV_VARIANT_STEM && stem == nullptr) return SGEMM_ERR_VARIANT_SHAPE;
+    // Packed filters (ldw = K) assumed.
+    const bool tile_ok = tile_fits(q, N, channels * kernel_h * kernel_w);
+    const TileEntry *tile = !tile_ok                          ? nullptr
+                            : variant == SCONV_VARIANT_TILE ? tile_forced(q, N, num_cus)
+                            : variant == SCONV_VARIANT_AUTO ? tile_for(q, N, num_cus)
+                                                            : nullptr;
+    if (variant == SCONV_VARIANT_TILE && tile == nullptr) return SGEMM_ERR_VARIANT_SHAPE;
+    // Packed, 16-byte aligned filters assumed.
+    static const float kAligned[4] = {0.f, 0.f, 0.f, 0.f};
+    const float *wt_aligned = reinterpret_cast<const float *>(
+        (reinterpret_cast<uintptr_t>(kAligned) + 15u) & ~(uintptr_t)15u);
+    const int K = channels * kernel_h * kernel_w;
+    const DlEntry *dl = variant == SCONV_VARIANT_DIRECT ? dl_for(q, N, wt_aligned, K, num_cus)
+                        : (variant == SCONV_VARIANT_AUTO && tile != nullptr)
+                            ? dl_for(q, N, wt_aligned, K, num_cus)
+                            : nullptr;
+    if (variant == SCONV_VARIANT_DIRECT && dl == nullptr) return SGEMM_ERR_VARIANT_SHAPE;
     char text[200];
     if (out_channels == 0 || N == 0) {
         std::snprintf(text, sizeof text, "none");
-    } else if (stem != nullptr && variant != SCONV_VARIANT_GENERAL) {
+    } else if (stem != nullptr && (variant == SCONV_VARIANT_AUTO || variant == SCONV_VARIANT_STEM)) {
         const int spi = (int)ceil_div64((int64_t)OH * OW, kStemStrip);
         const int64_t total = (int64_t)spi * batch;
         const int64_t resident = (int64_t)num_cus * stem->wpe;
@@ -287,6 +441,15 @@ extern "C" int sconv2d_plan(int variant, int batch, int channels, int height, in
                       stem->mb, channels * kernel_h * kernel_w, channels, stem->rows, stem->wpitch,
                       kStemStrip, (long long)total, (long long)(total < resident ? total : resident),
                       OH, OW);
+    } else if (dl != nullptr) {
+        const int64_t tiles = ceil_div64(out_channels, dl->bm) * ceil_div64(N, dl->bn);
+        std::snprintf(text, sizeof text, "direct bm=%d bn=%d waves=%d k=%d grid=%lld oh=%d ow=%d",
+                      dl->bm, dl->bn, dl->waves, K, (long long)tiles, OH, OW);
+    } else if (tile != nullptr) {
+        const int64_t tiles = ceil_div64(out_channels, tile->bm) * ceil_div64(N, tile->bn);
+        std::snprintf(text, sizeof text, "tile bm=%d bn=%d waves=%d k=%d grid=%lld oh=%d ow=%d",
+                      tile->bm, tile->bn, tile->waves, channels * kernel_h * kernel_w,
+                      (long long)tiles, OH, OW);
     } else {
         const int64_t tiles = ceil_div64(out_channels, kConvTile) * ceil_div64(N, kConvTile);
         std::snprintf(text, sizeof text, "general tile=%dx%d k=%d grid=%lld oh=%d ow=%d",

@@ -18,6 +18,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "mfma_dl.hpp"
 
 namespace sgemm {
 
@@ -186,6 +187,504 @@ __global__ void __launch_bounds__(256) conv_gemm_kernel(ConvArgs a, int tiles_m,
         float v = a.alpha * acc[i];
         if (a.beta != 0.f) v = fmaf(a.beta, *py, v);
         *py = v;
+    }
+}
+
+// ------------------------------------------------ implicit GEMM, MFMA tiles
+
+// One BM x BN tile of Y per workgroup, for any filter, channel count,
+// stride and padding: the shape of an image network's middle layers (many
+// channels, small filters), where the contraction K = C R S is long and the
+// work is dense.  The matrix-core pipeline is that of the GEMM tile kernel:
+// slabs of 16 taps, v_mfma_f32_16x16x4_f32, a wave per (BM / WM) x (BN / WN)
+// sub-tile, three LDS buffers per operand with the registers holding the
+// slab after next's loads, one barrier per slab.
+//
+// The order of the contraction is changed (a sum may take its terms in any
+// order): slab t covers filter tap (r, s) = rs(t) and channels
+// 16 cb .. 16 cb + 15, with cb = t / RS, rs = t % RS (channels past C are
+// zeros).  A slab's tap is then the same for every element of it, so:
+//   - a tap of output position n in channel c is X at
+//     base(n) + c H W + r W + s, base(n) the input offset of (b, 0, oh sh -
+//     ph, ow sw - pw): a per-thread part (base(n) + r W + s, worked out once
+//     per slab) plus a wave-uniform part (c H W), which is what a raw buffer
+//     load takes as its vector and scalar offsets;
+//   - a tap outside the image (or past N) gets a vector offset beyond the
+//     buffer's size, for which the hardware returns zero: no select after
+//     the load, so nothing waits for it before it is stored to LDS;
+//   - the filter element (m, c, r, s) is Wt at m ldw + c RS + rs: a
+//     per-thread offset (row and channel in the slab) plus a wave-uniform
+//     one (16 cb RS + rs).
+// Consecutive slabs walk the taps of one block of channels, so they read
+// the same lines of X and Wt.  Rows past M, positions past N and channels
+// past C are zeros; the epilogue writes alpha acc + beta Y (Y not read when
+// beta == 0) inside the window.  X and Wt must each be under 2^31 bytes.
+//
+// Thread roles per slab: B element (kk, col) with col = tid % BN and
+// kk = tid / BN + (NT / BN) i (kk, hence the channel, is the same for all
+// lanes of a wave); A element (m, kk) with kk = tid % 16 and
+// m = tid / 16 + (NT / 16) j.
+//
+// MFMA operand layout as in the GEMM tile kernel (lane l: A[l % 16][k],
+// B[k][l % 16] with k = 4 (l / 16) + step; D[4 (l / 16) + i][l % 16]).
+// LDS: A m-major with pitch 24 floats, B k-major with pitch BN + 4.
+template <int BM, int BN, int WM, int WN>
+struct ConvTile {
+    static constexpr int NT = WM * WN * 64;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 16, FN = TN / 16;
+    static constexpr int BK = 16;
+    static constexpr int SA = BK + 8, SB = BN + 4;
+    static constexpr int NA = BM * BK / NT;  // filter elements per thread per slab
+    static constexpr int NB = BK * BN / NT;  // taps per thread per slab
+    static constexpr int LDS_A = BM * SA, LDS_B = BK * SB;
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert(BN % 64 == 0 && NT % BN == 0 && NB >= 1, "a wave's taps share one channel");
+    static_assert(NT % BK == 0 && (BM * BK) % NT == 0, "filter slab splits evenly");
+};
+
+// Buffer descriptor word 3 for raw 32-bit loads (data format 32).
+constexpr int kBufferWord3 = 0x00020000;
+// A vector offset no buffer here reaches (buffers are under 2^31 bytes):
+// loads through it return zero.
+constexpr uint32_t kOffsetOut = 0x80000000u;
+
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff)
+{
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+
+template <int BM, int BN, int WM, int WN, int WPE>
+__global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+conv_tile_kernel(ConvArgs a, int tiles_m, int tiles_n)
+{
+    using T = ConvTile<BM, BN, WM, WN>;
+    constexpr int NT = T::NT, TM = T::TM, TN = T::TN, FM = T::FM, FN = T::FN;
+    constexpr int BK = T::BK, SA = T::SA, SB = T::SB, NA = T::NA, NB = T::NB;
+    __shared__ __attribute__((aligned(16))) float As[3 * T::LDS_A];
+    __shared__ __attribute__((aligned(16))) float Bs[3 * T::LDS_B];
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, tiles_m, tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int M = a.M, N = (int)a.N, C = a.C, S = a.S;
+    const int RS = a.R * a.S;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int wr = wave / WN, wc = wave % WN;
+    const int lm = lane & 15, lg = lane >> 4;
+
+    const uint32_t x_bytes = 4u * (uint32_t)a.batch * (uint32_t)C * (uint32_t)a.H * (uint32_t)a.W;
+    const uint32_t w_bytes = 4u * ((uint32_t)(M - 1) * (uint32_t)a.ldw + (uint32_t)a.K);
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.X), 0, (int)x_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t wr_ =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.Wt), 0, (int)w_bytes, kBufferWord3);
+
+    // Filter elements: channel akk of the slab, rows am0 + (NT / 16) j.
+    const int akk = tid % BK, am0 = tid / BK;
+    uint32_t a_off[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+        const int m = m0 + am0 + (NT / BK) * j;
+        a_off[j] = m < M ? 4u * ((uint32_t)m * (uint32_t)a.ldw + (uint32_t)akk * (uint32_t)RS)
+                         : kOffsetOut;
+    }
+
+    // Taps: this thread's output position, fixed for the tile.
+    const int col = tid % BN;
+    const int krow = wave_s * 64 / BN;  // first slab row of this wave; then + NT / BN
+    const int n = n0 + col;
+    const bool n_ok = n < N;
+    int ih0 = 0, iw0 = 0;
+    uint32_t pbase = 0;  // element offset of (b, 0, ih0, iw0), modulo 2^32
+    if (n_ok) {
+        const int ohw = a.OH * a.OW;
+        const int b = n / ohw;
+        const int p = n - b * ohw;
+        const int oh = p / a.OW, ow = p - oh * a.OW;
+        ih0 = oh * a.sh - a.ph;
+        iw0 = ow * a.sw - a.pw;
+        pbase = ((uint32_t)(b * C * a.H) + (uint32_t)ih0) * (uint32_t)a.W + (uint32_t)iw0;
+    }
+    const uint32_t hw4 = 4u * (uint32_t)a.H * (uint32_t)a.W;
+
+    float ra[NA], rb[NB];
+    // Slab t: channel block cb, filter tap (r, s) (wave-uniform).
+    auto fetch = [&](int cb, int r, int s) {
+        const int rs = r * S + s;
+        const int c0 = cb * BK;
+        const uint32_t a_soff = 4u * ((uint32_t)c0 * (uint32_t)RS + (uint32_t)rs);
+        const bool a_c_ok = c0 + akk < C;
+#pragma unroll
+        for (int j = 0; j < NA; ++j)
+            ra[j] = buffer_load_f32(wr_, a_c_ok ? a_off[j] : kOffsetOut, a_soff);
+        const bool tap_in = n_ok && (unsigned)(ih0 + r) < (unsigned)a.H &&
+                            (unsigned)(iw0 + s) < (unsigned)a.W;
+        const uint32_t b_voff =
+            tap_in ? 4u * (pbase + (uint32_t)r * (uint32_t)a.W + (uint32_t)s) : kOffsetOut;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int c = c0 + krow + (NT / BN) * i;  // wave-uniform
+            const bool c_ok = c < C;
+            rb[i] = buffer_load_f32(xr, c_ok ? b_voff : kOffsetOut, c_ok ? (uint32_t)c * hw4 : 0u);
+        }
+    };
+    auto stash = [&](int buf) {
+        float *as = As + buf * T::LDS_A;
+        float *bs = Bs + buf * T::LDS_B;
+#pragma unroll
+        for (int j = 0; j < NA; ++j) as[(am0 + (NT / BK) * j) * SA + akk] = ra[j];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) bs[(krow + (NT / BN) * i) * SB + col] = rb[i];
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int a_frag = (wr * TM + lm) * SA + 4 * lg;
+    const int b_frag = (4 * lg) * SB + wc * TN + lm;
+    // The slab's 4 k-steps; hook() runs before k-step 1 (the next slab's
+    // registers go to LDS there, behind MFMAs in flight).
+    auto compute = [&](int buf, auto hook) {
+        const float *as = As + buf * T::LDS_A + a_frag;
+        const float *bs = Bs + buf * T::LDS_B + b_frag;
+        f32x4 af[FM];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            af[fm] = *reinterpret_cast<const f32x4 *>(as + fm * 16 * SA);
+        float bf[4][FN];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) bf[s][fn] = bs[s * SB + fn * 16];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s == 1) hook();
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[fm][s], bf[s][fn],
+                                                                       acc[fm][fn], 0, 0, 0);
+        }
+    };
+
+    // Slab t is read from buffer t % 3.  The registers hold slab t + 1
+    // while slab t runs; they go to buffer (t + 1) % 3 inside slab t's MFMAs
+    // and are refilled with slab t + 2.  That buffer was last read in slab
+    // t - 2, which every wave left before the barrier that ended it.
+    const int nslab = ((C + BK - 1) / BK) * RS;
+    int f_cb = 0, f_r = 0, f_s = 0;  // the next slab to fetch
+    auto advance = [&] {
+        if (++f_s == S) {
+            f_s = 0;
+            if (++f_r == a.R) {
+                f_r = 0;
+                ++f_cb;
+            }
+        }
+    };
+    fetch(f_cb, f_r, f_s);
+    advance();
+    stash(0);
+    if (nslab > 1) {
+        fetch(f_cb, f_r, f_s);
+        advance();
+    }
+    __syncthreads();
+    int cur = 0;
+    for (int t = 0; t < nslab; ++t) {
+        const int nxt = cur == 2 ? 0 : cur + 1;
+        const bool more = t + 1 < nslab;
+        const bool more2 = t + 2 < nslab;
+        compute(cur, [&] {
+            if (more) {
+                stash(nxt);
+                if (more2) {
+                    fetch(f_cb, f_r, f_s);
+                    advance();
+                }
+            }
+        });
+        __syncthreads();
+        cur = nxt;
+    }
+
+    const float alpha = a.alpha, beta = a.beta;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + wr * TM + fm * 16 + 4 * lg + i;
+            if (row >= M) continue;
+            float *yrow = a.Y + (int64_t)row * a.ldy;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int c = n0 + wc * TN + fn * 16 + lm;
+                if (c < N) {
+                    float v = alpha * acc[fm][fn][i];
+                    if (beta != 0.f) v = fmaf(beta, yrow[c], v);
+                    yrow[c] = v;
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------ implicit GEMM, direct-to-LDS slabs
+
+// The fast form of the tile kernel above for R x S filters it is built for
+// (R and S compile-time), K = C R S a multiple of 16 and filter rows 16-byte
+// aligned: no register holds slab data.  Both operands travel from memory
+// straight into LDS with raw buffer loads in LDS mode (each lane's data lands
+// at a wave-uniform LDS address + its lane offset), in the slab pipeline of
+// the GEMM direct-load kernel: a ring of three buffers, the loads of slab
+// t + 2 spread over k-steps 0-1 of slab t, one wait and barrier, then the
+// next slab's operand reads spread over k-steps 2-3.  The contraction is in
+// the natural order k = (c R + r) S + s.
+//
+//   filters: chunk cm of a slab (rows 16 cm .. 16 cm + 15) is one 16-byte
+//     load per lane, lane l taking Wt[m0 + 16 cm + l % 16][k0 + 4 (l / 16)
+//     .. + 3] to LDS slot l (the operand read of block cm is then slot l);
+//     rows past M get an out-of-range offset, so they land as zeros.
+//   taps: one load of a wave covers one slab row k (tap (c, r, s), the same
+//     for the wave) and 64 consecutive output positions (the lane's
+//     position fixed for the tile): vector offset base(n) + r W + s, or an
+//     out-of-range offset for a tap outside the image (or past N), which
+//     lands as zero; scalar offset c H W.  B is k-major in LDS with row
+//     pitch BN + 4: a load writes 64 consecutive floats of one row, and the
+//     operand reads (lane group g reading row 4 g + s) fall in distinct
+//     banks.
+template <int BM, int BN, int WM, int WN, int R, int S>
+struct ConvDl {
+    static constexpr int NW = WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 16, FN = TN / 16;
+    static constexpr int CA = BM / 16;            // filter chunks per slab
+    static constexpr int BH = BN / 64;            // 64-position pieces of a tap row
+    static constexpr int SB = BN + 4;             // tap row pitch in LDS (floats)
+    static constexpr int A_FLOATS = CA * 256;
+    static constexpr int BUF = A_FLOATS + 16 * SB;  // floats per ring buffer
+    static constexpr int NBUF = 3;
+    static constexpr int LDS = NBUF * BUF;
+    static constexpr int LA = CA / NW;            // filter loads per wave per slab,
+    static constexpr int XA = CA % NW;            // and one more for waves 0 .. XA-1
+    static constexpr int LB = 16 * BH / NW;       // tap loads per wave per slab
+    static constexpr int L = LA + LB;
+    static constexpr int LMAX = L + (XA > 0 ? 1 : 0);
+    static constexpr int NREAD = FM + 2 * FN;     // operand reads per slab
+    static constexpr int STRIDE = 2 * FM * FN / (LMAX + 1);
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert(BN % 64 == 0 && (16 * BH) % NW == 0 && NW % BH == 0,
+                  "each wave loads whole tap rows of one 64-position piece");
+    static_assert(STRIDE >= 1 && NREAD <= 2 * FM * FN, "too few MFMAs per slab");
+    static_assert(LMAX * (NBUF - 1) <= 63, "loads in flight must fit the vmcnt field");
+    static_assert(R * S <= 32, "tap mask is 32 bits");
+};
+
+template <int BM, int BN, int WM, int WN, int WPE, int R, int S>
+__global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+conv_dl_kernel(ConvArgs a, int tiles_m, int tiles_n)
+{
+    using D = ConvDl<BM, BN, WM, WN, R, S>;
+    constexpr int NW = D::NW, TM = D::TM, TN = D::TN, FM = D::FM, FN = D::FN;
+    constexpr int BH = D::BH, SB = D::SB, BUF = D::BUF, NBUF = D::NBUF;
+    constexpr int LA = D::LA, XA = D::XA, LB = D::LB, L = D::L, LMAX = D::LMAX;
+    constexpr int NREAD = D::NREAD, S1 = D::STRIDE;
+    __shared__ __attribute__((aligned(16))) float lds[D::LDS];
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, tiles_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = a.M, N = (int)a.N;
+    const int nslab = a.K / 16;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave / WN, wc = wave % WN;
+    const bool extra = XA > 0 && wave < XA;
+
+    const uint32_t x_bytes = 4u * (uint32_t)a.batch * (uint32_t)a.C * (uint32_t)a.H * (uint32_t)a.W;
+    const uint32_t w_bytes = 4u * ((uint32_t)(M - 1) * (uint32_t)a.ldw + (uint32_t)a.K);
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.X), 0, (int)x_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t wrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.Wt), 0, (int)w_bytes, kBufferWord3);
+
+    // Filter loads: load q (< LA, or LA for the extra waves) of this wave
+    // fills chunk wave + q NW.
+    uint32_t a_voff[LA + 1];
+#pragma unroll
+    for (int q = 0; q <= LA; ++q) {
+        const int cm = wave + q * NW;
+        const int row = m0 + 16 * cm + (lane & 15);
+        a_voff[q] = row < M ? 4u * ((uint32_t)row * (uint32_t)a.ldw + 4u * (uint32_t)(lane >> 4))
+                            : kOffsetOut;
+    }
+    // Tap loads: this wave's 64-position piece h (fixed) and, for load q,
+    // slab row wave / BH + (NW / BH) q.
+    const int h = wave % BH;
+    const int n = n0 + 64 * h + lane;
+    uint32_t pbase4 = 0, tap_ok = 0;
+    if (n < N) {
+        const int ohw = a.OH * a.OW;
+        const int b = n / ohw;
+        const int p = n - b * ohw;
+        const int oh = p / a.OW, ow = p - oh * a.OW;
+        const int ih0 = oh * a.sh - a.ph, iw0 = ow * a.sw - a.pw;
+        pbase4 = 4u * (((uint32_t)(b * a.C * a.H) + (uint32_t)ih0) * (uint32_t)a.W + (uint32_t)iw0);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                if ((unsigned)(ih0 + r) < (unsigned)a.H && (unsigned)(iw0 + s) < (unsigned)a.W)
+                    tap_ok |= 1u << (r * S + s);
+    }
+    const uint32_t hw4 = 4u * (uint32_t)a.H * (uint32_t)a.W;
+    const uint32_t w4 = 4u * (uint32_t)a.W;
+
+    // Load q of slab ks (k0 = 16 ks) into ring buffer buf.
+    auto load = [&](int q, int ks, int buf) {
+        float *base = lds + buf * BUF;
+        const int k0 = 16 * ks;
+        if (q >= LA && q < L) {
+            const int kk = wave / BH + (NW / BH) * (q - LA);
+            const int k = k0 + kk;  // wave-uniform
+            const int c = k / (R * S);
+            const int rs = k - c * (R * S);
+            const int r = rs / S, s = rs - r * S;
+            const uint32_t voff = ((tap_ok >> rs) & 1u)
+                                      ? pbase4 + (uint32_t)r * w4 + 4u * (uint32_t)s
+                                      : kOffsetOut;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (lds_float *)(base + D::A_FLOATS + kk * SB + 64 * h), 4, (int)voff,
+                (int)((uint32_t)c * hw4), 0, 0);
+        } else {
+            const int qa = q < LA ? q : LA;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wrs, (lds_float *)(base + (wave + qa * NW) * 256), 16, (int)a_voff[qa],
+                4 * k0, 0, 0);
+        }
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    f32x4 afs[2][FM];
+    float bfs[2][4][FN];
+    const int lg = lane >> 4, lm = lane & 15;
+    const int b_lane = D::A_FLOATS + 4 * lg * SB + wc * TN + lm;
+    // Operand read r (0 .. NREAD-1) of the slab in buffer buf, in order of
+    // first use: filter blocks, then tap k-steps 0-1, then 2-3.
+    auto read_op = [&](int r, int buf, f32x4 (&af)[FM], float (&bf)[4][FN]) {
+        const float *base = lds + buf * BUF;
+        if (r < FM) {
+            af[r] = *reinterpret_cast<const f32x4 *>(base + (wr * FM + r) * 256 + 4 * lane);
+        } else {
+            const int hh = (r - FM) / FN, fn = (r - FM) % FN;
+            const float *bs = base + b_lane + 2 * hh * SB + 16 * fn;
+            bf[2 * hh][fn] = bs[0];
+            bf[2 * hh + 1][fn] = bs[SB];
+        }
+    };
+    auto ksteps = [&](int s0, int s1, const f32x4 (&af)[FM], const float (&bf)[4][FN],
+                      auto hook) {
+#pragma unroll
+        for (int s = s0; s < s1; ++s)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    hook(((s - s0) * FM + fm) * FN + fn);
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[fm][s], bf[s][fn],
+                                                                       acc[fm][fn], 0, 0, 0);
+                }
+    };
+
+    // Slab t from buffer buf with operands in set P; slab t+1's operands go
+    // to set P ^ 1.  After the last slab the reads fetch a stale buffer (in
+    // bounds; the values go unused).
+    auto slab = [&](auto P, int t, int buf) {
+        constexpr int p = decltype(P)::value;
+        // The loads of slab t + 2 go to the buffer slab t - 1 used (every
+        // wave's reads of it had returned at barrier t - 1).
+        const bool more = t >= 1 && t + NBUF - 1 < nslab;
+        const int lb = buf == 0 ? NBUF - 1 : buf - 1;
+        ksteps(0, 2, afs[p], bfs[p], [&](int i) {
+            if (i > 0 && i % S1 == 0 && i / S1 <= LMAX) {
+                if (more && (i / S1 <= L || extra)) load(i / S1 - 1, t + NBUF - 1, lb);
+            }
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        if (extra)
+            wait_slabs_barrier<LMAX, NBUF - 2>(nslab - 2 - t);
+        else
+            wait_slabs_barrier<L, NBUF - 2>(nslab - 2 - t);
+        const int nb = buf + 1 == NBUF ? 0 : buf + 1;
+        ksteps(2, 4, afs[p], bfs[p], [&](int i) {
+            if (i < NREAD) {
+                read_op(i, nb, afs[p ^ 1], bfs[p ^ 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+    };
+
+    // Prologue: slabs 0 .. NBUF-1 in flight, wait for slab 0.
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b)
+        if (b < nslab) {
+#pragma unroll
+            for (int q = 0; q < LMAX; ++q)
+                if (q < L || extra) load(q, b, b);
+        }
+    if (extra)
+        wait_slabs_barrier<LMAX, NBUF - 1>(nslab - 1);
+    else
+        wait_slabs_barrier<L, NBUF - 1>(nslab - 1);
+#pragma unroll
+    for (int r = 0; r < NREAD; ++r) read_op(r, 0, afs[0], bfs[0]);
+
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    int buf = 0;
+    for (int t = 0; t < nslab; t += 2) {
+        slab(P0{}, t, buf);
+        buf = buf + 1 == NBUF ? 0 : buf + 1;
+        if (t + 1 < nslab) {
+            slab(P1{}, t + 1, buf);
+            buf = buf + 1 == NBUF ? 0 : buf + 1;
+        }
+    }
+
+    const float alpha = a.alpha, beta = a.beta;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + wr * TM + fm * 16 + 4 * lg + i;
+            if (row >= M) continue;
+            float *yrow = a.Y + (int64_t)row * a.ldy;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int c = n0 + wc * TN + fn * 16 + lm;
+                if (c < N) {
+                    float v = alpha * acc[fm][fn][i];
+                    if (beta != 0.f) v = fmaf(beta, yrow[c], v);
+                    yrow[c] = v;
+                }
+            }
+        }
     }
 }
 

@@ -39,7 +39,10 @@ extern "C" {
 
 /* Kernel forms for sconv2d_f32_variant(). */
 enum sconv_variant {
-    SCONV_VARIANT_AUTO = 0,   /* the stem kernel where it applies, else general */
+    SCONV_VARIANT_AUTO = 0,   /* the stem kernel where it applies, else the tile
+                               * kernel (its direct form where that applies)
+                               * where its tiles keep the CUs busier, else
+                               * general */
     SCONV_VARIANT_STEM = 1,   /* input rows staged in LDS once per 256 output
                                * positions; only the geometries it is built for
                                * (3 channels, 7x7 or 3x3 filters at stride 2,
@@ -47,8 +50,19 @@ enum sconv_variant {
                                * out_channels <= 64, X and Y under 4 GiB);
                                * others return
                                * SGEMM_ERR_VARIANT_SHAPE (include/sgemm.h) */
-    SCONV_VARIANT_GENERAL = 2 /* any geometry: 64 x 64 output tiles, taps gathered
-                               * from X into LDS in slabs of 16 */
+    SCONV_VARIANT_GENERAL = 2, /* any geometry: 64 x 64 output tiles, taps gathered
+                                * from X into LDS in slabs of 16 */
+    SCONV_VARIANT_TILE = 3,    /* matrix-core tiles (64, 128 or 192 x 128) with
+                                * taps gathered into a three-slab LDS ring, the
+                                * contraction walked tap by tap over blocks of 16
+                                * channels; any geometry with X and the filter
+                                * rows under 2^31 bytes; others return
+                                * SGEMM_ERR_VARIANT_SHAPE */
+    SCONV_VARIANT_DIRECT = 4   /* the tile kernel's fast form: both operands loaded
+                                * straight into LDS; 3x3 and 1x1 filters, K a
+                                * multiple of 16, Wt 16-byte aligned with ldw a
+                                * multiple of 4, and the tile form's limits;
+                                * others return SGEMM_ERR_VARIANT_SHAPE */
 };
 
 /*
@@ -68,7 +82,8 @@ enum sconv_variant {
  *   -1 batch < 0 (or N > INT_MAX), -2 channels < 1 (or K > INT_MAX),
  *   -3 height < 1, -4 width < 1, -5 out_channels < 0,
  *   -6 kernel_h < 1 or > height + 2 pad_h, -7 kernel_w likewise,
- *   -8 stride_h < 1, -9 stride_w < 1, -10 pad_h < 0, -11 pad_w < 0,
+ *   -8 stride_h < 1, -9 stride_w < 1, -10 pad_h < 0 (or height + 2 pad_h
+ *   > INT_MAX), -11 pad_w likewise,
  *  -13 X NULL or not 4-byte aligned (while it is read), -14 Wt likewise,
  *  -15 ldw < K, -17 Y NULL or not 4-byte aligned (while M*N > 0),
  *  -18 ldy < max(1, N);
@@ -116,8 +131,11 @@ int sgemm_im2col_f32(int batch, int channels, int height, int width, int kernel_
 
 /*
  * sconv2d_plan -- describe, without touching any GPU, the kernel
- * sconv2d_f32_variant would launch on a device with num_cus compute units:
+ * sconv2d_f32_variant would launch on a device with num_cus compute units
+ * (for packed filters, 16-byte aligned):
  *   "stem mb=2 k=147 window=3x13x232 strip=256 strips=6272 grid=512 oh=112 ow=112"
+ *   "direct bm=192 bn=128 waves=8 k=1152 grid=222 oh=119 ow=119"
+ *   "tile bm=64 bn=128 waves=4 k=255 grid=3 oh=21 ow=9"
  *   "general tile=64x64 k=1152 grid=... oh=... ow=..."   or "none".
  * Writes at most buflen bytes (NUL-terminated).  Returns 0, the argument
  * codes of sconv2d_f32 for the geometry, SGEMM_ERR_BAD_VARIANT,

@@ -1,7 +1,7 @@
 """GPU parity of the convolution entry points against the CPU reference.
 
-sconv2d_f32 (stem and general kernels) and sgemm_im2col_f32 run through the C
-ABI on seeded inputs; every output element is compared with the reference
+sconv2d_f32 (stem, matrix-core tile and general kernels) and sgemm_im2col_f32
+run through the C ABI on seeded inputs; every output element is compared with the reference
 convolution: bit for bit on integer data (all partial sums are small
 integers, so any summation order gives the same float), within
 1e-5 * (|alpha| sum|w x| + |beta y|) + 1e-6 on uniform data.  Bytes of Y
@@ -142,6 +142,33 @@ STEM = [
     (1, 3, 224, 227, 33, 3, 3, (2, 2), (1, 1)),
 ]
 
+# Geometries for the matrix-core tile kernels: several tiles in both
+# directions with ragged edges, channel counts that are not multiples of 16
+# (5, 1, 20, 33), strides and paddings, batch > 1, 1x1 and 5x3 filters; the
+# last is a 3x3 stride-1 layer with 128 channels at a size that still runs
+# quickly on the reference.
+TILE = [
+    (2, 32, 30, 31, 200, 3, 3, (1, 1), (1, 1)),
+    (1, 5, 40, 37, 130, 3, 3, (1, 1), (1, 1)),
+    (3, 1, 33, 29, 64, 3, 3, (1, 1), (0, 0)),
+    (1, 64, 57, 57, 129, 3, 3, (2, 2), (1, 1)),
+    (2, 20, 23, 25, 70, 3, 3, (2, 1), (2, 0)),
+    (2, 48, 20, 21, 96, 1, 1, (1, 1), (0, 0)),
+    (1, 33, 15, 15, 260, 1, 1, (2, 2), (1, 1)),
+    (2, 17, 21, 18, 40, 5, 3, (1, 2), (2, 1)),
+    (1, 128, 36, 36, 384, 3, 3, (1, 1), (1, 1)),
+]
+
+
+def _plan(variant, g):
+    import fp32_gemm_04_amd as sg
+    batch, C, H, W, M, R, S, (sh, sw), (ph, pw) = g
+    return sg.sconv2d_plan(variant, batch, C, H, W, M, R, S, sh, sw, ph, pw, 256)
+
+
+def _direct_applies(g):
+    return _plan(4, g)[0] == 0
+
 
 def _stem_applies(g):
     import fp32_gemm_04_amd as sg
@@ -152,9 +179,12 @@ def _stem_applies(g):
 
 
 @pytest.mark.parametrize("integer", [True, False], ids=["integer", "uniform"])
-@pytest.mark.parametrize("variant", [0, 2], ids=["auto", "general"])
-@pytest.mark.parametrize("g", GENERAL + STEM, ids=[str(i) for i in range(len(GENERAL + STEM))])
+@pytest.mark.parametrize("variant", [0, 2, 3, 4], ids=["auto", "general", "tile", "direct"])
+@pytest.mark.parametrize("g", GENERAL + STEM + TILE,
+                         ids=[str(i) for i in range(len(GENERAL + STEM + TILE))])
 def test_conv_small(g, variant, integer):
+    if variant == 4 and not _direct_applies(g):
+        pytest.skip("the direct form takes 3x3 and 1x1 filters with K % 16 == 0")
     batch, C, H, W, M, R, S, stride, pad = g
     gen = _ints if integer else _uniform
     X = gen((batch, C, H, W), 11 + H)
@@ -174,17 +204,38 @@ def test_stem_geometries_take_the_stem_kernel(g):
                     * ((W + 2 * pad[1] - S) // stride[1] + 1)), 25))
 
 
-@pytest.mark.parametrize("variant", [0, 2], ids=["auto", "general"])
+@pytest.mark.parametrize("variant", [0, 2, 3, 4], ids=["auto", "general", "tile", "direct"])
 def test_padded_leading_dimensions_and_beta(variant):
-    for g in [STEM[1], GENERAL[3], STEM[6]]:
+    for g in [STEM[1], GENERAL[3], STEM[6], TILE[0], TILE[5], TILE[6]]:
+        if variant == 4 and not _direct_applies(g):
+            continue
         batch, C, H, W, M, R, S, stride, pad = g
         OH = (H + 2 * pad[0] - R) // stride[0] + 1
         OW = (W + 2 * pad[1] - S) // stride[1] + 1
         X = _ints((batch, C, H, W), 31)
         Wt = _ints((M, C * R * S), 32)
         Y0 = _ints((M, batch * OH * OW), 33)
+        # The direct form needs filter rows 16-byte aligned: pad by 4 there.
         check(X, Wt, R, S, stride, pad, variant, True, alpha=-1.0, beta=2.0, Y0=Y0,
-              ldw=C * R * S + 3, ldy=batch * OH * OW + 5)
+              ldw=C * R * S + (4 if variant == 4 else 3), ldy=batch * OH * OW + 5)
+
+
+def test_direct_form_needs_aligned_filters():
+    """The call takes the register-staged tile form when the filter rows are
+    not 16-byte aligned, the direct form otherwise; both match the reference."""
+    import fp32_gemm_04_amd as sg
+    g = TILE[0]
+    batch, C, H, W, M, R, S, (sh, sw), (ph, pw) = g
+    K = C * R * S
+    assert _direct_applies(g)
+    X = _ints((batch, C, H, W), 35)
+    Wt = _ints((M, K), 36)
+    for ldw in (K + 1, K + 4):
+        check(X, Wt, R, S, (sh, sw), (ph, pw), 0, True, ldw=ldw)
+    s = torch.cuda.current_stream()
+    rc = sg.sconv2d_f32_variant(4, batch, C, H, W, M, R, S, sh, sw, ph, pw, 1.0, 0x1000,
+                                0x2004, K + 4, 0.0, 0x3000, batch * H * W, s.cuda_stream)
+    assert rc == sg.SGEMM_ERR_VARIANT_SHAPE  # misaligned filters: refused before any launch
 
 
 def test_beta_zero_does_not_read_y_and_alpha_zero_scales():
@@ -196,6 +247,11 @@ def test_beta_zero_does_not_read_y_and_alpha_zero_scales():
     for variant in (0, 2):
         out = check(X, Wt, R, S, stride, pad, variant, True)  # Y starts as NaN
         assert not np.isnan(out).any()
+    g = TILE[1]
+    Xt = _ints(g[:4], 44)
+    Wtt = _ints((g[4], g[1] * 9), 45)
+    out = check(Xt, Wtt, 3, 3, g[7], g[8], 3, True)
+    assert not np.isnan(out).any()
     Y0 = _ints((M, batch * OH * OW), 43)
     out = run_conv(X, Wt, M, R, S, stride, pad, alpha=0.0, beta=-0.5, Y0=Y0)
     assert np.array_equal(out, -0.5 * Y0)
@@ -233,16 +289,33 @@ def test_im2col_matches_reference_and_feeds_sgemm():
 
 
 # The two stem readings at full size (N = 128 * 112 * 112 = 1605632), and
-# the mid-size readings through the general kernel.
+# the mid-size readings through the kernel the call picks (the direct-to-LDS
+# tile kernel), the register-staged tile kernel and the general kernel, all
+# against one reference result.
 @pytest.mark.parametrize("integer", [False, True], ids=["uniform", "integer"])
 @pytest.mark.parametrize("case", workloads.CONV_STEMS + workloads.CONV_MID,
                          ids=[c.name for c in workloads.CONV_STEMS + workloads.CONV_MID])
 def test_full_size_readings(case, integer):
+    import fp32_gemm_04_amd as sg
     X, Wt = workloads.conv_operands(case, integer)
     g = case.geometry
     b, C, H, W, M, R, S, sh, sw, ph, pw = g
+    stride, pad = (sh, sw), (ph, pw)
+    rc, plan = sg.sconv2d_plan(0, b, C, H, W, M, R, S, sh, sw, ph, pw, 256)
+    assert rc == 0
     if case in workloads.CONV_STEMS:
-        assert _stem_applies((b, C, H, W, M, R, S, (sh, sw), (ph, pw)))
-    out = check(X, Wt, case.R, case.S, (case.sh, case.sw), (case.ph, case.pw), 0, integer)
-    assert out.shape == (case.M, case.N)
-    say("%s %s: %d elements" % (case.name, "integer" if integer else "uniform", out.size))
+        assert plan.startswith("stem"), plan
+        variants = [0]
+    else:
+        assert plan.startswith("direct"), plan
+        variants = [0, 3, 2]
+    ref, t = oracle.conv2d(X, Wt, R, S, stride, pad, with_absdot=not integer)
+    for variant in variants:
+        out = run_conv(X, Wt, M, R, S, stride, pad, variant=variant)
+        what = "%s variant %d" % (case.name, variant)
+        if integer:
+            assert_bits_equal(out, ref, what)
+        else:
+            assert_within_tolerance(out, ref, t, 1.0, 0.0, None, what)
+        assert out.shape == (case.M, case.N)
+        say("%s %s: %d elements" % (what, "integer" if integer else "uniform", out.size))

@@ -1,7 +1,8 @@
 """Host logic of the convolution entry points, on a host without a GPU:
 argument checks come before any HIP call, quick returns make none, and the
-plan picks the stem kernel for the geometries it is built for and the
-general kernel otherwise."""
+plan picks the stem kernel for the geometries it is built for, the matrix-core
+tile kernel where its tiles keep the CUs busier, and the general kernel
+otherwise."""
 import os
 
 import pytest
@@ -32,6 +33,7 @@ def call(**kw):
     (dict(batch=-1), -1), (dict(channels=0), -2), (dict(height=0), -3), (dict(width=0), -4),
     (dict(out_channels=-1), -5), (dict(kernel_h=0), -6), (dict(kernel_w=0), -7),
     (dict(stride_h=0), -8), (dict(stride_w=0), -9), (dict(pad_h=-1), -10), (dict(pad_w=-1), -11),
+    (dict(pad_h=2 ** 30), -10), (dict(pad_w=2 ** 30), -11),
     (dict(kernel_h=231), -6), (dict(kernel_w=231), -7),
     (dict(X=0), -13), (dict(X=4098), -13), (dict(Wt=0), -14), (dict(ldw=146), -15),
     (dict(Y=0), -17), (dict(Y=12290), -17), (dict(ldy=1000), -18),
@@ -51,7 +53,7 @@ def test_alpha_zero_reads_no_operands():
 
 
 def test_bad_variant_first():
-    for v in (-1, 3, 100):
+    for v in (-1, 5, 100):
         rc = sg.sconv2d_f32_variant(v, *[GEOM[n] for n in NAMES], 1.0, 0, 0, 0, 0.0, 0, 0, 0)
         assert rc == sg.SGEMM_ERR_BAD_VARIANT
 
@@ -80,10 +82,47 @@ def test_plans():
         g.update(kw)
         rc, _ = sg.sconv2d_plan(sg.SCONV_VARIANT_STEM, *[g[n] for n in NAMES], 256)
         assert rc == sg.SGEMM_ERR_VARIANT_SHAPE, kw
-    # the mid-size readings: 3x3 stride 1 pad 1 over 128 channels, batch 1
-    p = plan(batch=1, channels=128, height=119, width=119, out_channels=384, kernel_h=3,
-             kernel_w=3, stride_h=1, stride_w=1, pad_h=1, pad_w=1)
-    assert p.startswith("general") and "oh=119 ow=119" in p and "k=1152" in p, p
+    # the mid-size readings: 3x3 stride 1 pad 1 over 128 channels, batch 1.
+    # 384 x 14161: 2 x 111 tiles of 192 x 128 fill 256 CUs once, where
+    # 3 x 111 of 128 x 128 would put two on some CUs; 256 x 43264: 128 x 128.
+    mid = dict(batch=1, channels=128, kernel_h=3, kernel_w=3, stride_h=1, stride_w=1, pad_h=1,
+               pad_w=1)
+    p = plan(height=119, width=119, out_channels=384, **mid)
+    assert p == "direct bm=192 bn=128 waves=8 k=1152 grid=222 oh=119 ow=119", p
+    p = plan(height=208, width=208, out_channels=256, **mid)
+    assert p == "direct bm=128 bn=128 waves=4 k=1152 grid=676 oh=208 ow=208", p
+    p = plan(variant=sg.SCONV_VARIANT_TILE, height=208, width=208, out_channels=256, **mid)
+    assert p == "tile bm=128 bn=128 waves=4 k=1152 grid=676 oh=208 ow=208", p
+    # the direct form: 3x3 and 1x1 filters with K % 16 == 0 only
+    assert plan(variant=sg.SCONV_VARIANT_DIRECT, height=20, width=20, out_channels=64,
+                **mid).startswith("direct")
+    for kw in [dict(channels=5), dict(kernel_h=5, kernel_w=5)]:
+        g = dict(GEOM, height=20, width=20, out_channels=64)
+        g.update(mid)
+        g.update(kw)
+        rc, _ = sg.sconv2d_plan(sg.SCONV_VARIANT_DIRECT, *[g[n] for n in NAMES], 256)
+        assert rc == sg.SGEMM_ERR_VARIANT_SHAPE, kw
+    assert plan(variant=sg.SCONV_VARIANT_GENERAL, height=208, width=208, out_channels=256,
+                **mid).startswith("general tile=64x64")
+    # a small problem keeps the general kernel's finer tiles; the forced
+    # tile form still takes it; 1x1 filters have tile kernels too
+    small = dict(batch=2, channels=16, height=17, width=19, out_channels=33, kernel_h=3,
+                 kernel_w=3, stride_h=1, stride_w=1, pad_h=1, pad_w=1)
+    assert plan(**small).startswith("general")
+    assert plan(variant=sg.SCONV_VARIANT_TILE, **small).startswith("tile bm=64 bn=128")
+    p = plan(batch=8, channels=256, height=56, width=56, out_channels=512, kernel_h=1,
+             kernel_w=1, stride_h=1, stride_w=1, pad_h=0, pad_w=0)
+    assert p.startswith("direct") and "k=256" in p, p
+    p = plan(batch=8, channels=250, height=56, width=56, out_channels=512, kernel_h=1,
+             kernel_w=1, stride_h=1, stride_w=1, pad_h=0, pad_w=0)
+    assert p.startswith("tile") and "k=250" in p, p
+    # the tile kernels take any filter; they refuse inputs of 2^31 bytes or more
+    for kw in [dict(), dict(kernel_h=3), dict(kernel_h=5, kernel_w=5)]:
+        assert plan(variant=sg.SCONV_VARIANT_TILE, **kw).startswith("tile"), kw
+    g = dict(GEOM, batch=4096)  # 4096 * 3 * 224 * 224 * 4 bytes > 2^31
+    rc, _ = sg.sconv2d_plan(sg.SCONV_VARIANT_TILE, *[g[n] for n in NAMES], 256)
+    assert rc == sg.SGEMM_ERR_VARIANT_SHAPE
+    assert plan(batch=4096).startswith("general")  # Y over 2^32 bytes: not the stem either
     assert plan(out_channels=0) == "none"
 
 
