@@ -36,6 +36,7 @@ SCONV_VARIANT_STEM = 1
 SCONV_VARIANT_GENERAL = 2
 SCONV_VARIANT_TILE = 3
 SCONV_VARIANT_DIRECT = 4
+SCONV_VARIANT_TAP = 5
 
 EXPORTS = ("sgemm_f32", "sgemm_f32_variant", "sgemm_plan", "sgemm_tune", "sgemm_tune_reset",
            "sgemm_num_mfma_tiles", "sgemm_status_string",

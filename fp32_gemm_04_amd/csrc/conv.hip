@@ -124,6 +124,16 @@ const DlEntry kDlTiles[] = {
     SGEMM_CONV_DL(192, 128, 4, 2, 1, 1), SGEMM_CONV_DL(64, 128, 1, 4, 1, 1),
 };
 
+// The one-tap-per-k-step forms (3 x 3 filters): eight waves, one workgroup
+// per CU (the three-slab ring of 4-channel slabs takes 118-145 KB of LDS).
+#define SGEMM_CONV_TAP(BM, BN, WM, WN, R, S) \
+    {R, S, BM, BN, WM * WN, conv_tap_kernel<BM, BN, WM, WN, 2, R, S>}
+
+const DlEntry kTapTiles[] = {
+    SGEMM_CONV_TAP(128, 128, 2, 4, 3, 3),
+    SGEMM_CONV_TAP(192, 128, 4, 2, 3, 3),
+};
+
 // The general kernel's rate relative to the tile kernels' (measured on the
 // 3 x 3 readings: about 0.3 against 0.6 and more of the matrix peak).
 constexpr int64_t kGeneralCost = 2;
@@ -186,6 +196,23 @@ const DlEntry *dl_for(const Geometry &q, int64_t N, const float *Wt, int ldw, in
     return best;
 }
 
+// The one-tap-per-k-step kernel for this problem, or null: a filter built,
+// C a multiple of 4, the filter rows 16-byte aligned, and the tile kernels'
+// limits; among those built, the least busiest-CU work.
+const DlEntry *tap_for(const Geometry &q, int64_t N, const float *Wt, int ldw, int cus)
+{
+    if (q.C % 4 != 0 || ldw % 4 != 0 || ((uintptr_t)Wt & 15u) != 0 || !tile_fits(q, N, ldw))
+        return nullptr;
+    const DlEntry *best = nullptr;
+    for (const DlEntry &e : kTapTiles) {
+        if (e.R != q.R || e.S != q.S) continue;
+        if (best == nullptr ||
+            tile_cost(q.M, N, e.bm, e.bn, cus) < tile_cost(q.M, N, best->bm, best->bn, cus))
+            best = &e;
+    }
+    return best;
+}
+
 // The tile kernel with the least busiest-CU work, for the forced tile form.
 const TileEntry *tile_forced(const Geometry &q, int64_t N, int cus)
 {
@@ -222,7 +249,7 @@ hipError_t conv_device_cus(int *cus)
 int conv_launch(int variant, const Geometry &q, float alpha, const float *X, const float *Wt,
                 int ldw, float beta, float *Y, int ldy, hipStream_t stream)
 {
-    if (variant < SCONV_VARIANT_AUTO || variant > SCONV_VARIANT_DIRECT) return SGEMM_ERR_BAD_VARIANT;
+    if (variant < SCONV_VARIANT_AUTO || variant > SCONV_VARIANT_TAP) return SGEMM_ERR_BAD_VARIANT;
     int OH = 0, OW = 0;
     int64_t N = 0;
     const int bad = check_geometry(q, &OH, &OW, &N);
@@ -243,6 +270,8 @@ int conv_launch(int variant, const Geometry &q, float alpha, const float *X, con
     const bool tile_ok = tile_fits(q, N, ldw);
     if (variant == SCONV_VARIANT_TILE && !tile_ok) return SGEMM_ERR_VARIANT_SHAPE;
     if (variant == SCONV_VARIANT_DIRECT && dl_for(q, N, Wt, ldw, 1) == nullptr)
+        return SGEMM_ERR_VARIANT_SHAPE;
+    if (variant == SCONV_VARIANT_TAP && tap_for(q, N, Wt, ldw, 1) == nullptr)
         return SGEMM_ERR_VARIANT_SHAPE;
     if (q.M == 0 || N == 0) return 0;
 
@@ -296,10 +325,13 @@ int conv_launch(int variant, const Geometry &q, float alpha, const float *X, con
                             : variant == SCONV_VARIANT_TILE ? tile_forced(q, N, cus)
                             : variant == SCONV_VARIANT_AUTO ? tile_for(q, N, cus)
                                                             : nullptr;
-    // The direct-to-LDS form where it applies, in the tile kernels' place.
+    // The direct-to-LDS forms where they apply, in the tile kernels' place:
+    // one tap per k-step first, then 16-tap slabs.
     const DlEntry *dl = variant == SCONV_VARIANT_DIRECT ? dl_for(q, N, Wt, ldw, cus)
+                        : variant == SCONV_VARIANT_TAP  ? tap_for(q, N, Wt, ldw, cus)
                         : (variant == SCONV_VARIANT_AUTO && tile != nullptr)
-                            ? dl_for(q, N, Wt, ldw, cus)
+                            ? (tap_for(q, N, Wt, ldw, cus) != nullptr ? tap_for(q, N, Wt, ldw, cus)
+                                                                       : dl_for(q, N, Wt, ldw, cus))
                             : nullptr;
     if (dl != nullptr) {
         const int tiles_m = (int)ceil_div64(q.M, dl->bm);
@@ -398,7 +430,7 @@ extern "C" int sconv2d_plan(int variant, int batch, int channels, int height, in
                             int stride_w, int pad_h, int pad_w, int num_cus, char *buf, int buflen)
 {
     using namespace sgemm;
-    if (variant < SCONV_VARIANT_AUTO || variant > SCONV_VARIANT_DIRECT) return SGEMM_ERR_BAD_VARIANT;
+    if (variant < SCONV_VARIANT_AUTO || variant > SCONV_VARIANT_TAP) return SGEMM_ERR_BAD_VARIANT;
     const Geometry q = {batch,    channels, height,   width,    out_channels, kernel_h,
                         kernel_w, stride_h, stride_w, pad_h,    pad_w};
     int OH = 0, OW = 0;
@@ -424,11 +456,15 @@ extern "C" int sconv2d_plan(int variant, int batch, int channels, int height, in
     const float *wt_aligned = reinterpret_cast<const float *>(
         (reinterpret_cast<uintptr_t>(kAligned) + 15u) & ~(uintptr_t)15u);
     const int K = channels * kernel_h * kernel_w;
+    const DlEntry *tap = tap_for(q, N, wt_aligned, K, num_cus);
     const DlEntry *dl = variant == SCONV_VARIANT_DIRECT ? dl_for(q, N, wt_aligned, K, num_cus)
+                        : variant == SCONV_VARIANT_TAP  ? tap
                         : (variant == SCONV_VARIANT_AUTO && tile != nullptr)
-                            ? dl_for(q, N, wt_aligned, K, num_cus)
+                            ? (tap != nullptr ? tap : dl_for(q, N, wt_aligned, K, num_cus))
                             : nullptr;
-    if (variant == SCONV_VARIANT_DIRECT && dl == nullptr) return SGEMM_ERR_VARIANT_SHAPE;
+    if ((variant == SCONV_VARIANT_DIRECT || variant == SCONV_VARIANT_TAP) && dl == nullptr)
+        return SGEMM_ERR_VARIANT_SHAPE;
+    const bool is_tap = dl != nullptr && dl == tap;
     char text[200];
     if (out_channels == 0 || N == 0) {
         std::snprintf(text, sizeof text, "none");
@@ -443,8 +479,9 @@ extern "C" int sconv2d_plan(int variant, int batch, int channels, int height, in
                       OH, OW);
     } else if (dl != nullptr) {
         const int64_t tiles = ceil_div64(out_channels, dl->bm) * ceil_div64(N, dl->bn);
-        std::snprintf(text, sizeof text, "direct bm=%d bn=%d waves=%d k=%d grid=%lld oh=%d ow=%d",
-                      dl->bm, dl->bn, dl->waves, K, (long long)tiles, OH, OW);
+        std::snprintf(text, sizeof text, "%s bm=%d bn=%d waves=%d k=%d grid=%lld oh=%d ow=%d",
+                      is_tap ? "tap" : "direct", dl->bm, dl->bn, dl->waves, K, (long long)tiles,
+                      OH, OW);
     } else if (tile != nullptr) {
         const int64_t tiles = ceil_div64(out_channels, tile->bm) * ceil_div64(N, tile->bn);
         std::snprintf(text, sizeof text, "tile bm=%d bn=%d waves=%d k=%d grid=%lld oh=%d ow=%d",

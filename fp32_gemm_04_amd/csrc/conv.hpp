@@ -688,6 +688,248 @@ conv_dl_kernel(ConvArgs a, int tiles_m, int tiles_n)
     }
 }
 
+// ------------------------------ implicit GEMM, one filter tap per k-step
+
+// The direct-to-LDS form for R x S filters with the contraction ordered so
+// that the tap arithmetic disappears from the loop.  A slab is 4 channels x
+// RS taps (BK = 4 RS); in k-step st of a slab, lane group g (lanes 16 g ..
+// 16 g + 15) of every MFMA takes channel c0 + g at tap st.  So:
+//   - the filter slab of row m is Wt[m][BK t .. BK t + BK - 1], contiguous
+//     (channels c0 .. c0 + 3, all taps), loaded 16 bytes per lane straight
+//     into LDS (row pitch BK floats, no padding: lane (g, m) reads
+//     m BK + g RS + st, which falls in 64 distinct banks for RS = 9);
+//   - a tap load covers one (channel, tap) row of the slab and 64 output
+//     positions: vector offset vtap[st] (worked out once per thread: the
+//     input offset of its position at tap st, or an out-of-range offset
+//     where the tap leaves the image), scalar offset c H W.  The tap index
+//     is a compile-time constant in the unrolled loop, so a load is an M0
+//     write, a scalar add and the load.  B rows have pitch P, chosen so that
+//     RS P = 16 or 48 (mod 64): the four lane groups' rows then fall in
+//     distinct banks.
+// Operands are read from LDS one k-step ahead (two register sets); a slab's
+// buffer is read during the whole slab, so the ring has three buffers: the
+// loads of slab t + 2 are spread over slab t's MFMAs into the buffer slab
+// t - 1 used, and at the end of slab t one wait (slab t + 1 landed) and one
+// barrier (every wave done with buffer t) hand over to slab t + 1.
+// C must be a multiple of 4; filter rows 16-byte aligned.
+template <int RS, int BN>
+constexpr int conv_tap_pitch()
+{
+    for (int p = BN; p < BN + 64; ++p)
+        if ((RS * p) % 64 == 16 || (RS * p) % 64 == 48) return p;
+    return -1;
+}
+
+template <int BM, int BN, int WM, int WN, int R, int S>
+struct ConvTap {
+    static constexpr int RS = R * S;
+    static constexpr int BK = 4 * RS;
+    static constexpr int NW = WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 16, FN = TN / 16;
+    static constexpr int BH = BN / 64;               // 64-position pieces of a tap row
+    static constexpr int P = conv_tap_pitch<RS, BN>();
+    static constexpr int A_FLOATS = BM * BK;
+    static constexpr int BUF = A_FLOATS + BK * P;
+    static constexpr int NBUF = 3;
+    static constexpr int LDS = NBUF * BUF;
+    static constexpr int AW = BM * RS / 64;          // filter loads per slab
+    static constexpr int LA = AW / NW, XA = AW % NW;
+    static constexpr int G = 4 * BH / NW;            // channels whose taps a wave loads
+    static constexpr int LB = G * RS;                // tap loads per wave per slab
+    static constexpr int L = LA + LB;
+    static constexpr int LMAX = L + (XA > 0 ? 1 : 0);
+    static constexpr int MF = RS * FM * FN;          // MFMAs per wave per slab
+    static constexpr int STRIDE = MF / (LMAX + 1);
+    static_assert(P > 0, "no conflict-free tap row pitch");
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert((BM * RS) % 64 == 0, "filter slab splits into whole loads");
+    static_assert(BN % 64 == 0 && (4 * BH) % NW == 0 && G >= 1 && NW % BH == 0,
+                  "each wave loads the taps of whole channels for one 64-position piece");
+    static_assert(STRIDE >= 1, "too few MFMAs per slab for the loads");
+    static_assert(LMAX * (NBUF - 1) <= 63, "loads in flight must fit the vmcnt field");
+};
+
+template <int BM, int BN, int WM, int WN, int WPE, int R, int S>
+__global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+conv_tap_kernel(ConvArgs a, int tiles_m, int tiles_n)
+{
+    using D = ConvTap<BM, BN, WM, WN, R, S>;
+    constexpr int RS = D::RS, BK = D::BK, NW = D::NW, TM = D::TM, TN = D::TN;
+    constexpr int FM = D::FM, FN = D::FN, BH = D::BH, P = D::P, BUF = D::BUF;
+    constexpr int LA = D::LA, XA = D::XA, G = D::G, LB = D::LB, L = D::L, LMAX = D::LMAX;
+    constexpr int S1 = D::STRIDE;
+    __shared__ __attribute__((aligned(16))) float lds[D::LDS];
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, tiles_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = a.M, N = (int)a.N;
+    const int nslab = a.C / 4;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave / WN, wc = wave % WN;
+    const bool extra = XA > 0 && wave < XA;
+
+    const uint32_t x_bytes = 4u * (uint32_t)a.batch * (uint32_t)a.C * (uint32_t)a.H * (uint32_t)a.W;
+    const uint32_t w_bytes = 4u * ((uint32_t)(M - 1) * (uint32_t)a.ldw + (uint32_t)a.K);
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.X), 0, (int)x_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t wrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.Wt), 0, (int)w_bytes, kBufferWord3);
+
+    // Filter loads: load qa of this wave is slab load j = wave + qa NW, whose
+    // lane l takes 16-byte slot 64 j + l: row (64 j + l) / RS, quad
+    // (64 j + l) % RS of the row's BK floats.
+    uint32_t a_voff[LA + 1];
+#pragma unroll
+    for (int qa = 0; qa <= LA; ++qa) {
+        const int j = wave + qa * NW;
+        const int slot = 64 * j + lane;
+        const int row = m0 + slot / RS;
+        a_voff[qa] = (j < D::AW && row < M)
+                         ? 4u * ((uint32_t)row * (uint32_t)a.ldw + 4u * (uint32_t)(slot % RS))
+                         : kOffsetOut;
+    }
+    // Tap loads: this wave's 64-position piece h and channels g0 .. g0 + G - 1
+    // of each slab; vtap[st] is the lane's input offset at tap st.
+    const int h = wave % BH;
+    const int g0 = (wave / BH) * G;
+    const int n = n0 + 64 * h + lane;
+    uint32_t vtap[RS];
+#pragma unroll
+    for (int st = 0; st < RS; ++st) vtap[st] = kOffsetOut;
+    if (n < N) {
+        const int ohw = a.OH * a.OW;
+        const int b = n / ohw;
+        const int p = n - b * ohw;
+        const int oh = p / a.OW, ow = p - oh * a.OW;
+        const int ih0 = oh * a.sh - a.ph, iw0 = ow * a.sw - a.pw;
+        const uint32_t pbase4 =
+            4u * (((uint32_t)(b * a.C * a.H) + (uint32_t)ih0) * (uint32_t)a.W + (uint32_t)iw0);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                if ((unsigned)(ih0 + r) < (unsigned)a.H && (unsigned)(iw0 + s) < (unsigned)a.W)
+                    vtap[r * S + s] = pbase4 + 4u * ((uint32_t)r * (uint32_t)a.W + (uint32_t)s);
+    }
+    const uint32_t hw4 = 4u * (uint32_t)a.H * (uint32_t)a.W;
+
+    // Load q of slab t into ring buffer buf: the tap loads, then the filter
+    // loads (the extra waves' additional filter load last).
+    auto load = [&](int q, int t, int buf) {
+        float *base = lds + buf * BUF;
+        if (q < LB) {
+            const int g = g0 + q / RS, st = q % RS;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (lds_float *)(base + D::A_FLOATS + (g * RS + st) * P + 64 * h), 4,
+                (int)vtap[st], (int)((uint32_t)(4 * t + g) * hw4), 0, 0);
+        } else {
+            const int qa = q - LB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wrs, (lds_float *)(base + (wave + qa * NW) * 256), 16, (int)a_voff[qa],
+                4 * BK * t, 0, 0);
+        }
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int lg = lane >> 4, lm = lane & 15;
+    const int a_lane = (wr * TM + lm) * BK + lg * RS;
+    const int b_lane = D::A_FLOATS + lg * RS * P + wc * TN + lm;
+    float af[2][FM], bf[2][FN];
+    // Operands of k-step st of the slab in buffer buf into set p.
+    auto read = [&](int p, int buf, int st) {
+        const float *base = lds + buf * BUF;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) af[p][fm] = base[a_lane + fm * 16 * BK + st];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) bf[p][fn] = base[b_lane + st * P + fn * 16];
+    };
+
+    // Slab t from buffer buf; its k-step st uses operand set (P0 + st) & 1.
+    auto slab = [&](auto P0, int t, int buf) {
+        constexpr int p0 = decltype(P0)::value;
+        const bool more = t + 2 < nslab;
+        const int lb = buf == 0 ? 2 : buf - 1;  // the buffer of slab t - 1
+#pragma unroll
+        for (int st = 0; st < RS; ++st) {
+            const int p = (p0 + st) & 1;
+            if (st + 1 < RS) read(p ^ 1, buf, st + 1);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    const int i = (st * FM + fm) * FN + fn;
+                    if (i > 0 && i % S1 == 0 && i / S1 <= LMAX) {
+                        const int q = i / S1 - 1;
+                        if (more && (q < L || extra)) load(q, t + 2, lb);
+                    }
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[p][fm], bf[p][fn],
+                                                                       acc[fm][fn], 0, 0, 0);
+                }
+        }
+        // Slab t + 1 has landed and every wave is done with buffer buf.
+        if (extra)
+            wait_slabs_barrier<LMAX, 1>(nslab - 2 - t);
+        else
+            wait_slabs_barrier<L, 1>(nslab - 2 - t);
+        if (t + 1 < nslab) read((p0 + RS) & 1, buf == 2 ? 0 : buf + 1, 0);
+    };
+
+    // Prologue: slabs 0 and 1 in flight, wait for slab 0.
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+        if (b < nslab) {
+#pragma unroll
+            for (int q = 0; q < LMAX; ++q)
+                if (q < L || extra) load(q, b, b);
+        }
+    if (extra)
+        wait_slabs_barrier<LMAX, 1>(nslab - 1);
+    else
+        wait_slabs_barrier<L, 1>(nslab - 1);
+    read(0, 0, 0);
+
+    using Q0 = std::integral_constant<int, 0>;
+    using Q1 = std::integral_constant<int, RS & 1>;
+    int buf = 0;
+    for (int t = 0; t < nslab; t += 2) {
+        slab(Q0{}, t, buf);
+        buf = buf == 2 ? 0 : buf + 1;
+        if (t + 1 < nslab) {
+            slab(Q1{}, t + 1, buf);
+            buf = buf == 2 ? 0 : buf + 1;
+        }
+    }
+
+    const float alpha = a.alpha, beta = a.beta;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + wr * TM + fm * 16 + 4 * lg + i;
+            if (row >= M) continue;
+            float *yrow = a.Y + (int64_t)row * a.ldy;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int c = n0 + wc * TN + fn * 16 + lm;
+                if (c < N) {
+                    float v = alpha * acc[fm][fn][i];
+                    if (beta != 0.f) v = fmaf(beta, yrow[c], v);
+                    yrow[c] = v;
+                }
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------ stem fast path
 
 // For the first layers of image networks: few input channels, a large

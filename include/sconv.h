@@ -40,9 +40,9 @@ extern "C" {
 /* Kernel forms for sconv2d_f32_variant(). */
 enum sconv_variant {
     SCONV_VARIANT_AUTO = 0,   /* the stem kernel where it applies, else the tile
-                               * kernel (its direct form where that applies)
-                               * where its tiles keep the CUs busier, else
-                               * general */
+                               * kernel (its tap form, else its direct form,
+                               * where those apply) where its tiles keep the
+                               * CUs busier, else general */
     SCONV_VARIANT_STEM = 1,   /* input rows staged in LDS once per 256 output
                                * positions; only the geometries it is built for
                                * (3 channels, 7x7 or 3x3 filters at stride 2,
@@ -58,11 +58,16 @@ enum sconv_variant {
                                 * channels; any geometry with X and the filter
                                 * rows under 2^31 bytes; others return
                                 * SGEMM_ERR_VARIANT_SHAPE */
-    SCONV_VARIANT_DIRECT = 4   /* the tile kernel's fast form: both operands loaded
+    SCONV_VARIANT_DIRECT = 4,  /* the tile kernel's fast form: both operands loaded
                                 * straight into LDS; 3x3 and 1x1 filters, K a
                                 * multiple of 16, Wt 16-byte aligned with ldw a
                                 * multiple of 4, and the tile form's limits;
                                 * others return SGEMM_ERR_VARIANT_SHAPE */
+    SCONV_VARIANT_TAP = 5      /* the direct form with one filter tap per matrix
+                                * k-step (slabs of 4 channels x 9 taps); 3x3
+                                * filters, channels a multiple of 4, Wt as for
+                                * SCONV_VARIANT_DIRECT; others return
+                                * SGEMM_ERR_VARIANT_SHAPE */
 };
 
 /*
@@ -134,7 +139,8 @@ int sgemm_im2col_f32(int batch, int channels, int height, int width, int kernel_
  * sconv2d_f32_variant would launch on a device with num_cus compute units
  * (for packed filters, 16-byte aligned):
  *   "stem mb=2 k=147 window=3x13x232 strip=256 strips=6272 grid=512 oh=112 ow=112"
- *   "direct bm=192 bn=128 waves=8 k=1152 grid=222 oh=119 ow=119"
+ *   "tap bm=192 bn=128 waves=8 k=1152 grid=222 oh=119 ow=119"
+ *   "direct bm=128 bn=128 waves=4 k=256 grid=1568 oh=56 ow=56"
  *   "tile bm=64 bn=128 waves=4 k=255 grid=3 oh=21 ow=9"
  *   "general tile=64x64 k=1152 grid=... oh=... ow=..."   or "none".
  * Writes at most buflen bytes (NUL-terminated).  Returns 0, the argument

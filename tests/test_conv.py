@@ -170,6 +170,14 @@ def _direct_applies(g):
     return _plan(4, g)[0] == 0
 
 
+def _tap_applies(g):
+    return _plan(5, g)[0] == 0
+
+
+def _applies(variant, g):
+    return {4: _direct_applies, 5: _tap_applies}.get(variant, lambda g: True)(g)
+
+
 def _stem_applies(g):
     import fp32_gemm_04_amd as sg
     batch, C, H, W, M, R, S, (sh, sw), (ph, pw) = g
@@ -179,12 +187,13 @@ def _stem_applies(g):
 
 
 @pytest.mark.parametrize("integer", [True, False], ids=["integer", "uniform"])
-@pytest.mark.parametrize("variant", [0, 2, 3, 4], ids=["auto", "general", "tile", "direct"])
+@pytest.mark.parametrize("variant", [0, 2, 3, 4, 5],
+                         ids=["auto", "general", "tile", "direct", "tap"])
 @pytest.mark.parametrize("g", GENERAL + STEM + TILE,
                          ids=[str(i) for i in range(len(GENERAL + STEM + TILE))])
 def test_conv_small(g, variant, integer):
-    if variant == 4 and not _direct_applies(g):
-        pytest.skip("the direct form takes 3x3 and 1x1 filters with K % 16 == 0")
+    if not _applies(variant, g):
+        pytest.skip("form %d does not take this geometry" % variant)
     batch, C, H, W, M, R, S, stride, pad = g
     gen = _ints if integer else _uniform
     X = gen((batch, C, H, W), 11 + H)
@@ -204,10 +213,11 @@ def test_stem_geometries_take_the_stem_kernel(g):
                     * ((W + 2 * pad[1] - S) // stride[1] + 1)), 25))
 
 
-@pytest.mark.parametrize("variant", [0, 2, 3, 4], ids=["auto", "general", "tile", "direct"])
+@pytest.mark.parametrize("variant", [0, 2, 3, 4, 5],
+                         ids=["auto", "general", "tile", "direct", "tap"])
 def test_padded_leading_dimensions_and_beta(variant):
-    for g in [STEM[1], GENERAL[3], STEM[6], TILE[0], TILE[5], TILE[6]]:
-        if variant == 4 and not _direct_applies(g):
+    for g in [STEM[1], GENERAL[3], STEM[6], TILE[0], TILE[3], TILE[5], TILE[6]]:
+        if not _applies(variant, g):
             continue
         batch, C, H, W, M, R, S, stride, pad = g
         OH = (H + 2 * pad[0] - R) // stride[0] + 1
@@ -215,9 +225,9 @@ def test_padded_leading_dimensions_and_beta(variant):
         X = _ints((batch, C, H, W), 31)
         Wt = _ints((M, C * R * S), 32)
         Y0 = _ints((M, batch * OH * OW), 33)
-        # The direct form needs filter rows 16-byte aligned: pad by 4 there.
+        # The direct forms need filter rows 16-byte aligned: pad by 4 there.
         check(X, Wt, R, S, stride, pad, variant, True, alpha=-1.0, beta=2.0, Y0=Y0,
-              ldw=C * R * S + (4 if variant == 4 else 3), ldy=batch * OH * OW + 5)
+              ldw=C * R * S + (4 if variant in (4, 5) else 3), ldy=batch * OH * OW + 5)
 
 
 def test_direct_form_needs_aligned_filters():
@@ -289,9 +299,9 @@ def test_im2col_matches_reference_and_feeds_sgemm():
 
 
 # The two stem readings at full size (N = 128 * 112 * 112 = 1605632), and
-# the mid-size readings through the kernel the call picks (the direct-to-LDS
-# tile kernel), the register-staged tile kernel and the general kernel, all
-# against one reference result.
+# the mid-size readings through the kernel the call picks (the tap form),
+# the 16-tap direct form, the register-staged tile kernel and the general
+# kernel, all against one reference result.
 @pytest.mark.parametrize("integer", [False, True], ids=["uniform", "integer"])
 @pytest.mark.parametrize("case", workloads.CONV_STEMS + workloads.CONV_MID,
                          ids=[c.name for c in workloads.CONV_STEMS + workloads.CONV_MID])
@@ -307,8 +317,8 @@ def test_full_size_readings(case, integer):
         assert plan.startswith("stem"), plan
         variants = [0]
     else:
-        assert plan.startswith("direct"), plan
-        variants = [0, 3, 2]
+        assert plan.startswith("tap"), plan
+        variants = [0, 4, 3, 2]
     ref, t = oracle.conv2d(X, Wt, R, S, stride, pad, with_absdot=not integer)
     for variant in variants:
         out = run_conv(X, Wt, M, R, S, stride, pad, variant=variant)

@@ -53,7 +53,7 @@ def test_alpha_zero_reads_no_operands():
 
 
 def test_bad_variant_first():
-    for v in (-1, 5, 100):
+    for v in (-1, 6, 100):
         rc = sg.sconv2d_f32_variant(v, *[GEOM[n] for n in NAMES], 1.0, 0, 0, 0, 0.0, 0, 0, 0)
         assert rc == sg.SGEMM_ERR_BAD_VARIANT
 
@@ -88,9 +88,20 @@ def test_plans():
     mid = dict(batch=1, channels=128, kernel_h=3, kernel_w=3, stride_h=1, stride_w=1, pad_h=1,
                pad_w=1)
     p = plan(height=119, width=119, out_channels=384, **mid)
-    assert p == "direct bm=192 bn=128 waves=8 k=1152 grid=222 oh=119 ow=119", p
+    assert p == "tap bm=192 bn=128 waves=8 k=1152 grid=222 oh=119 ow=119", p
     p = plan(height=208, width=208, out_channels=256, **mid)
+    assert p == "tap bm=128 bn=128 waves=8 k=1152 grid=676 oh=208 ow=208", p
+    p = plan(variant=sg.SCONV_VARIANT_DIRECT, height=208, width=208, out_channels=256, **mid)
     assert p == "direct bm=128 bn=128 waves=4 k=1152 grid=676 oh=208 ow=208", p
+    # the tap form: 3x3 filters over a multiple of 4 channels
+    assert plan(variant=sg.SCONV_VARIANT_TAP, height=20, width=20, out_channels=64,
+                **mid).startswith("tap")
+    for kw in [dict(channels=6), dict(kernel_h=1, kernel_w=1)]:
+        g = dict(GEOM, height=20, width=20, out_channels=64)
+        g.update(mid)
+        g.update(kw)
+        rc, _ = sg.sconv2d_plan(sg.SCONV_VARIANT_TAP, *[g[n] for n in NAMES], 256)
+        assert rc == sg.SGEMM_ERR_VARIANT_SHAPE, kw
     p = plan(variant=sg.SCONV_VARIANT_TILE, height=208, width=208, out_channels=256, **mid)
     assert p == "tile bm=128 bn=128 waves=4 k=1152 grid=676 oh=208 ow=208", p
     # the direct form: 3x3 and 1x1 filters with K % 16 == 0 only
