@@ -90,9 +90,10 @@ enum sgemm_variant {
  * keep partial tiles in a workspace slot: 64 MiB of a 256 MiB static device
  * array that the HIP runtime places when it loads the library's code and
  * keeps until the process ends, one copy per device.  A slot serves one
- * stream at a time, in stream order; after each use an event is recorded on
- * that stream, and a call on another stream takes the slot over only once
- * that event has completed (a query, not a wait).  So calls on different
+ * stream at a time, in stream order; each use sets the slot's event to the
+ * completion of its last kernel (the event rides on that kernel's launch),
+ * and a call on another stream takes the slot over only once that event has
+ * completed (a query, not a wait).  So calls on different
  * streams never share partials, whatever they overlap.  When all four slots
  * of the device are busy with other streams' queued work, or when `stream`
  * is being captured into a graph, the selector's choice runs one tile per
