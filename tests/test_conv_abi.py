@@ -71,7 +71,7 @@ def test_plans():
     p = plan(batch=128)
     assert p.startswith("stem mb=2 k=147") and "strips=6272" in p and "grid=512" in p, p
     p = plan(batch=128, out_channels=32, kernel_h=3, kernel_w=3, pad_h=1, pad_w=1)
-    assert p.startswith("stem mb=1 k=27") and "grid=512" in p, p
+    assert p.startswith("stem mb=1 k=27") and "grid=768" in p, p  # three per CU
     assert plan(out_channels=20).startswith("stem mb=1")
     assert plan(variant=sg.SCONV_VARIANT_GENERAL).startswith("general")
     # outside the stem kernels' geometries: general, and the forced stem form refuses
