@@ -19,12 +19,16 @@ KernelFn direct_kernel(int bm, int bn, int wm, int wn, int wpe, bool shifted)
             return mfma_dl_kernel<128, 128, 2, 2, 2, 3, true>;
         if (bm == 64 && bn == 256 && wm == 1 && wn == 4 && wpe == 2)
             return mfma_dl_kernel<64, 256, 1, 4, 2, 3, true>;
+        if (bm == 192 && bn == 128 && wm == 4 && wn == 2 && wpe == 2)
+            return mfma_dl_kernel<192, 128, 4, 2, 2, 3, true>;
         return nullptr;
     }
     if (bm == 64 && bn == 64 && wm == 2 && wn == 2 && wpe == 1)
         return mfma_dl_kernel<64, 64, 2, 2, 1, 4>;
     if (bm == 128 && bn == 128 && wm == 2 && wn == 4 && wpe == 2)
         return mfma_dl_kernel<128, 128, 2, 4, 2, 3>;
+    if (bm == 192 && bn == 128 && wm == 4 && wn == 2 && wpe == 2)
+        return mfma_dl_kernel<192, 128, 4, 2, 2, 3>;
     if (wpe != 2) return nullptr;
     if (bm == 160 && bn == 160 && wm == 2 && wn == 2) return mfma_dl_kernel<160, 160, 2, 2, 2>;
     if (bm == 128 && bn == 128 && wm == 2 && wn == 2) return mfma_dl_kernel<128, 128, 2, 2, 2>;
@@ -43,12 +47,16 @@ SkKernelFn direct_sk_kernel(int bm, int bn, int wm, int wn, int wpe, bool shifte
             return mfma_dl_sk_kernel<128, 128, 2, 2, 2, 3, true>;
         if (bm == 64 && bn == 256 && wm == 1 && wn == 4 && wpe == 2)
             return mfma_dl_sk_kernel<64, 256, 1, 4, 2, 3, true>;
+        if (bm == 192 && bn == 128 && wm == 4 && wn == 2 && wpe == 2)
+            return mfma_dl_sk_kernel<192, 128, 4, 2, 2, 3, true>;
         return nullptr;
     }
     if (bm == 64 && bn == 64 && wm == 2 && wn == 2 && wpe == 1)
         return mfma_dl_sk_kernel<64, 64, 2, 2, 1, 4>;
     if (bm == 128 && bn == 128 && wm == 2 && wn == 4 && wpe == 2)
         return mfma_dl_sk_kernel<128, 128, 2, 4, 2, 3>;
+    if (bm == 192 && bn == 128 && wm == 4 && wn == 2 && wpe == 2)
+        return mfma_dl_sk_kernel<192, 128, 4, 2, 2, 3>;
     if (wpe != 2) return nullptr;
     if (bm == 160 && bn == 160 && wm == 2 && wn == 2) return mfma_dl_sk_kernel<160, 160, 2, 2, 2>;
     if (bm == 128 && bn == 128 && wm == 2 && wn == 2) return mfma_dl_sk_kernel<128, 128, 2, 2, 2>;

@@ -127,7 +127,6 @@ struct MfmaDl {
     // every STRIDE MFMAs; the second half R operand reads, one per MFMA.
     static constexpr int R = FM + 2 * FN;
     static constexpr int STRIDE = 2 * FM * FN / (LMAX + 1);
-    static_assert(BSH || X == 0, "slab chunks must split evenly over the waves");
     static_assert(L >= 1, "every wave loads");
     static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile must be 16-aligned");
     static_assert(STRIDE >= 1 && R <= 2 * FM * FN, "too few MFMAs per slab for the reads and loads");

@@ -165,6 +165,11 @@ int sk_dmode(int dmode, int K) { return K % 16 == 0 ? dmode : kDirectNone; }
 // stream-K at 1280^3: 49.4 against 52.1); with several tiles per CU it is
 // slower (2304^3: 293 against 202 us), since no second workgroup overlaps a
 // tile's fill and epilogue.  Its register-staged kernels are forced-only.
+// The 192 x 128 direct-load tile (eight waves of 48 x 64, one workgroup per
+// CU) is for M = 384-like shapes whose 128 x 128 tiles would leave a
+// part-full round: (384,14161,1152) is 222 of them, one per CU, 111.8 us
+// against 117.4 for the stream-K 128 x 128 plan (ldb 14164: 109.0 against
+// 112.2).  Its register-staged kernels are forced-only too.
 const TileConfig kMfmaTiles[] = {
     SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 3, 0.77, SGEMM_DL_KERNEL(160, 160, 2, 2, 2), 0.88,
                      SGEMM_DL_SK_KERNEL(160, 160, 2, 2, 2), 0.82),
@@ -179,6 +184,8 @@ const TileConfig kMfmaTiles[] = {
                        SGEMM_DL_SK_KERNEL(64, 64, 2, 2, 1), 0.56),
     SGEMM_MFMA_ENTRY_R(128, 128, 16, 2, 4, 1, 1, 3, 0.0, SGEMM_DL_KERNEL(128, 128, 2, 4, 1), 0.80,
                        SGEMM_DL_SK_KERNEL(128, 128, 2, 4, 1), 0.82),
+    SGEMM_MFMA_ENTRY_R(192, 128, 16, 4, 2, 1, 1, 3, 0.0, SGEMM_DL_KERNEL(192, 128, 4, 2, 1), 0.80,
+                       SGEMM_DL_SK_KERNEL(192, 128, 4, 2, 1), 0.82),
 };
 
 // The vector-FMA kernel's two tiles (both two workgroups per CU).
