@@ -181,14 +181,17 @@ const TileEntry *tile_for(const Geometry &q, int64_t N, int cus)
     return best;
 }
 
+// Whether the filter rows are 16-byte aligned (base and row pitch), as the
+// direct-to-LDS forms load them.
+bool rows_aligned(const float *Wt, int ldw) { return ldw % 4 == 0 && ((uintptr_t)Wt & 15u) == 0; }
+
 // The direct-to-LDS kernel for this problem, or null: the filter must be one
-// built, K a multiple of 16, the filter rows 16-byte aligned, and the tile
-// kernels' limits hold; among those built, the least busiest-CU work.
-const DlEntry *dl_for(const Geometry &q, int64_t N, const float *Wt, int ldw, int cus)
+// built, K a multiple of 16, the filter rows 16-byte aligned (w_aligned), and
+// the tile kernels' limits hold; among those built, the least busiest-CU work.
+const DlEntry *dl_for(const Geometry &q, int64_t N, bool w_aligned, int ldw, int cus)
 {
     const int64_t K = (int64_t)q.C * q.R * q.S;
-    if (K % 16 != 0 || ldw % 4 != 0 || ((uintptr_t)Wt & 15u) != 0 || !tile_fits(q, N, ldw))
-        return nullptr;
+    if (K % 16 != 0 || !w_aligned || !tile_fits(q, N, ldw)) return nullptr;
     const DlEntry *best = nullptr;
     for (const DlEntry &e : kDlTiles) {
         if (e.R != q.R || e.S != q.S) continue;
@@ -200,12 +203,11 @@ const DlEntry *dl_for(const Geometry &q, int64_t N, const float *Wt, int ldw, in
 }
 
 // The one-tap-per-k-step kernel for this problem, or null: a filter built,
-// C a multiple of 4, the filter rows 16-byte aligned, and the tile kernels'
-// limits; among those built, the least busiest-CU work.
-const DlEntry *tap_for(const Geometry &q, int64_t N, const float *Wt, int ldw, int cus)
+// C a multiple of 4, the filter rows 16-byte aligned (w_aligned), and the
+// tile kernels' limits; among those built, the least busiest-CU work.
+const DlEntry *tap_for(const Geometry &q, int64_t N, bool w_aligned, int ldw, int cus)
 {
-    if (q.C % 4 != 0 || ldw % 4 != 0 || ((uintptr_t)Wt & 15u) != 0 || !tile_fits(q, N, ldw))
-        return nullptr;
+    if (q.C % 4 != 0 || !w_aligned || !tile_fits(q, N, ldw)) return nullptr;
     const DlEntry *best = nullptr;
     for (const DlEntry &e : kTapTiles) {
         if (e.R != q.R || e.S != q.S) continue;
@@ -272,9 +274,10 @@ int conv_launch(int variant, const Geometry &q, float alpha, const float *X, con
     if (variant == SCONV_VARIANT_STEM && stem == nullptr) return SGEMM_ERR_VARIANT_SHAPE;
     const bool tile_ok = tile_fits(q, N, ldw);
     if (variant == SCONV_VARIANT_TILE && !tile_ok) return SGEMM_ERR_VARIANT_SHAPE;
-    if (variant == SCONV_VARIANT_DIRECT && dl_for(q, N, Wt, ldw, 1) == nullptr)
+    const bool w_aligned = rows_aligned(Wt, ldw);
+    if (variant == SCONV_VARIANT_DIRECT && dl_for(q, N, w_aligned, ldw, 1) == nullptr)
         return SGEMM_ERR_VARIANT_SHAPE;
-    if (variant == SCONV_VARIANT_TAP && tap_for(q, N, Wt, ldw, 1) == nullptr)
+    if (variant == SCONV_VARIANT_TAP && tap_for(q, N, w_aligned, ldw, 1) == nullptr)
         return SGEMM_ERR_VARIANT_SHAPE;
     if (q.M == 0 || N == 0) return 0;
 
@@ -330,11 +333,11 @@ int conv_launch(int variant, const Geometry &q, float alpha, const float *X, con
                                                             : nullptr;
     // The direct-to-LDS forms where they apply, in the tile kernels' place:
     // one tap per k-step first, then 16-tap slabs.
-    const DlEntry *dl = variant == SCONV_VARIANT_DIRECT ? dl_for(q, N, Wt, ldw, cus)
-                        : variant == SCONV_VARIANT_TAP  ? tap_for(q, N, Wt, ldw, cus)
+    const DlEntry *tap = tap_for(q, N, w_aligned, ldw, cus);
+    const DlEntry *dl = variant == SCONV_VARIANT_DIRECT ? dl_for(q, N, w_aligned, ldw, cus)
+                        : variant == SCONV_VARIANT_TAP  ? tap
                         : (variant == SCONV_VARIANT_AUTO && tile != nullptr)
-                            ? (tap_for(q, N, Wt, ldw, cus) != nullptr ? tap_for(q, N, Wt, ldw, cus)
-                                                                       : dl_for(q, N, Wt, ldw, cus))
+                            ? (tap != nullptr ? tap : dl_for(q, N, w_aligned, ldw, cus))
                             : nullptr;
     if (dl != nullptr) {
         const int tiles_m = (int)ceil_div64(q.M, dl->bm);
@@ -454,16 +457,14 @@ extern "C" int sconv2d_plan(int variant, int batch, int channels, int height, in
                             : variant == SCONV_VARIANT_AUTO ? tile_for(q, N, num_cus)
                                                             : nullptr;
     if (variant == SCONV_VARIANT_TILE && tile == nullptr) return SGEMM_ERR_VARIANT_SHAPE;
-    // Packed, 16-byte aligned filters assumed.
-    static const float kAligned[4] = {0.f, 0.f, 0.f, 0.f};
-    const float *wt_aligned = reinterpret_cast<const float *>(
-        (reinterpret_cast<uintptr_t>(kAligned) + 15u) & ~(uintptr_t)15u);
+    // Packed filters (ldw = K) at a 16-byte aligned base assumed.
     const int K = channels * kernel_h * kernel_w;
-    const DlEntry *tap = tap_for(q, N, wt_aligned, K, num_cus);
-    const DlEntry *dl = variant == SCONV_VARIANT_DIRECT ? dl_for(q, N, wt_aligned, K, num_cus)
+    const bool w_aligned = K % 4 == 0;
+    const DlEntry *tap = tap_for(q, N, w_aligned, K, num_cus);
+    const DlEntry *dl = variant == SCONV_VARIANT_DIRECT ? dl_for(q, N, w_aligned, K, num_cus)
                         : variant == SCONV_VARIANT_TAP  ? tap
                         : (variant == SCONV_VARIANT_AUTO && tile != nullptr)
-                            ? (tap != nullptr ? tap : dl_for(q, N, wt_aligned, K, num_cus))
+                            ? (tap != nullptr ? tap : dl_for(q, N, w_aligned, K, num_cus))
                             : nullptr;
     if ((variant == SCONV_VARIANT_DIRECT || variant == SCONV_VARIANT_TAP) && dl == nullptr)
         return SGEMM_ERR_VARIANT_SHAPE;
