@@ -63,17 +63,46 @@ __global__ void __launch_bounds__(256) sk_fixup_kernel(GemmArgs g, SkArgs s, int
     const int row = tm * bm + r, col = tn * bn + c;
     if (row >= g.M || col >= g.N) return;
     const int64_t slot_floats = (int64_t)bm * bn;
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < nw; ++i)
-        sum += *reinterpret_cast<const f32x4 *>(s.ws + slot_of[i] * slot_floats + e);
     float *pc = g.C + (int64_t)row * g.ldc + col;
+    // C as one 128-bit access where the four columns exist and are aligned;
+    // it is read (beta != 0) before the partials, so the two latencies overlap.
+    const bool vec = col + 3 < g.N && (reinterpret_cast<uintptr_t>(pc) & 15u) == 0;
+    f32x4 c_old = {0.f, 0.f, 0.f, 0.f};
+    if (g.beta != 0.f) {
+        if (vec) {
+            c_old = *reinterpret_cast<const f32x4 *>(pc);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (col + q < g.N) c_old[q] = pc[q];
+        }
+    }
+    // The partial sums, added in worker order; loaded four at a time, so
+    // that a thread waits for one memory latency per four partials, not one
+    // per partial (nw is the same for the whole workgroup).
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < nw; i += 4) {
+        f32x4 part[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (i + j < nw)
+                part[j] = *reinterpret_cast<const f32x4 *>(s.ws + slot_of[i + j] * slot_floats + e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (i + j < nw) sum += part[j];
+    }
+    f32x4 v;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        if (col + q < g.N) {
-            float v = g.alpha * sum[q];
-            if (g.beta != 0.f) v = fmaf(g.beta, pc[q], v);
-            pc[q] = v;
-        }
+        v[q] = g.alpha * sum[q];
+        if (g.beta != 0.f) v[q] = fmaf(g.beta, c_old[q], v[q]);
+    }
+    if (vec) {
+        *reinterpret_cast<f32x4 *>(pc) = v;
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (col + q < g.N) pc[q] = v[q];
     }
 }
 
