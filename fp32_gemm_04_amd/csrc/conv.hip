@@ -5,6 +5,7 @@
 // is queued on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cstdint>
 #include <cstdio>
@@ -231,22 +232,24 @@ const TileEntry *tile_forced(const Geometry &q, int64_t N, int cus)
 
 // Per-device compute-unit count, cached.
 constexpr int kConvMaxDevices = 64;
-int g_conv_cus[kConvMaxDevices];
+std::atomic<int> g_conv_cus[kConvMaxDevices];
 
 hipError_t conv_device_cus(int *cus)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kConvMaxDevices && g_conv_cus[dev] > 0) {
-        *cus = g_conv_cus[dev];
+    const int cached =
+        dev >= 0 && dev < kConvMaxDevices ? g_conv_cus[dev].load(std::memory_order_relaxed) : 0;
+    if (cached > 0) {
+        *cus = cached;
         return hipSuccess;
     }
     int n = 0;
     e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     if (n < 1) n = 1;
-    if (dev >= 0 && dev < kConvMaxDevices) g_conv_cus[dev] = n;
+    if (dev >= 0 && dev < kConvMaxDevices) g_conv_cus[dev].store(n, std::memory_order_relaxed);
     *cus = n;
     return hipSuccess;
 }

@@ -839,16 +839,25 @@ int launch_streamk(const Choice &ch, GemmArgs g, int cus, int dmode, bool avec, 
     // attached to that kernel's dispatch: a separate event record costs a
     // queue entry of its own (measured: 3 us more per call at 1280^3-1792^3,
     // against 1-2 us for the attached form).
+    // (A plan without a slot, which may run under graph capture, uses plain
+    // launches.)
     hipEvent_t done = pool != nullptr ? pool->slot[slot].done : nullptr;
     const bool fixup = ch.sk.split_tiles > 0;
-    hipExtLaunchKernelGGL(fn, dim3((unsigned)sa.workers), dim3(c->threads), 0, stream, nullptr,
-                          fixup ? nullptr : done, 0, g, sa);
+    const dim3 main_grid((unsigned)sa.workers), main_block(c->threads);
+    if (done != nullptr && !fixup)
+        hipExtLaunchKernelGGL(fn, main_grid, main_block, 0, stream, nullptr, done, 0, g, sa);
+    else
+        hipLaunchKernelGGL(fn, main_grid, main_block, 0, stream, g, sa);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && fixup) {
-        hipExtLaunchKernelGGL(sk_fixup_kernel,
-                              dim3((unsigned)(blocks - sa.dp_tiles),
-                                   (unsigned)ceil_div(c->bm * c->bn, kSkFixupElems)),
-                              dim3(256), 0, stream, nullptr, done, 0, g, sa, c->bm, c->bn);
+        const dim3 fix_grid((unsigned)(blocks - sa.dp_tiles),
+                            (unsigned)ceil_div(c->bm * c->bn, kSkFixupElems));
+        if (done != nullptr)
+            hipExtLaunchKernelGGL(sk_fixup_kernel, fix_grid, dim3(256), 0, stream, nullptr, done,
+                                  0, g, sa, c->bm, c->bn);
+        else
+            hipLaunchKernelGGL(sk_fixup_kernel, fix_grid, dim3(256), 0, stream, g, sa, c->bm,
+                               c->bn);
         e = hipGetLastError();
         // The first kernel is queued: the slot's event must follow it.
         if (e != hipSuccess && done != nullptr) (void)hipEventRecord(done, stream);
