@@ -445,14 +445,14 @@ def bench_conv(sg, stream, check=True):
             "hbm_gbps": round(case.alg_bytes / (ms * 1e-3) / 1e9, 1),
             "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4),
             "frac_roofline": round(roof_us / (ms * 1e3), 4)}
-        if plan.split()[0] in ("tap", "direct", "tile"):
+        if plan.split()[0] in ("gemm", "tap", "direct", "tile"):
             # The other implicit forms on the same sets, for comparison: the
             # 16-tap direct form, the register-staged tile kernel and the
             # general 64 x 64 kernel.
             forms = [("general_us", sg.SCONV_VARIANT_GENERAL)]
-            if plan.split()[0] in ("tap", "direct"):
+            if plan.split()[0] in ("gemm", "tap", "direct"):
                 forms.insert(0, ("tile_us", sg.SCONV_VARIANT_TILE))
-            if plan.startswith("tap"):
+            if plan.split()[0] in ("gemm", "tap"):
                 forms.insert(0, ("direct_us", sg.SCONV_VARIANT_DIRECT))
             for key, v in forms:
                 def other(i, v=v):

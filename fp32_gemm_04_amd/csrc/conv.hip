@@ -98,6 +98,14 @@ const StemEntry *stem_for(const Geometry &q, int OH, int OW)
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// A pointwise layer: 1 x 1 filter, stride 1, no padding (then OH = H, OW = W,
+// and image b's im2col matrix is its own C x (H W) block of X).  H W must fit
+// the GEMM's int N, which N = batch H W <= INT_MAX already ensures.
+bool pointwise(const Geometry &q)
+{
+    return q.R == 1 && q.S == 1 && q.sh == 1 && q.sw == 1 && q.ph == 0 && q.pw == 0;
+}
+
 // The MFMA tile kernels built: tile and waves; all run two waves per SIMD
 // (two 4-wave workgroups or one 8-wave workgroup per CU).
 struct TileEntry {
@@ -292,6 +300,19 @@ int conv_launch(int variant, const Geometry &q, float alpha, const float *X, con
         return (int)hipGetLastError();
     }
 
+    // A 1 x 1 filter at stride 1 without padding: the taps of image b are
+    // its C x (H W) block of X itself, so the convolution is one product
+    // per image, Y[:, b H W ..] = Wt X_b, run by the GEMM path on X in place.
+    if (variant == SCONV_VARIANT_AUTO && pointwise(q)) {
+        const int hw = q.H * q.W;
+        for (int b = 0; b < q.batch; ++b) {
+            const int rc = sgemm_f32(q.M, hw, q.C, alpha, Wt, ldw, X + (int64_t)b * q.C * hw, hw,
+                                     beta, Y + (int64_t)b * hw, ldy, stream);
+            if (rc != 0) return rc;
+        }
+        return 0;
+    }
+
     ConvArgs a;
     a.X = X;
     a.Wt = Wt;
@@ -475,6 +496,9 @@ extern "C" int sconv2d_plan(int variant, int batch, int channels, int height, in
     char text[200];
     if (out_channels == 0 || N == 0) {
         std::snprintf(text, sizeof text, "none");
+    } else if (variant == SCONV_VARIANT_AUTO && pointwise(q)) {
+        std::snprintf(text, sizeof text, "gemm images=%d m=%d n=%d k=%d oh=%d ow=%d", batch,
+                      out_channels, height * width, channels, OH, OW);
     } else if (stem != nullptr && (variant == SCONV_VARIANT_AUTO || variant == SCONV_VARIANT_STEM)) {
         const int spi = (int)ceil_div64((int64_t)OH * OW, kStemStrip);
         const int64_t total = (int64_t)spi * batch;

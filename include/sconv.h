@@ -39,10 +39,12 @@ extern "C" {
 
 /* Kernel forms for sconv2d_f32_variant(). */
 enum sconv_variant {
-    SCONV_VARIANT_AUTO = 0,   /* the stem kernel where it applies, else the tile
-                               * kernel (its tap form, else its direct form,
-                               * where those apply) where its tiles keep the
-                               * CUs busier, else general */
+    SCONV_VARIANT_AUTO = 0,   /* a pointwise layer (1x1 filter, stride 1, no
+                               * padding) as one sgemm_f32 per image on X in
+                               * place; else the stem kernel where it applies,
+                               * else the tile kernel (its tap form, else its
+                               * direct form, where those apply) where its
+                               * tiles keep the CUs busier, else general */
     SCONV_VARIANT_STEM = 1,   /* input rows staged in LDS once per 256 output
                                * positions; only the geometries it is built for
                                * (3 channels, 7x7 or 3x3 filters at stride 2,
@@ -102,8 +104,9 @@ enum sconv_variant {
  * partial sums stay below 2^24 (then equal, bit for bit, to sgemm_f32 on
  * the im2col matrix).
  *
- * Thread safety: re-entrant; the only shared state is a per-device cache of
- * the compute-unit count.
+ * Thread safety: re-entrant; the shared state is a per-device cache of the
+ * compute-unit count and, for pointwise layers (run through sgemm_f32), the
+ * stream-K workspace slots sgemm_f32 documents.
  */
 int sconv2d_f32(int batch, int channels, int height, int width, int out_channels,
                 int kernel_h, int kernel_w, int stride_h, int stride_w, int pad_h, int pad_w,
@@ -139,6 +142,7 @@ int sgemm_im2col_f32(int batch, int channels, int height, int width, int kernel_
  * sconv2d_f32_variant would launch on a device with num_cus compute units
  * (for packed filters, 16-byte aligned):
  *   "stem mb=2 k=147 window=3x13x232 strip=256 strips=6272 grid=512 oh=112 ow=112"
+ *   "gemm images=1 m=256 n=50176 k=1024 oh=224 ow=224"   (one sgemm_f32 per image)
  *   "tap bm=192 bn=128 waves=8 k=1152 grid=222 oh=119 ow=119"
  *   "direct bm=128 bn=128 waves=4 k=256 grid=1568 oh=56 ow=56"
  *   "tile bm=64 bn=128 waves=4 k=255 grid=3 oh=21 ow=9"

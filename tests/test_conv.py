@@ -299,9 +299,10 @@ def test_im2col_matches_reference_and_feeds_sgemm():
 
 
 # The two stem readings at full size (N = 128 * 112 * 112 = 1605632), and
-# the mid-size readings through the kernel the call picks (the tap form),
-# the 16-tap direct form, the register-staged tile kernel and the general
-# kernel, all against one reference result.
+# the other readings through the kernel the call picks (the tap form; for
+# the 1x1 reading the GEMM on the input in place), the 16-tap direct form,
+# the register-staged tile kernel and the general kernel, all against one
+# reference result.
 @pytest.mark.parametrize("integer", [False, True], ids=["uniform", "integer"])
 @pytest.mark.parametrize("case", workloads.CONV_STEMS + workloads.CONV_MID,
                          ids=[c.name for c in workloads.CONV_STEMS + workloads.CONV_MID])
@@ -317,7 +318,8 @@ def test_full_size_readings(case, integer):
         assert plan.startswith("stem"), plan
         variants = [0]
     else:
-        assert plan.startswith("tap"), plan
+        # 3x3 readings: the tap form; the 1x1 reading: one product on X in place
+        assert plan.startswith("gemm" if case.R == 1 else "tap"), plan
         variants = [0, 4, 3, 2]
     ref, t = oracle.conv2d(X, Wt, R, S, stride, pad, with_absdot=not integer)
     for variant in variants:

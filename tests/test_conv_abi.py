@@ -121,11 +121,18 @@ def test_plans():
                  kernel_w=3, stride_h=1, stride_w=1, pad_h=1, pad_w=1)
     assert plan(**small).startswith("general")
     assert plan(variant=sg.SCONV_VARIANT_TILE, **small).startswith("tile bm=64 bn=128")
-    p = plan(batch=8, channels=256, height=56, width=56, out_channels=512, kernel_h=1,
-             kernel_w=1, stride_h=1, stride_w=1, pad_h=0, pad_w=0)
+    # a pointwise layer (1x1, stride 1, no padding) runs as one product per image
+    pw = dict(batch=8, channels=256, height=56, width=56, out_channels=512, kernel_h=1,
+              kernel_w=1, stride_h=1, stride_w=1, pad_h=0, pad_w=0)
+    assert plan(**pw) == "gemm images=8 m=512 n=3136 k=256 oh=56 ow=56", plan(**pw)
+    p = plan(variant=sg.SCONV_VARIANT_DIRECT, **pw)
     assert p.startswith("direct") and "k=256" in p, p
-    p = plan(batch=8, channels=250, height=56, width=56, out_channels=512, kernel_h=1,
-             kernel_w=1, stride_h=1, stride_w=1, pad_h=0, pad_w=0)
+    p = plan(variant=sg.SCONV_VARIANT_TILE, **dict(pw, channels=250))
+    assert p.startswith("tile") and "k=250" in p, p
+    # with a stride or padding, a 1x1 filter takes the implicit forms
+    p = plan(**dict(pw, stride_h=2, stride_w=2))
+    assert p.startswith("direct") and "k=256" in p, p
+    p = plan(**dict(pw, channels=250, pad_h=1, pad_w=1))
     assert p.startswith("tile") and "k=250" in p, p
     # the tile kernels take any filter; they refuse inputs of 2^31 bytes or more
     for kw in [dict(), dict(kernel_h=3), dict(kernel_h=5, kernel_w=5)]:

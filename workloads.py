@@ -200,6 +200,9 @@ CONV_STEMS = [
 CONV_MID = [
     ConvCase(2, "conv3x3s1_384x14161x1152", 1, 128, 119, 119, 384, 3, 3, 1, 1, 1, 1),
     ConvCase(3, "conv3x3s1_256x43264x1152", 1, 128, 208, 208, 256, 3, 3, 1, 1, 1, 1),
+    # (256, 50176, 1024): one 224 x 224 output (50176 = 224^2) of a 1 x 1 filter over 1024
+    # channels, the plainest geometry with those factors
+    ConvCase(4, "conv1x1_256x50176x1024", 1, 1024, 224, 224, 256, 1, 1, 1, 1, 0, 0),
 ]
 
 
