@@ -35,6 +35,7 @@ struct ConvArgs {
     int OH, OW, K;       // output extent, taps per output (C*R*S)
     int64_t N;           // batch * OH * OW
     float alpha, beta;
+    int rounds;          // stem kernel: workgroups per CU in its resident grid (else 1)
 };
 
 typedef void (*ConvKernelFn)(ConvArgs, int, int);
@@ -1014,8 +1015,17 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
     // Two adjacent positions per lane can be one 64-bit store.
     const bool vec_y = ((reinterpret_cast<uintptr_t>(a.Y) & 7u) == 0) && (a.ldy % 2 == 0) &&
                        (ohw % 2 == 0);
-    const int64_t s0 = (int64_t)blockIdx.x * total_strips / gridDim.x;
-    const int64_t s1 = (int64_t)(blockIdx.x + 1) * total_strips / gridDim.x;
+    // Workgroups take contiguous ranges of strips (12 or 13 on the 7 x 7
+    // reading).  With a.rounds > 1 they are numbered CU-major: in a resident
+    // grid of `rounds` workgroups per CU, workgroups b, b + G / rounds, ...
+    // (which the dispatcher places on one CU) take adjacent ranges, so a
+    // CU's share differs from the mean by at most one strip.
+    const int per_round = (int)gridDim.x / a.rounds;
+    const int wg = a.rounds > 1 && per_round * a.rounds == (int)gridDim.x
+                       ? ((int)blockIdx.x % per_round) * a.rounds + (int)blockIdx.x / per_round
+                       : (int)blockIdx.x;
+    const int64_t s0 = (int64_t)wg * total_strips / gridDim.x;
+    const int64_t s1 = (int64_t)(wg + 1) * total_strips / gridDim.x;
     const float *a_lane = As + (h * 32 * MB + j) * TP;
 
     // The window of strip st, fetched into registers: this thread's groups
