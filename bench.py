@@ -935,8 +935,8 @@ def main():
                 json.dump(records, f, indent=1)
         return 0
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(an N-split of B and C needs no collective; see the design notes).",
+        print("bench.py runs on one GPU only: libsgemm has no multi-GPU path (the product "
+              "would split N across GPUs, B and C in column blocks, with no collective).",
               file=sys.stderr)
         return 2
 

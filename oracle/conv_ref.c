@@ -25,7 +25,7 @@
  *   Y[m][n] <- alpha * sum_k Wt[m][k] * B[k][n] + beta * Y[m][n]
  *   B[k][n] =  the tap of (c, r, s) for output position n  (im2col)
  *
- * Readings (each also listed in the design notes):
+ * Readings of the pages (where they leave the convolution open):
  *   - Zero padding holds real zeros: a tap outside the image contributes
  *     w * 0, which is 0 for finite w and NaN for an infinite or NaN weight,
  *     exactly as the product with the im2col matrix does.

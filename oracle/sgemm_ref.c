@@ -20,7 +20,7 @@
  *   - Leading dimensions follow that README's OFFSET(row, col, ld) macro
  *     ("kernel 6" section): element (r, c) lives at r*ld + c.
  *
- * Readings where the pages are silent (each also listed in the design notes):
+ * Readings where the pages are silent:
  *   - Products and sums are taken in double precision and rounded to float
  *     once at the end (the page-3 reference sums in float; the spec of this
  *     library asks for fp64 accumulation).  A product of two floats is exact
