@@ -140,14 +140,17 @@ const DlEntry kDlTiles[] = {
     SGEMM_CONV_DL(192, 128, 4, 2, 1, 1), SGEMM_CONV_DL(64, 128, 1, 4, 1, 1),
 };
 
-// The one-tap-per-k-step forms (3 x 3 filters): eight waves, one workgroup
-// per CU (the three-slab ring of 4-channel slabs takes 118-145 KB of LDS).
-#define SGEMM_CONV_TAP(BM, BN, WM, WN, R, S) \
-    {R, S, BM, BN, WM * WN, conv_tap_kernel<BM, BN, WM, WN, 2, R, S>}
+// The one-tap-per-k-step forms (3 x 3 filters), all at two waves per SIMD:
+// four waves with a two-slab ring (78 KB of LDS, two workgroups per CU) or
+// eight waves with a three-slab ring (118-145 KB, one per CU).  At equal
+// busiest-CU work the first entry is taken.
+#define SGEMM_CONV_TAP(BM, BN, WM, WN, NB, R, S) \
+    {R, S, BM, BN, WM * WN, conv_tap_kernel<BM, BN, WM, WN, 2, R, S, NB>}
 
 const DlEntry kTapTiles[] = {
-    SGEMM_CONV_TAP(128, 128, 2, 4, 3, 3),
-    SGEMM_CONV_TAP(192, 128, 4, 2, 3, 3),
+    SGEMM_CONV_TAP(128, 128, 2, 2, 2, 3, 3),
+    SGEMM_CONV_TAP(128, 128, 2, 4, 3, 3, 3),
+    SGEMM_CONV_TAP(192, 128, 4, 2, 3, 3, 3),
 };
 
 // The general kernel's rate relative to the tile kernels' (measured on the

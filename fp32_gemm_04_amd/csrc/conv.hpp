@@ -708,10 +708,13 @@ conv_dl_kernel(ConvArgs a, int tiles_m, int tiles_n)
 //     RS P = 16 or 48 (mod 64): the four lane groups' rows then fall in
 //     distinct banks.
 // Operands are read from LDS one k-step ahead (two register sets); a slab's
-// buffer is read during the whole slab, so the ring has three buffers: the
+// buffer is read during the whole slab.  With a ring of three buffers the
 // loads of slab t + 2 are spread over slab t's MFMAs into the buffer slab
 // t - 1 used, and at the end of slab t one wait (slab t + 1 landed) and one
-// barrier (every wave done with buffer t) hand over to slab t + 1.
+// barrier (every wave done with buffer t) hand over to slab t + 1.  With two
+// (half the LDS, so that two workgroups share a CU) the loads of slab t + 1
+// go into that buffer over the first half of slab t's MFMAs, and the wait at
+// its end takes them all.
 // C must be a multiple of 4; filter rows 16-byte aligned.
 template <int RS, int BN>
 constexpr int conv_tap_pitch()
@@ -721,7 +724,7 @@ constexpr int conv_tap_pitch()
     return -1;
 }
 
-template <int BM, int BN, int WM, int WN, int R, int S>
+template <int BM, int BN, int WM, int WN, int R, int S, int NBUF_ = 3>
 struct ConvTap {
     static constexpr int RS = R * S;
     static constexpr int BK = 4 * RS;
@@ -732,7 +735,7 @@ struct ConvTap {
     static constexpr int P = conv_tap_pitch<RS, BN>();
     static constexpr int A_FLOATS = BM * BK;
     static constexpr int BUF = A_FLOATS + BK * P;
-    static constexpr int NBUF = 3;
+    static constexpr int NBUF = NBUF_;
     static constexpr int LDS = NBUF * BUF;
     static constexpr int AW = BM * RS / 64;          // filter loads per slab
     static constexpr int LA = AW / NW, XA = AW % NW;
@@ -741,23 +744,27 @@ struct ConvTap {
     static constexpr int L = LA + LB;
     static constexpr int LMAX = L + (XA > 0 ? 1 : 0);
     static constexpr int MF = RS * FM * FN;          // MFMAs per wave per slab
-    static constexpr int STRIDE = MF / (LMAX + 1);
+    // Loads are spread over the whole slab with three buffers (they land a
+    // slab later), over its first half with two (they land at its end).
+    static constexpr int STRIDE = (NBUF == 2 ? MF / 2 : MF) / (LMAX + 1);
     static_assert(P > 0, "no conflict-free tap row pitch");
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
     static_assert((BM * RS) % 64 == 0, "filter slab splits into whole loads");
     static_assert(BN % 64 == 0 && (4 * BH) % NW == 0 && G >= 1 && NW % BH == 0,
                   "each wave loads the taps of whole channels for one 64-position piece");
     static_assert(STRIDE >= 1, "too few MFMAs per slab for the loads");
+    static_assert(NBUF == 2 || NBUF == 3, "a ring of two or three slabs");
     static_assert(LMAX * (NBUF - 1) <= 63, "loads in flight must fit the vmcnt field");
 };
 
-template <int BM, int BN, int WM, int WN, int WPE, int R, int S>
+template <int BM, int BN, int WM, int WN, int WPE, int R, int S, int NBUF_ = 3>
 __global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 conv_tap_kernel(ConvArgs a, int tiles_m, int tiles_n)
 {
-    using D = ConvTap<BM, BN, WM, WN, R, S>;
+    using D = ConvTap<BM, BN, WM, WN, R, S, NBUF_>;
     constexpr int RS = D::RS, BK = D::BK, NW = D::NW, TM = D::TM, TN = D::TN;
     constexpr int FM = D::FM, FN = D::FN, BH = D::BH, P = D::P, BUF = D::BUF;
+    constexpr int NBUF = D::NBUF;
     constexpr int LA = D::LA, XA = D::XA, G = D::G, LB = D::LB, L = D::L, LMAX = D::LMAX;
     constexpr int S1 = D::STRIDE;
     __shared__ __attribute__((aligned(16))) float lds[D::LDS];
@@ -855,10 +862,12 @@ conv_tap_kernel(ConvArgs a, int tiles_m, int tiles_n)
     };
 
     // Slab t from buffer buf; its k-step st uses operand set (P0 + st) & 1.
+    // It loads slab t + NBUF - 1 into the buffer slab t - 1 used (every
+    // wave was done with it at the barrier that ended slab t - 1).
     auto slab = [&](auto P0, int t, int buf) {
         constexpr int p0 = decltype(P0)::value;
-        const bool more = t + 2 < nslab;
-        const int lb = buf == 0 ? 2 : buf - 1;  // the buffer of slab t - 1
+        const bool more = t + NBUF - 1 < nslab;
+        const int lb = buf == 0 ? NBUF - 1 : buf - 1;  // the buffer of slab t - 1
 #pragma unroll
         for (int st = 0; st < RS; ++st) {
             const int p = (p0 + st) & 1;
@@ -870,7 +879,7 @@ conv_tap_kernel(ConvArgs a, int tiles_m, int tiles_n)
                     const int i = (st * FM + fm) * FN + fn;
                     if (i > 0 && i % S1 == 0 && i / S1 <= LMAX) {
                         const int q = i / S1 - 1;
-                        if (more && (q < L || extra)) load(q, t + 2, lb);
+                        if (more && (q < L || extra)) load(q, t + NBUF - 1, lb);
                     }
                     acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[p][fm], bf[p][fn],
                                                                        acc[fm][fn], 0, 0, 0);
@@ -878,24 +887,24 @@ conv_tap_kernel(ConvArgs a, int tiles_m, int tiles_n)
         }
         // Slab t + 1 has landed and every wave is done with buffer buf.
         if (extra)
-            wait_slabs_barrier<LMAX, 1>(nslab - 2 - t);
+            wait_slabs_barrier<LMAX, NBUF - 2>(nslab - 2 - t);
         else
-            wait_slabs_barrier<L, 1>(nslab - 2 - t);
-        if (t + 1 < nslab) read((p0 + RS) & 1, buf == 2 ? 0 : buf + 1, 0);
+            wait_slabs_barrier<L, NBUF - 2>(nslab - 2 - t);
+        if (t + 1 < nslab) read((p0 + RS) & 1, buf == NBUF - 1 ? 0 : buf + 1, 0);
     };
 
-    // Prologue: slabs 0 and 1 in flight, wait for slab 0.
+    // Prologue: slabs 0 .. NBUF - 2 in flight, wait for slab 0.
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < NBUF - 1; ++b)
         if (b < nslab) {
 #pragma unroll
             for (int q = 0; q < LMAX; ++q)
                 if (q < L || extra) load(q, b, b);
         }
     if (extra)
-        wait_slabs_barrier<LMAX, 1>(nslab - 1);
+        wait_slabs_barrier<LMAX, NBUF - 2>(nslab - 1);
     else
-        wait_slabs_barrier<L, 1>(nslab - 1);
+        wait_slabs_barrier<L, NBUF - 2>(nslab - 1);
     read(0, 0, 0);
 
     using Q0 = std::integral_constant<int, 0>;
@@ -903,10 +912,10 @@ conv_tap_kernel(ConvArgs a, int tiles_m, int tiles_n)
     int buf = 0;
     for (int t = 0; t < nslab; t += 2) {
         slab(Q0{}, t, buf);
-        buf = buf == 2 ? 0 : buf + 1;
+        buf = buf == NBUF - 1 ? 0 : buf + 1;
         if (t + 1 < nslab) {
             slab(Q1{}, t + 1, buf);
-            buf = buf == 2 ? 0 : buf + 1;
+            buf = buf == NBUF - 1 ? 0 : buf + 1;
         }
     }
 

@@ -90,7 +90,7 @@ def test_plans():
     p = plan(height=119, width=119, out_channels=384, **mid)
     assert p == "tap bm=192 bn=128 waves=8 k=1152 grid=222 oh=119 ow=119", p
     p = plan(height=208, width=208, out_channels=256, **mid)
-    assert p == "tap bm=128 bn=128 waves=8 k=1152 grid=676 oh=208 ow=208", p
+    assert p == "tap bm=128 bn=128 waves=4 k=1152 grid=676 oh=208 ow=208", p
     p = plan(variant=sg.SCONV_VARIANT_DIRECT, height=208, width=208, out_channels=256, **mid)
     assert p == "direct bm=128 bn=128 waves=4 k=1152 grid=676 oh=208 ow=208", p
     # the tap form: 3x3 filters over a multiple of 4 channels
