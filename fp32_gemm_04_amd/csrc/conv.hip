@@ -141,16 +141,19 @@ const DlEntry kDlTiles[] = {
 };
 
 // The one-tap-per-k-step forms (3 x 3 filters), all at two waves per SIMD:
-// four waves with a two-slab ring (78 KB of LDS, two workgroups per CU) or
-// eight waves with a three-slab ring (118-145 KB, one per CU).  At equal
-// busiest-CU work the first entry is taken.
+// four waves with a two-slab ring (70-78 KB of LDS, two workgroups per CU)
+// or eight waves with a three-slab ring (145 KB, one per CU).  At equal
+// busiest-CU work the earlier entry is taken: (256,43264,1152) runs the
+// four-wave 128 x 128 tile (223.4 us; the eight-wave one, three-slab ring,
+// 232.5), (384,14161,1152) the 192 x 128 tile (112.6 us; 96 x 128 two per
+// CU, 114.2).  The 96-row tile serves M <= 96.
 #define SGEMM_CONV_TAP(BM, BN, WM, WN, NB, R, S) \
     {R, S, BM, BN, WM * WN, conv_tap_kernel<BM, BN, WM, WN, 2, R, S, NB>}
 
 const DlEntry kTapTiles[] = {
     SGEMM_CONV_TAP(128, 128, 2, 2, 2, 3, 3),
-    SGEMM_CONV_TAP(128, 128, 2, 4, 3, 3, 3),
     SGEMM_CONV_TAP(192, 128, 4, 2, 3, 3, 3),
+    SGEMM_CONV_TAP(96, 128, 2, 2, 2, 3, 3),
 };
 
 // The general kernel's rate relative to the tile kernels' (measured on the

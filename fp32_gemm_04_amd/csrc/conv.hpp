@@ -733,11 +733,11 @@ struct ConvTap {
     static constexpr int FM = TM / 16, FN = TN / 16;
     static constexpr int BH = BN / 64;               // 64-position pieces of a tap row
     static constexpr int P = conv_tap_pitch<RS, BN>();
-    static constexpr int A_FLOATS = BM * BK;
+    static constexpr int AW = (BM * RS + 63) / 64;   // filter loads (64 16-byte slots) per slab
+    static constexpr int A_FLOATS = AW * 256;        // BM * BK, padded to whole loads
     static constexpr int BUF = A_FLOATS + BK * P;
     static constexpr int NBUF = NBUF_;
     static constexpr int LDS = NBUF * BUF;
-    static constexpr int AW = BM * RS / 64;          // filter loads per slab
     static constexpr int LA = AW / NW, XA = AW % NW;
     static constexpr int G = 4 * BH / NW;            // channels whose taps a wave loads
     static constexpr int LB = G * RS;                // tap loads per wave per slab
@@ -749,7 +749,6 @@ struct ConvTap {
     static constexpr int STRIDE = (NBUF == 2 ? MF / 2 : MF) / (LMAX + 1);
     static_assert(P > 0, "no conflict-free tap row pitch");
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
-    static_assert((BM * RS) % 64 == 0, "filter slab splits into whole loads");
     static_assert(BN % 64 == 0 && (4 * BH) % NW == 0 && G >= 1 && NW % BH == 0,
                   "each wave loads the taps of whole channels for one 64-position piece");
     static_assert(STRIDE >= 1, "too few MFMAs per slab for the loads");
@@ -789,14 +788,15 @@ conv_tap_kernel(ConvArgs a, int tiles_m, int tiles_n)
 
     // Filter loads: load qa of this wave is slab load j = wave + qa NW, whose
     // lane l takes 16-byte slot 64 j + l: row (64 j + l) / RS, quad
-    // (64 j + l) % RS of the row's BK floats.
+    // (64 j + l) % RS of the row's BK floats.  Slots past the tile's BM
+    // rows (the last load's padding) and rows past M land as zeros.
     uint32_t a_voff[LA + 1];
 #pragma unroll
     for (int qa = 0; qa <= LA; ++qa) {
         const int j = wave + qa * NW;
         const int slot = 64 * j + lane;
         const int row = m0 + slot / RS;
-        a_voff[qa] = (j < D::AW && row < M)
+        a_voff[qa] = (j < D::AW && slot < BM * RS && row < M)
                          ? 4u * ((uint32_t)row * (uint32_t)a.ldw + 4u * (uint32_t)(slot % RS))
                          : kOffsetOut;
     }
