@@ -53,12 +53,11 @@ int check_geometry(const Geometry &q, int *OH, int *OW, int64_t *N)
 // The stem kernels built: geometry, row blocks, window shape, waves per SIMD.
 struct StemEntry {
     int C, R, S, sh, sw, mb, wpitch, rows, wpe;
-    bool cu_major;  // number the workgroups CU by CU (see the kernel's strip split)
     ConvKernelFn fn;
 };
 
-#define SGEMM_STEM(MB, CH, R, S, SH, SW, WP, ROWS, WPE, CUM) \
-    {CH, R, S, SH, SW, MB, WP, ROWS, WPE, CUM, conv_stem_kernel<MB, CH, R, S, SH, SW, WP, ROWS, WPE>}
+#define SGEMM_STEM(MB, CH, R, S, SH, SW, WP, ROWS, WPE) \
+    {CH, R, S, SH, SW, MB, WP, ROWS, WPE, conv_stem_kernel<MB, CH, R, S, SH, SW, WP, ROWS, WPE>}
 
 // Windows for 224-wide images: 232 columns hold the image and its padding
 // (column 4 is input column 0); 13 rows (7 x 7, stride 2) or 9 (3 x 3,
@@ -67,15 +66,12 @@ struct StemEntry {
 // four waves; the last column is the waves per SIMD the register budget is
 // set for, i.e. workgroups per CU: two, or three for the 3 x 3 kernel with
 // one row block (161 registers; 70.9 -> 68.0 us on the 3 x 3 stem reading,
-// and a four-wave budget spills).  The last column numbers the workgroups
-// CU by CU, so that a CU's strips differ from the mean by at most one: the
-// 7 x 7 reading, bound by its matrix work, gains (286.5 -> 280.3 us); the
-// memory-bound 3 x 3 one loses (67.9 -> 70.1 us) and keeps the plain order.
+// and a four-wave budget spills).
 const StemEntry kStems[] = {
-    SGEMM_STEM(2, 3, 7, 7, 2, 2, 232, 13, 2, true),
-    SGEMM_STEM(1, 3, 7, 7, 2, 2, 232, 13, 2, true),
-    SGEMM_STEM(2, 3, 3, 3, 2, 2, 232, 9, 2, false),
-    SGEMM_STEM(1, 3, 3, 3, 2, 2, 232, 9, 3, false),
+    SGEMM_STEM(2, 3, 7, 7, 2, 2, 232, 13, 2),
+    SGEMM_STEM(1, 3, 7, 7, 2, 2, 232, 13, 2),
+    SGEMM_STEM(2, 3, 3, 3, 2, 2, 232, 9, 2),
+    SGEMM_STEM(1, 3, 3, 3, 2, 2, 232, 9, 3),
 };
 constexpr int kNumStems = (int)(sizeof(kStems) / sizeof(kStems[0]));
 
@@ -346,7 +342,6 @@ int conv_launch(int variant, const Geometry &q, float alpha, const float *X, con
     a.N = N;
     a.alpha = alpha;
     a.beta = beta;
-    a.rounds = 1;
 
     int cus = 0;
     const hipError_t ce = conv_device_cus(&cus);
@@ -358,7 +353,6 @@ int conv_launch(int variant, const Geometry &q, float alpha, const float *X, con
         // A workgroup is four waves, one per SIMD: wpe of them fit a CU.
         const int64_t resident = (int64_t)cus * stem->wpe;
         const int64_t grid = total < resident ? total : resident;
-        a.rounds = stem->cu_major && grid == resident ? stem->wpe : 1;
         hipLaunchKernelGGL(stem->fn, dim3((unsigned)grid), dim3(256), 0, stream, a, spi,
                            (int)total);
         return (int)hipGetLastError();
