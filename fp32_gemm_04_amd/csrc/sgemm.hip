@@ -199,6 +199,14 @@ int sk_dmode(int dmode, int K) { return K % 16 == 0 ? dmode : kDirectNone; }
 // part-full round: (384,14161,1152) is 222 of them, one per CU, 111.8 us
 // against 117.4 for the stream-K 128 x 128 plan (ldb 14164: 109.0 against
 // 112.2).  Its register-staged kernels are forced-only too.
+// The 96 x 96 direct-load tile (four waves of 48 x 48, two workgroups per
+// CU) cuts 1536^3 into 256 tiles, one per CU, with no partial tiles to add
+// up: 66.7 against 71.9 us for the stream-K 128 x 128 plan.  It also takes
+// shapes whose 128 x 128 or 64 x 64 tiles fill the CUs worse: 3000^3 420.6
+// against 502.6 us, (1536, 1536, 768) 39.4 against 49.0, 1600^3 82.3
+// against 86.8.  Its efficiencies: 0.69 with one tile per CU (1536^3),
+// 0.82-0.84 with two or three (2048^3 to 2560^3), entered as 0.80.  Its
+// register-staged kernels are forced-only.
 const TileConfig kMfmaTiles[] = {
     SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 3, 0.77, SGEMM_DL_KERNEL(160, 160, 2, 2, 2), 0.88,
                      SGEMM_DL_SK_KERNEL(160, 160, 2, 2, 2), 0.82),
@@ -215,6 +223,8 @@ const TileConfig kMfmaTiles[] = {
                        SGEMM_DL_SK_KERNEL(128, 128, 2, 4, 1), 0.82),
     SGEMM_MFMA_ENTRY_R(192, 128, 16, 4, 2, 1, 1, 3, 0.0, SGEMM_DL_KERNEL(192, 128, 4, 2, 1), 0.80,
                        SGEMM_DL_SK_KERNEL(192, 128, 4, 2, 1), 0.82),
+    SGEMM_MFMA_ENTRY(96, 96, 16, 2, 2, 2, 3, 0.0, SGEMM_DL_KERNEL(96, 96, 2, 2, 2), 0.80,
+                     SGEMM_DL_SK_KERNEL(96, 96, 2, 2, 2), 0.69),
 };
 
 // The vector-FMA kernel's two tiles (both two workgroups per CU).
