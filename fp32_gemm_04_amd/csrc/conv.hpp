@@ -1023,6 +1023,7 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
     // Two adjacent positions per lane can be one 64-bit store.
     const bool vec_y = ((reinterpret_cast<uintptr_t>(a.Y) & 7u) == 0) && (a.ldy % 2 == 0) &&
                        (ohw % 2 == 0);
+    const bool full_rows = a.M == 32 * MB;  // every row of the row blocks is an output
     // Strip order.  Workgroups are dealt to the eight XCDs in turn
     // (workgroup b runs on XCD b % 8), so the strips are cut into eight
     // contiguous regions, one per XCD, and an XCD's workgroups take its
@@ -1085,6 +1086,14 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
     }
     f32x4 pre[NST];
     uint64_t valid = 0;  // col_ok and the group's row inside the image
+    // With aligned rows, a 16-byte group lies wholly inside the image or
+    // wholly outside it, and inputs under 2^31 bytes are read through a
+    // buffer resource: a group outside gets an offset past the end, the
+    // load returns zeros, and the window is written as loaded.
+    const bool buf_x = vec_x && (int64_t)a.batch * a.C * a.H * a.W < (1ll << 29);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.X), 0,
+        buf_x ? (int)(4 * (int64_t)a.batch * a.C * a.H * a.W) : 0, kBufferWord3);
     auto fetch = [&](int64_t st) {
         const int b = (int)(st / strips_per_image);
         const int p0 = (int)(st - (int64_t)b * strips_per_image) * kStemStrip;
@@ -1098,6 +1107,12 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
             const int rr = ((tid + 256 * i) / G4) % ROWS;
             const bool row_ok = (unsigned)(ih_lo + rr) < (unsigned)a.H;
             const uint64_t ok4 = row_ok ? (col_ok >> (4 * i)) & 15ull : 0ull;
+            if (buf_x) {
+                pre[i] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               xr, (int)(ok4 ? sbase + goff[i] : kOffsetOut), 0, 0));
+                continue;
+            }
             valid |= ok4 << (4 * i);
             if (vec_x) {
                 pre[i] = *reinterpret_cast<const f32x4 *>(xbase + (ok4 ? sbase + goff[i] : 0u));
@@ -1114,10 +1129,12 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
         for (int i = 0; i < NST; ++i) {
             const int e = tid + 256 * i;
             if (e < CH * ROWS * G4) {
-                f32x4 v;
+                f32x4 v = pre[i];
+                if (!buf_x) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    v[q] = (valid >> (4 * i + q)) & 1 ? pre[i][q] : 0.f;
+                    for (int q = 0; q < 4; ++q)
+                        v[q] = (valid >> (4 * i + q)) & 1 ? pre[i][q] : 0.f;
+                }
                 *reinterpret_cast<f32x4 *>(win + 4 * e) = v;
             }
         }
@@ -1186,27 +1203,51 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
         const uint32_t n0 = (uint32_t)(b * ohw + q0);
         const uint32_t ldy = (uint32_t)a.ldy;
         const bool both = q0 + 1 < ohw;
+        if (full_rows && vec_y && p0 + wave * 64 + 64 <= ohw) {
+            // Every lane stores both positions of every row: the address is
+            // a wave-uniform row base plus this lane's fixed offset.
+            const uint32_t wbase = (uint32_t)(b * ohw + p0 + wave * 64) * 4u;
+            const uint32_t lane_off = (4u * (uint32_t)h * ldy + 2u * (uint32_t)j) * 4u;
+            // The row stride, opaque here so that the 16 MB row bases are
+            // formed store by store (a few scalar instructions each) rather
+            // than hoisted out of the strip loop into scalar registers.
+            uint32_t ldy4 = ldy * 4u;
+            asm volatile("" : "+s"(ldy4));
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-                if (row >= a.M || q0 >= ohw) continue;
-                float *py = reinterpret_cast<float *>(ybase + ((uint32_t)row * ldy + n0) * 4u);
-                float v0 = alpha * acc[mb][0][i], v1 = alpha * acc[mb][1][i];
-                if (vec_y && both) {
-                    f32x2 v = {v0, v1};
-                    if (beta != 0.f) v += beta * *reinterpret_cast<const f32x2 *>(py);
-                    __builtin_nontemporal_store(v, reinterpret_cast<f32x2 *>(py));
-                } else {
-                    if (beta != 0.f) v0 = fmaf(beta, py[0], v0);
-                    __builtin_nontemporal_store(v0, py);
-                    if (both) {
-                        if (beta != 0.f) v1 = fmaf(beta, py[1], v1);
-                        __builtin_nontemporal_store(v1, py + 1);
+                for (int i = 0; i < 16; ++i) {
+                    const int row0 = mb * 32 + 8 * (i >> 2) + (i & 3);  // half-wave 0's row
+                    char *rb = ybase + (wbase + (uint32_t)row0 * ldy4);
+                    f32x2 *py = reinterpret_cast<f32x2 *>(rb + lane_off);
+                    f32x2 v = {alpha * acc[mb][0][i], alpha * acc[mb][1][i]};
+                    if (beta != 0.f) v += beta * *py;
+                    __builtin_nontemporal_store(v, py);
+                }
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int row = mb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+                    if (row >= a.M || q0 >= ohw) continue;
+                    float *py =
+                        reinterpret_cast<float *>(ybase + ((uint32_t)row * ldy + n0) * 4u);
+                    float v0 = alpha * acc[mb][0][i], v1 = alpha * acc[mb][1][i];
+                    if (vec_y && both) {
+                        f32x2 v = {v0, v1};
+                        if (beta != 0.f) v += beta * *reinterpret_cast<const f32x2 *>(py);
+                        __builtin_nontemporal_store(v, reinterpret_cast<f32x2 *>(py));
+                    } else {
+                        if (beta != 0.f) v0 = fmaf(beta, py[0], v0);
+                        __builtin_nontemporal_store(v0, py);
+                        if (both) {
+                            if (beta != 0.f) v1 = fmaf(beta, py[1], v1);
+                            __builtin_nontemporal_store(v1, py + 1);
+                        }
                     }
                 }
-            }
+        }
 
         __syncthreads();  // every wave is done with this window
         if (st + sstep < s1) place();
