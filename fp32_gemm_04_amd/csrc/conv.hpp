@@ -1094,10 +1094,9 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(a.X), 0,
         buf_x ? (int)(4 * (int64_t)a.batch * a.C * a.H * a.W) : 0, kBufferWord3);
-    auto fetch = [&](int64_t st) {
-        const int b = (int)(st / strips_per_image);
-        const int p0 = (int)(st - (int64_t)b * strips_per_image) * kStemStrip;
-        const int ih_lo = (p0 / a.OW) * SH - a.ph;
+    // The window of a strip of image b whose first output row is oh_lo.
+    auto fetch = [&](int b, int oh_lo) {
+        const int ih_lo = oh_lo * SH - a.ph;
         // Byte offset of (image b, channel 0, row ih_lo, column 0); may
         // wrap when ih_lo < 0, where only rows inside the image are read.
         const uint32_t sbase = (uint32_t)((b * a.C * a.H + ih_lo) * a.W) * 4u;
@@ -1140,29 +1139,55 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
         }
     };
 
+    // Strip st is strip si of image b (st = b spi + si).  The loop carries
+    // (b, si) and the strip's first output row from one strip to the next,
+    // by additions: the step is qstep images and rstep strips.
+    const int spi = strips_per_image;
+    const int qstep = (int)(sstep / spi), rstep = (int)(sstep % spi);
+    int cur_b = (int)(s0 / spi), cur_si = (int)(s0 % spi);
+    int cur_oh = cur_si * kStemStrip / a.OW;
     if (s0 < s1) {
-        fetch(s0);
+        fetch(cur_b, cur_oh);
         place();
     }
     __syncthreads();  // the weights and the first window are in LDS
     for (int64_t st = s0; st < s1; st += sstep) {
-        const int b = (int)(st / strips_per_image);
-        const int p0 = (int)(st - (int64_t)b * strips_per_image) * kStemStrip;
-        const int oh_lo = p0 / a.OW;
+        const int b = cur_b;
+        const int p0 = cur_si * kStemStrip;
+        const int oh_lo = cur_oh;
+        int nxt_b = cur_b + qstep, nxt_si = cur_si + rstep;
+        if (nxt_si >= spi) {
+            nxt_si -= spi;
+            ++nxt_b;
+        }
+        const int nxt_oh = nxt_si * kStemStrip / a.OW;
         // The next strip's window travels while this one is computed.
-        if (st + sstep < s1) fetch(st + sstep);
+        if (st + sstep < s1) fetch(nxt_b, nxt_oh);
+        cur_b = nxt_b;
+        cur_si = nxt_si;
+        cur_oh = nxt_oh;
 
         // Per-lane window bases.  Lane j of a wave holds positions 2j and
         // 2j + 1 of the wave's 64 (column blocks cb = 0, 1 interleaved), so its
         // two outputs of a row are adjacent.  Positions past the image clamp
-        // to its last one; their outputs are not stored.
+        // to its last one; their outputs are not stored.  A position's
+        // offset from the strip's first output row is below OW + 255, so
+        // its output row is at most (ROWS - R) / SH rows on (what the host
+        // checks when it picks this kernel): a few compare-and-subtract
+        // steps find it, with no division.
         int base[2][4];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             int q = p0 + wave * 64 + 2 * j + cb;
             q = q < ohw ? q : ohw - 1;
-            const int oh = q / a.OW, ow = q - oh * a.OW;
-            const int pb = (oh - oh_lo) * SH * WPITCH + ow * SW - a.pw + kStemCol0;
+            int ow = q - oh_lo * a.OW, dr = 0;
+#pragma unroll
+            for (int u = 0; u < (ROWS - R) / SH; ++u)
+                if (ow >= a.OW) {
+                    ow -= a.OW;
+                    ++dr;
+                }
+            const int pb = dr * SH * WPITCH + ow * SW - a.pw + kStemCol0;
             base[cb][0] = pb + h * G::D_ROW;
             base[cb][1] = pb + h * G::D_NEXT_ROW;
             base[cb][2] = pb + h * G::D_NEXT_CH;
