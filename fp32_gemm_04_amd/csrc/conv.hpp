@@ -1089,29 +1089,47 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
     // With aligned rows, a 16-byte group lies wholly inside the image or
     // wholly outside it, and inputs under 2^31 bytes are read through a
     // buffer resource: a group outside gets an offset past the end, the
-    // load returns zeros, and the window is written as loaded.
-    const bool buf_x = vec_x && (int64_t)a.batch * a.C * a.H * a.W < (1ll << 29);
+    // load returns zeros, and the window is written as loaded.  A group
+    // whose columns are outside carries that offset (2^31) from the start
+    // and adds it to the strip's base: a base at or past zero is below
+    // 2^31, so the sum is at or past 2^31; a base that wrapped (first window
+    // row above image 0, by at most pad_h rows) gives 2^31 - pad_h W 4,
+    // which the condition below keeps past the input's end.
+    const bool buf_x =
+        vec_x && 4 * ((int64_t)a.batch * a.C * a.H * a.W + (int64_t)a.ph * a.W) <= (1ll << 31);
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(a.X), 0,
         buf_x ? (int)(4 * (int64_t)a.batch * a.C * a.H * a.W) : 0, kBufferWord3);
+    uint32_t gbuf[NST];  // goff, or kOffsetOut for a group outside the columns
+    int grow[NST];       // the group's window row
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+        gbuf[i] = (col_ok >> (4 * i)) & 15ull ? goff[i] : kOffsetOut;
+        grow[i] = ((tid + 256 * i) / G4) % ROWS;
+    }
     // The window of a strip of image b whose first output row is oh_lo.
     auto fetch = [&](int b, int oh_lo) {
         const int ih_lo = oh_lo * SH - a.ph;
         // Byte offset of (image b, channel 0, row ih_lo, column 0); may
         // wrap when ih_lo < 0, where only rows inside the image are read.
         const uint32_t sbase = (uint32_t)((b * a.C * a.H + ih_lo) * a.W) * 4u;
+        if (buf_x) {
+            // Strips away from the image's top and bottom edges test no rows.
+            const bool rows_in = ih_lo >= 0 && ih_lo + ROWS <= a.H;
+#pragma unroll
+            for (int i = 0; i < NST; ++i) {
+                const bool ok = rows_in || (unsigned)(ih_lo + grow[i]) < (unsigned)a.H;
+                pre[i] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               xr, (int)(ok ? sbase + gbuf[i] : kOffsetOut), 0, 0));
+            }
+            return;
+        }
         valid = 0;
 #pragma unroll
         for (int i = 0; i < NST; ++i) {
-            const int rr = ((tid + 256 * i) / G4) % ROWS;
-            const bool row_ok = (unsigned)(ih_lo + rr) < (unsigned)a.H;
+            const bool row_ok = (unsigned)(ih_lo + grow[i]) < (unsigned)a.H;
             const uint64_t ok4 = row_ok ? (col_ok >> (4 * i)) & 15ull : 0ull;
-            if (buf_x) {
-                pre[i] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                               xr, (int)(ok4 ? sbase + goff[i] : kOffsetOut), 0, 0));
-                continue;
-            }
             valid |= ok4 << (4 * i);
             if (vec_x) {
                 pre[i] = *reinterpret_cast<const f32x4 *>(xbase + (ok4 ? sbase + goff[i] : 0u));
@@ -1124,16 +1142,22 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
         }
     };
     auto place = [&]() {
+        if (buf_x) {
+#pragma unroll
+            for (int i = 0; i < NST; ++i) {
+                const int e = tid + 256 * i;
+                if (e < CH * ROWS * G4) *reinterpret_cast<f32x4 *>(win + 4 * e) = pre[i];
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < NST; ++i) {
             const int e = tid + 256 * i;
             if (e < CH * ROWS * G4) {
-                f32x4 v = pre[i];
-                if (!buf_x) {
+                f32x4 v;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        v[q] = (valid >> (4 * i + q)) & 1 ? pre[i][q] : 0.f;
-                }
+                for (int q = 0; q < 4; ++q)
+                    v[q] = (valid >> (4 * i + q)) & 1 ? pre[i][q] : 0.f;
                 *reinterpret_cast<f32x4 *>(win + 4 * e) = v;
             }
         }
