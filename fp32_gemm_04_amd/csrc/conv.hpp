@@ -1035,15 +1035,17 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
     // 5.6 TB/s dealt out).  A workgroup's strip count differs from the mean
     // by at most one.  Grids of fewer than eight deal out all strips.
     const int NG = (int)gridDim.x;
-    int64_t s0, s1, sstep;
+    // Strip indices are below total_strips <= INT_MAX, and a step is at
+    // most the grid size, so they and their sums fit 32 unsigned bits.
+    uint32_t s0, s1, sstep;
     if (NG < 8) {
         s0 = blockIdx.x;
         s1 = total_strips;
         sstep = NG;
     } else {
         const int x = (int)blockIdx.x % 8;
-        s0 = (int64_t)x * total_strips / 8 + (int)blockIdx.x / 8;
-        s1 = (int64_t)(x + 1) * total_strips / 8;
+        s0 = (uint32_t)((int64_t)x * total_strips / 8) + blockIdx.x / 8;
+        s1 = (uint32_t)((int64_t)(x + 1) * total_strips / 8);
         sstep = (NG - 1 - x) / 8 + 1;  // the workgroups of XCD x
     }
     const float *a_lane = As + (h * 32 * MB + j) * TP;
@@ -1175,7 +1177,7 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
         place();
     }
     __syncthreads();  // the weights and the first window are in LDS
-    for (int64_t st = s0; st < s1; st += sstep) {
+    for (uint32_t st = s0; st < s1; st += sstep) {
         const int b = cur_b;
         const int p0 = cur_si * kStemStrip;
         const int oh_lo = cur_oh;
