@@ -207,6 +207,13 @@ int sk_dmode(int dmode, int K) { return K % 16 == 0 ? dmode : kDirectNone; }
 // against 86.8.  Its efficiencies: 0.69 with one tile per CU (1536^3),
 // 0.82-0.84 with two or three (2048^3 to 2560^3), entered as 0.80.  Its
 // register-staged kernels are forced-only.
+// The 64 x 32 tile (four waves of 32 x 16, two workgroups per CU) is for
+// problems too small to fill the CUs with 64 x 64 tiles: twice the tiles,
+// each half the work, 24-31% faster from 128^3 to 640^3 (512^3: 9.7 against
+// 13.1 us; (333, 517, 259) on the register-staged path 11.6 against 16.9;
+// (500, 501, 500) shifted 13.0 against 18.9).  Its efficiencies (0.355 with
+// one tile per CU, 0.45 register-staged and 0.50 direct-load with more) keep
+// it off 768^3 and up, where it is slower (1024^3: 23.8 against 22.9 us).
 const TileConfig kMfmaTiles[] = {
     SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 3, 0.77, SGEMM_DL_KERNEL(160, 160, 2, 2, 2), 0.88,
                      SGEMM_DL_SK_KERNEL(160, 160, 2, 2, 2), 0.82),
@@ -225,6 +232,8 @@ const TileConfig kMfmaTiles[] = {
                        SGEMM_DL_SK_KERNEL(192, 128, 4, 2, 1), 0.82),
     SGEMM_MFMA_ENTRY(96, 96, 16, 2, 2, 2, 3, 0.0, SGEMM_DL_KERNEL(96, 96, 2, 2, 2), 0.80,
                      SGEMM_DL_SK_KERNEL(96, 96, 2, 2, 2), 0.69),
+    SGEMM_MFMA_ENTRY(64, 32, 16, 2, 2, 2, 3, 0.45, SGEMM_DL_KERNEL(64, 32, 2, 2, 2), 0.50,
+                     nullptr, 0.355),
 };
 
 // The vector-FMA kernel's two tiles (both two workgroups per CU).

@@ -87,7 +87,7 @@ def test_captured_call_replays_like_eager(variant, M, N, K, alpha, beta):
 
 # Shapes the selector runs stream-K on aligned operands (the 64 x 64 ring,
 # the eight-wave 128 x 128 tile) and with B rows unaligned (shifted form).
-STREAMK_SHAPES = [(384, 1000, 1152, 1.0, 0.0), (1280, 1280, 1280, 1.5, 0.5),
+STREAMK_SHAPES = [(384, 1000, 2048, 1.0, 0.0), (1280, 1280, 1280, 1.5, 0.5),
                   (384, 2001, 1152, -1.0, 1.0)]
 
 
