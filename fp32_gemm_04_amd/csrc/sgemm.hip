@@ -214,6 +214,14 @@ int sk_dmode(int dmode, int K) { return K % 16 == 0 ? dmode : kDirectNone; }
 // (500, 501, 500) shifted 13.0 against 18.9).  Its efficiencies (0.355 with
 // one tile per CU, 0.45 register-staged and 0.50 direct-load with more) keep
 // it off 768^3 and up, where it is slower (1024^3: 23.8 against 22.9 us).
+// The 96 x 224 direct-load tile (four waves of 48 x 112, one workgroup per
+// CU) cuts (384, 14161, 1152) into 4 x 64 = 256 tiles, one per CU, where
+// 192 x 128 makes 222 and leaves the busiest CU 15% above the mean: 101.4
+// against 112.8 us with operands rotating through HBM, 118.0 against
+// 121.3 back to back on one operand set.  Its one-tile efficiency is
+// entered as 0.74 (scaled to the 192 x 128 entry's 0.82, which that shape
+// measures at 0.755); 0.60 with more tiles per CU keeps it to the
+// one-tile case.
 const TileConfig kMfmaTiles[] = {
     SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 3, 0.77, SGEMM_DL_KERNEL(160, 160, 2, 2, 2), 0.88,
                      SGEMM_DL_SK_KERNEL(160, 160, 2, 2, 2), 0.82),
@@ -234,6 +242,8 @@ const TileConfig kMfmaTiles[] = {
                      SGEMM_DL_SK_KERNEL(96, 96, 2, 2, 2), 0.69),
     SGEMM_MFMA_ENTRY(64, 32, 16, 2, 2, 2, 3, 0.45, SGEMM_DL_KERNEL(64, 32, 2, 2, 2), 0.50,
                      nullptr, 0.355),
+    SGEMM_MFMA_ENTRY_R(96, 224, 16, 2, 2, 1, 1, 3, 0.0, SGEMM_DL_KERNEL(96, 224, 2, 2, 1), 0.60,
+                       nullptr, 0.74),
 };
 
 // The vector-FMA kernel's two tiles (both two workgroups per CU).

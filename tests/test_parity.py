@@ -49,7 +49,7 @@ def _full_check(A, B, C, alpha, beta, variant=0, exact=False, **kw):
 # forced MFMA tiles, the same tiles run
 # stream-K (variant 48 + i), and the eight rungs of the pages' SIMT ladder
 # (variant 32 + r).
-NUM_TILES = 11  # entries of the MFMA tile table (checked against the library in test_abi)
+NUM_TILES = 12  # entries of the MFMA tile table (checked against the library in test_abi)
 STREAMK_FAMILIES = [48 + i for i in range(NUM_TILES)]
 FAMILIES = ([0, 1, 2, 3] + [16 + i for i in range(NUM_TILES)] + STREAMK_FAMILIES
             + [32 + r for r in range(8)])
