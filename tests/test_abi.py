@@ -258,9 +258,9 @@ def test_tune_reset_and_untuned_plans():
     # the mid im2col shapes
     (256, 50176, 1024, dict(bm="128", streamk="512", dp="512")),
     (256, 43264, 1152, dict(bm="128", load="direct", streamk="0")),
-    # odd ldb: B rows at every alignment, the shifted direct-load form; 2 x 111
-    # tiles of 192 x 128 fill the CUs once
-    (384, 14161, 1152, dict(bm="192", bn="128", waves="4x2", occ="1", load="shifted", vecB="0",
+    # odd ldb: B rows at every alignment, the shifted direct-load form; 4 x 64
+    # tiles of 96 x 224 fill the CUs once
+    (384, 14161, 1152, dict(bm="96", bn="224", waves="2x2", occ="1", load="shifted", vecB="0",
                             streamk="0")),
     (256, 43265, 1152, dict(bm="128", waves="2x2", load="shifted", streamk="0")),
     # the four-slab ring with a K tail, and shifted
