@@ -41,6 +41,8 @@ KernelFn direct_kernel(int bm, int bn, int wm, int wn, int wpe, bool shifted)
         return mfma_dl_kernel<64, 32, 2, 2, 2, 4>;
     if (bm == 96 && bn == 224 && wm == 2 && wn == 2 && wpe == 1)
         return mfma_dl_kernel<96, 224, 2, 2, 1, 3>;
+    if (bm == 128 && bn == 176 && wm == 4 && wn == 1 && wpe == 2)
+        return mfma_dl_kernel<128, 176, 4, 1, 2, 3>;
     if (wpe != 2) return nullptr;
     if (bm == 160 && bn == 160 && wm == 2 && wn == 2) return mfma_dl_kernel<160, 160, 2, 2, 2>;
     if (bm == 128 && bn == 128 && wm == 2 && wn == 2) return mfma_dl_kernel<128, 128, 2, 2, 2>;

@@ -222,6 +222,13 @@ int sk_dmode(int dmode, int K) { return K % 16 == 0 ? dmode : kDirectNone; }
 // entered as 0.74 (scaled to the 192 x 128 entry's 0.82, which that shape
 // measures at 0.755); 0.60 with more tiles per CU keeps it to the
 // one-tile case.
+// The 128 x 176 direct-load tile (four waves of 32 x 176, two workgroups per
+// CU) gives (256, 43264, 1152) 492 tiles, at most two per CU, where 128 x
+// 128 makes 676 and puts three on the busiest CU: 191.8 against 207.7 us.
+// 176 = 11 x 16 allows no other wave split; at two waves per SIMD the
+// kernel spills 36 bytes (four values reloaded once per loop trip).  At
+// 3328^3 it lost to the stream-K plan (560 against 550 us): its efficiency
+// of 0.83 is the lowest that still takes the first shape.
 const TileConfig kMfmaTiles[] = {
     SGEMM_MFMA_ENTRY(160, 160, 16, 2, 2, 2, 3, 0.77, SGEMM_DL_KERNEL(160, 160, 2, 2, 2), 0.88,
                      SGEMM_DL_SK_KERNEL(160, 160, 2, 2, 2), 0.82),
@@ -244,6 +251,8 @@ const TileConfig kMfmaTiles[] = {
                      nullptr, 0.355),
     SGEMM_MFMA_ENTRY_R(96, 224, 16, 2, 2, 1, 1, 3, 0.0, SGEMM_DL_KERNEL(96, 224, 2, 2, 1), 0.60,
                        nullptr, 0.74),
+    SGEMM_MFMA_ENTRY(128, 176, 16, 4, 1, 2, 3, 0.0, SGEMM_DL_KERNEL(128, 176, 4, 1, 2), 0.83,
+                     nullptr, 0.0),
 };
 
 // The vector-FMA kernel's two tiles (both two workgroups per CU).

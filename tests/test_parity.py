@@ -49,7 +49,7 @@ def _full_check(A, B, C, alpha, beta, variant=0, exact=False, **kw):
 # forced MFMA tiles, the same tiles run
 # stream-K (variant 48 + i), and the eight rungs of the pages' SIMT ladder
 # (variant 32 + r).
-NUM_TILES = 12  # entries of the MFMA tile table (checked against the library in test_abi)
+NUM_TILES = 13  # entries of the MFMA tile table (checked against the library in test_abi)
 STREAMK_FAMILIES = [48 + i for i in range(NUM_TILES)]
 FAMILIES = ([0, 1, 2, 3] + [16 + i for i in range(NUM_TILES)] + STREAMK_FAMILIES
             + [32 + r for r in range(8)])
@@ -393,11 +393,37 @@ def test_skinny_kernel_shapes(M, N, K):
 # ranges then start and end inside tiles (partial tiles at both ends, tiles
 # split over three or more workers) and edge tiles take the masked body.
 STREAMK_SHAPES = [(300, 200, 1000), (513, 257, 333), (160, 320, 2048), (97, 1000, 640)]
+SLOT_BYTES = 2 * 512 * 128 * 128 * 4  # one stream-K workspace slot of the library (64 MiB)
+
+
+def _sk_refused(variant, M, N, K):
+    """A forced stream-K plan whose partial tiles exceed a workspace slot
+    (a wide tile shared over many workers: 128 x 176 over more than 372) is
+    refused with SGEMM_ERR_WORKSPACE, queuing nothing.  Returns True after
+    checking that refusal for such a plan, False for a plan that fits."""
+    import fp32_gemm_04_amd as sg
+    import torch
+    _, text = sg.sgemm_plan(variant, M, N, K, K, N, N, 1.0, 256)
+    ws = int(text.split(" ws=")[1].split()[0])
+    if ws <= SLOT_BYTES:
+        return False
+    dA = torch.zeros((M, K), device="cuda")
+    dB = torch.zeros((K, N), device="cuda")
+    dC = torch.full((M, N), float("nan"), device="cuda")
+    s = torch.cuda.current_stream()
+    rc = sg.sgemm_f32_variant(variant, M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0,
+                              dC.data_ptr(), N, s.cuda_stream)
+    assert rc == sg.SGEMM_ERR_WORKSPACE, (variant, M, N, K, rc)
+    s.synchronize()
+    assert torch.isnan(dC).all(), "a refused call wrote C"
+    return True
 
 
 @pytest.mark.parametrize("variant", STREAMK_FAMILIES)
 def test_streamk_integer_exact(variant):
     for M, N, K in STREAMK_SHAPES:
+        if _sk_refused(variant, M, N, K):
+            continue
         A = workloads.integers(M, K, 41 * M + K)
         B = workloads.integers(K, N, 43 * N + K)
         C = workloads.integers(M, N, 47 * M + N)
@@ -410,6 +436,7 @@ def test_streamk_uniform_repeatable(variant):
     """Uniform data within tolerance, and the same bits on a second call
     (the partial tiles are added in a fixed order)."""
     M, N, K = 513, 257, 333
+    assert not _sk_refused(variant, M, N, K)
     A = workloads.uniform(M, K, 53)
     B = workloads.uniform(K, N, 59)
     C = workloads.uniform(M, N, 61)
