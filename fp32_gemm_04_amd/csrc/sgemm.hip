@@ -595,6 +595,12 @@ int check_args(int M, int N, int K, float alpha, const void *A, int lda, const v
 }
 
 constexpr int kNumMfmaTiles = (int)(sizeof(kMfmaTiles) / sizeof(kMfmaTiles[0]));
+// The forced-tile variants must stay below the ladder's and the stream-K
+// ones inside the values the variant field reserves for them.
+static_assert(SGEMM_VARIANT_MFMA_TILE + kNumMfmaTiles <= SGEMM_VARIANT_LADDER,
+              "MFMA tile variants would reach the ladder's values");
+static_assert(SGEMM_VARIANT_LADDER + SGEMM_LADDER_RUNGS <= SGEMM_VARIANT_STREAMK_TILE,
+              "ladder variants would reach the stream-K tile values");
 
 bool is_ladder(int v)
 {
