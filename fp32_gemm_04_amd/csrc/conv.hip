@@ -65,8 +65,8 @@ struct StemEntry {
 // output touches.  LDS: 75 KB (7 x 7) and 30 KB (3 x 3).  Workgroups of
 // four waves; the last column is the waves per SIMD the register budget is
 // set for, i.e. workgroups per CU: two, or three for the 3 x 3 kernel with
-// one row block (161 registers; 70.9 -> 68.0 us on the 3 x 3 stem reading,
-// and a four-wave budget spills).
+// one row block (168 registers; 70.9 -> 68.0 us on the 3 x 3 stem reading
+// when it was introduced, and a four-wave budget spills).
 const StemEntry kStems[] = {
     SGEMM_STEM(2, 3, 7, 7, 2, 2, 232, 13, 2),
     SGEMM_STEM(1, 3, 7, 7, 2, 2, 232, 13, 2),

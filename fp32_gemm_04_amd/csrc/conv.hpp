@@ -1033,7 +1033,8 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
     // per row rather than one short piece per workgroup (stores alone, in
     // this stem's pattern: 5.1 TB/s with contiguous ranges per workgroup,
     // 5.6 TB/s dealt out).  A workgroup's strip count differs from the mean
-    // by at most one.  Grids of fewer than eight deal out all strips.
+    // of its XCD's workgroups by at most one.  Grids of fewer than eight
+    // deal out all strips.
     const int NG = (int)gridDim.x;
     // Strip indices are below total_strips <= INT_MAX, and a step is at
     // most the grid size, so they and their sums fit 32 unsigned bits.
@@ -1050,8 +1051,6 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
     }
     const float *a_lane = As + (h * 32 * MB + j) * TP;
 
-    // The window of strip st, fetched into registers: this thread's groups
-    // e = tid + 256 i of the CH * ROWS rows of G4 16-byte groups.
     // Input loads and output stores address the kernel argument's base with
     // 32-bit byte offsets (the host takes this kernel only for inputs and
     // outputs below 4 GiB), which keeps 64-bit address arithmetic out of the
@@ -1060,9 +1059,10 @@ conv_stem_kernel(ConvArgs a, int strips_per_image, int total_strips)
     // The window of strip st is fetched into registers (this thread's
     // 16-byte groups e = tid + 256 i of the CH * ROWS rows of G4 groups)
     // before the strip's MFMAs and written to LDS after them.  The loads
-    // are unconditional, from a clamped address where the data lie outside
-    // the image, and which of them hold data is kept as bits of one
-    // register: a lane-dependent branch around a load would keep its
+    // are unconditional: through a buffer resource with an out-of-range
+    // offset where a group lies outside the image (below), else from a
+    // clamped address, with which of them hold data kept as bits of one
+    // register.  A lane-dependent branch around a load would keep its
     // execution mask alive across the MFMA loop.
     const char *xbase = reinterpret_cast<const char *>(a.X);
     char *ybase = reinterpret_cast<char *>(a.Y);

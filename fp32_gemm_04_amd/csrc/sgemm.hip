@@ -183,7 +183,7 @@ int sk_dmode(int dmode, int K) { return K % 16 == 0 ? dmode : kDirectNone; }
 // The 64 x 64 tile with a three-stage pipeline at two workgroups per CU is
 // faster than the four-per-CU entry when a CU has one tile (1024^3: 27.6
 // against 31.1 us), slower when it has several, which its lower efficiency
-// encodes.  The last entry is the 64 x 64 direct-load tile with a four-slab
+// encodes.  The entry after it is the 64 x 64 direct-load tile with a four-slab
 // ring (one workgroup per CU; twelve slabs measured 6% slower, 1024^3: 24.3
 // against 22.8 us) and with one tile per CU (1024^3: 22.8 against 27.6 us; 768^3: 18.1
 // against 22.5).  Its register-staged kernels (the two-per-CU build) are
@@ -198,7 +198,8 @@ int sk_dmode(int dmode, int K) { return K % 16 == 0 ? dmode : kDirectNone; }
 // CU) is for M = 384-like shapes whose 128 x 128 tiles would leave a
 // part-full round: (384,14161,1152) is 222 of them, one per CU, 111.8 us
 // against 117.4 for the stream-K 128 x 128 plan (ldb 14164: 109.0 against
-// 112.2).  Its register-staged kernels are forced-only too.
+// 112.2); the 96 x 224 tile below now takes that shape.  Its
+// register-staged kernels are forced-only too.
 // The 96 x 96 direct-load tile (four waves of 48 x 48, two workgroups per
 // CU) cuts 1536^3 into 256 tiles, one per CU, with no partial tiles to add
 // up: 66.7 against 71.9 us for the stream-K 128 x 128 plan.  It also takes
