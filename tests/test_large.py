@@ -62,3 +62,43 @@ def test_beyond_32_bit_indices(variant, M, N, K, what, axis):
     assert_bits_equal(got, ref, what)
     del A, B, C
     torch.cuda.empty_cache()
+
+
+# Stem convolutions whose input passes 2^31 bytes (3600 images of 3 x 224 x
+# 224): too large for the stem's buffer-load window fetch, so the aligned
+# input is read with plain 128-bit loads from clamped addresses; the output
+# (20 x 45 M floats, 3.6 GB) stays under the stem's 4 GiB bound.  Integer
+# data drawn on the device; the first, a middle and the last image are
+# compared in full with the reference convolution of that image alone.
+STEM_LARGE = [(3, 1), (7, 3)]  # (filter size, padding), stride 2
+
+
+@pytest.mark.parametrize("R,pad", STEM_LARGE, ids=["3x3", "7x7"])
+def test_stem_input_beyond_2gib(R, pad):
+    import fp32_gemm_04_amd as sg
+    batch, C, H, W, M = 3600, 3, 224, 224, 20
+    geom = (batch, C, H, W, M, R, R, 2, 2, pad, pad)
+    OH = (H + 2 * pad - R) // 2 + 1
+    OW = (W + 2 * pad - R) // 2 + 1
+    N, K = batch * OH * OW, C * R * R
+    assert 4 * batch * C * H * W > 1 << 31
+    _, plan = sg.sconv2d_plan(0, *geom, 256)
+    say("large stem input: %dx%d, plan %s" % (R, R, plan))
+    assert plan.startswith("stem mb=1"), plan
+    X = workloads.device_integers(batch * C * H, W, 980 + R)
+    Wt = workloads.integers(M, K, 981 + R)
+    Y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    dW = torch.from_numpy(Wt).cuda()
+    s = torch.cuda.current_stream()
+    rc = sg.sconv2d_f32(*geom, 1.0, X.data_ptr(), dW.data_ptr(), K, 0.0, Y.data_ptr(), N,
+                        s.cuda_stream)
+    assert rc == 0, sg.sgemm_status_string(rc)
+    torch.cuda.synchronize()
+    ohw = OH * OW
+    for b in (0, batch // 2, batch - 1):
+        img = X[b * C * H:(b + 1) * C * H].reshape(1, C, H, W).cpu().numpy()
+        ref, _ = oracle.conv2d(img, Wt, R, R, (2, 2), (pad, pad), with_absdot=False)
+        got = Y[:, b * ohw:(b + 1) * ohw].cpu().numpy()
+        assert_bits_equal(got, ref, "stem %dx%d image %d" % (R, R, b))
+    del X, Y
+    torch.cuda.empty_cache()
