@@ -257,7 +257,8 @@ def test_tune_reset_and_untuned_plans():
     (3072, 3072, 3072, dict(bm="128", waves="2x2", streamk="512", dp="512", split="64")),
     # the mid im2col shapes
     (256, 50176, 1024, dict(bm="128", streamk="512", dp="512")),
-    (256, 43264, 1152, dict(bm="128", load="direct", streamk="0")),
+    (256, 43264, 1152, dict(bm="128", bn="176", waves="4x1", occ="2", load="direct",
+                            streamk="0")),
     # odd ldb: B rows at every alignment, the shifted direct-load form; 4 x 64
     # tiles of 96 x 224 fill the CUs once
     (384, 14161, 1152, dict(bm="96", bn="224", waves="2x2", occ="1", load="shifted", vecB="0",
@@ -268,6 +269,17 @@ def test_tune_reset_and_untuned_plans():
     (1000, 1001, 1024, dict(bm="64", occ="1", load="shifted", streamk="0")),
     # K % 16 != 0: no direct-load stream-K
     (384, 14161, 1156, dict(streamk="0")),
+    # 4 x 64 tiles of 96 x 224 with B rows aligned too
+    (384, 14164, 1152, dict(bm="96", bn="224", load="direct", streamk="0")),
+    # 256 tiles of 96 x 96, one per CU, no stream-K
+    (1536, 1536, 1536, dict(bm="96", bn="96", streamk="0")),
+    # too small for 64 x 64 tiles to fill the CUs: 64 x 32 on all three load paths
+    (512, 512, 512, dict(bm="64", bn="32", load="direct")),
+    (500, 501, 500, dict(bm="64", bn="32", load="shifted")),
+    (333, 517, 259, dict(bm="64", bn="32", load="regs")),
+    # where the new tiles lost, the earlier plans stay
+    (768, 768, 768, dict(bm="64", bn="64", occ="1")),
+    (3328, 3328, 3328, dict(bm="128", bn="128", streamk="512")),
 ])
 def test_selector_choices(M, N, K, expect):
     """The cost model's choices on the configurations, as measured best on
