@@ -155,15 +155,16 @@ def test_padded_leading_dimensions(variant):
                     lds=(K + pads[0], N + pads[1], N + pads[2]))
 
 
-# K a multiple of 16 with 16-byte aligned rows (other K below): the 160, 128, 64x256 and
-# 64x64 ring families take the direct global -> LDS path, border tiles
+# K a multiple of 16 with 16-byte aligned rows (other K below): the 160, 128, 64x256,
+# 64x64 ring, eight-wave 128, 192x128, 96x96, 64x32, 96x224 and 128x176 families
+# take the direct global -> LDS path, border tiles
 # through its clamped and masked copy.  K = 16 .. 64 covers one to
 # four slabs (every prologue case of the three-buffer pipeline); K = 80 an
 # odd slab count; ldb is rounded up to a multiple of 4 so that ragged N
 # still gives aligned B rows.
 DIRECT_SHAPES = [(160, 160, 16), (320, 320, 32), (321, 319, 48), (333, 517, 64),
                  (256, 512, 80), (480, 160, 1024)]
-DIRECT_FAMILIES = [16, 17, 20, 22, 23, 48, 49, 52, 54, 55]
+DIRECT_FAMILIES = [16, 17, 20, 22, 23, 24, 25, 26, 27, 28, 48, 49, 52, 54, 55, 56, 57]
 
 
 def _plan_load(variant, M, N, K, lda, ldb, ldc):
@@ -239,7 +240,7 @@ def test_direct_load_path_uniform(variant):
 # reaches C.
 SHIFTED_SHAPES = [(128, 128, 16), (256, 257, 32), (257, 389, 48), (384, 1001, 64),
                   (130, 263, 80), (384, 1041, 320)]
-SHIFTED_FAMILIES = [17, 20, 22, 23, 49, 52, 54, 55]
+SHIFTED_FAMILIES = [17, 20, 22, 23, 24, 25, 26, 27, 49, 52, 54, 55, 56, 57]
 
 
 @pytest.mark.parametrize("variant", [0] + SHIFTED_FAMILIES)
